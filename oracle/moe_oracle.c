@@ -1,0 +1,492 @@
+/*
+ * moe_oracle.c -- plain, slow, obviously-correct CPU oracle of the fused
+ * mixture-of-experts layer forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's
+ * CPU-baseline leg may load this library.  It shares no code, header, table or
+ * helper with the HIP library in mixture_experts_layer_14_amd/csrc, and it
+ * never reads anything that library produced.
+ *
+ * Sources (the three web pages the method is taken from):
+ *   [vLLM-layer]  vLLM API docs page "vllm.model_executor.layers.fused_moe.layer",
+ *                 class FusedMoE (constructor arguments, select_experts,
+ *                 forward_native, weight loaders _load_w13/_load_w2).
+ *   [SGL-layer]   SGLang source page "srt/layers/moe/fused_moe_triton/layer.py",
+ *                 class FusedMoE (w13/w2 parameter creation, forward_impl).
+ *   [SGL-DSV2]    SGLang source page "srt/models/deepseek_v2.py", classes
+ *                 DeepseekV2MLP, MoEGate, DeepseekV2MoE (forward_normal,
+ *                 _maybe_quant_moe_input_once, shared-expert add).
+ *
+ * Everything floating-point is evaluated in double from the exactly decoded
+ * inputs (fp32, bf16 or e4m3 times its fp32 block scale).  The two fp8
+ * quantisation points are the exception: there the pages' rule is applied in
+ * fp32, because a quantised code is an integer decided by floating point and
+ * the kernel decides it in fp32.
+ *
+ * Readings of points the pages leave open are listed with each function.
+ * Parity pins: every function here is pinned by the CPU tests in
+ * tests/test_oracle_*.py (brute force, closed forms, library cross-checks and
+ * invariants).  The fp8 layer path is pinned only through its codec, its
+ * quantisation rule and a lossless special case; beyond that it is
+ * "parity unpinned".
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "moe_oracle.h"
+
+/* ------------------------------------------------------------------------ */
+/* Number formats                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* bf16 is the upper half of an IEEE binary32. */
+double or_bf16_to_f64(uint16_t v)
+{
+    uint32_t u = (uint32_t)v << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* OCP fp8 E4M3 ("e4m3fn"): 1 sign, 4 exponent (bias 7), 3 mantissa bits,
+ * no infinities, S.1111.111 is NaN, largest finite 448.  Exponent field 0
+ * holds the subnormals m * 2^-9. */
+double or_e4m3_to_f64(uint8_t v)
+{
+    int sign = v >> 7;
+    int e = (v >> 3) & 0xF;
+    int m = v & 0x7;
+    double mag;
+    if (e == 0xF && m == 0x7)
+        return NAN;
+    if (e == 0)
+        mag = ldexp((double)m, -9);
+    else
+        mag = ldexp(1.0 + m / 8.0, e - 7);
+    return sign ? -mag : mag;
+}
+
+/* fp32 -> e4m3 by round-to-nearest, ties to the even code, saturating at
+ * +-448 (reading: the pages only name the format; the OCP format has no
+ * infinity, so out-of-range values clamp to the largest finite value).
+ * Written as a search over the 127 non-negative finite codes, which are
+ * monotone in value, so that it can be checked by eye. */
+uint8_t or_e4m3_from_f32(float x)
+{
+    uint8_t sign = 0;
+    double a = (double)x;
+    int best = 0;
+    if (isnan(x))
+        return 0x7F;
+    if (signbit(x)) {
+        sign = 0x80;
+        a = -a;
+    }
+    if (a >= 448.0)
+        return (uint8_t)(sign | 0x7E);
+    for (int c = 1; c <= 0x7E; c++) {
+        double lo = or_e4m3_to_f64((uint8_t)(c - 1));
+        double hi = or_e4m3_to_f64((uint8_t)c);
+        if (a < hi) {
+            double mid = 0.5 * (lo + hi);
+            if (a < mid)
+                best = c - 1;
+            else if (a > mid)
+                best = c;
+            else
+                best = ((c - 1) & 1) ? c : c - 1; /* tie: even code */
+            return (uint8_t)(sign | best);
+        }
+    }
+    return (uint8_t)(sign | 0x7E);
+}
+
+/* Per-token-group fp8 quantisation ([SGL-DSV2], DeepseekV2MoE
+ * _maybe_quant_moe_input_once and DeepseekV2MLP.forward: groups of 128
+ * consecutive elements of a row, one fp32 scale per group).
+ * Reading of the scale rule: s = max(amax, 1e-10) / 448, q = e4m3(x / s),
+ * dequantised value q * s.  Evaluated in fp32.
+ * x: rows x cols fp32, cols a multiple of group.  q: rows x cols codes.
+ * s: rows x (cols/group). */
+void or_quant_fp8_groups(int64_t rows, int64_t cols, int64_t group,
+                         const float *x, uint8_t *q, float *s)
+{
+    int64_t ng = cols / group;
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t g = 0; g < ng; g++) {
+            const float *xg = x + r * cols + g * group;
+            float amax = 0.0f;
+            float scale;
+            for (int64_t i = 0; i < group; i++) {
+                float v = fabsf(xg[i]);
+                if (v > amax)
+                    amax = v;
+            }
+            scale = fmaxf(amax, 1e-10f) / 448.0f;
+            s[r * ng + g] = scale;
+            for (int64_t i = 0; i < group; i++)
+                q[r * cols + g * group + i] = or_e4m3_from_f32(xg[i] / scale);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Routing ([vLLM-layer] FusedMoE.select_experts; [SGL-DSV2] DeepseekV2MoE    */
+/* TopK arguments; MoEGate e_score_correction_bias)                           */
+/* ------------------------------------------------------------------------ */
+
+/* Route one token.
+ *  scoring OR_SOFTMAX: score p_e = softmax(l)_e; selection key = l_e
+ *     (the same order as p_e, since softmax is monotone; no transcendental
+ *     touches the decision).
+ *  scoring OR_SIGMOID: score s_e = 1/(1+exp(-l_e)); key c_e = s_e + b_e
+ *     (b = 0 when no bias is given).
+ *  Groups (G > 1): experts [j*E/G, (j+1)*E/G) form group j.  Group score =
+ *     sum of the two largest keys of the group when a correction bias is
+ *     given (the largest key alone for one-expert groups), else the largest
+ *     key.  The TG best groups stay eligible.
+ *  Selection: K times, the eligible unselected expert with the largest key;
+ *     ties go to the lower index (groups too).  ids come out in descending
+ *     key order.
+ *  Weights: w_k = score of the k-th id (the bias never enters a weight);
+ *     if renormalize, w_k /= sum of the K scores; then w_k *= rsf.
+ */
+static int or_route_one(int E, int K, const float *l, const float *bias,
+                        int scoring, int renorm, int G, int TG, double rsf,
+                        int32_t *ids, double *w)
+{
+    double score[OR_MAX_EXPERTS], key[OR_MAX_EXPERTS];
+    int eligible[OR_MAX_EXPERTS], taken[OR_MAX_EXPERTS];
+    double denom = 0.0;
+
+    if (scoring == OR_SOFTMAX) {
+        double m = -INFINITY, z = 0.0;
+        for (int e = 0; e < E; e++)
+            if ((double)l[e] > m)
+                m = (double)l[e];
+        for (int e = 0; e < E; e++)
+            z += exp((double)l[e] - m);
+        for (int e = 0; e < E; e++) {
+            score[e] = exp((double)l[e] - m) / z;
+            key[e] = (double)l[e];
+        }
+    } else {
+        for (int e = 0; e < E; e++) {
+            score[e] = 1.0 / (1.0 + exp(-(double)l[e]));
+            key[e] = score[e] + (bias ? (double)bias[e] : 0.0);
+        }
+    }
+
+    for (int e = 0; e < E; e++) {
+        eligible[e] = 1;
+        taken[e] = 0;
+    }
+
+    if (G > 1) {
+        int per = E / G;
+        double gscore[OR_MAX_EXPERTS];
+        int gkeep[OR_MAX_EXPERTS];
+        for (int j = 0; j < G; j++) {
+            double best1 = -INFINITY, best2 = -INFINITY;
+            for (int e = j * per; e < (j + 1) * per; e++) {
+                if (key[e] > best1) {
+                    best2 = best1;
+                    best1 = key[e];
+                } else if (key[e] > best2) {
+                    best2 = key[e];
+                }
+            }
+            gscore[j] = (bias && per >= 2) ? best1 + best2 : best1;
+            gkeep[j] = 0;
+        }
+        for (int r = 0; r < TG; r++) {
+            int bj = -1;
+            for (int j = 0; j < G; j++)
+                if (!gkeep[j] && (bj < 0 || gscore[j] > gscore[bj]))
+                    bj = j;
+            gkeep[bj] = 1;
+        }
+        for (int e = 0; e < E; e++)
+            eligible[e] = gkeep[e / per];
+    }
+
+    for (int k = 0; k < K; k++) {
+        int be = -1;
+        for (int e = 0; e < E; e++)
+            if (eligible[e] && !taken[e] && (be < 0 || key[e] > key[be]))
+                be = e;
+        if (be < 0)
+            return -1;
+        taken[be] = 1;
+        ids[k] = be;
+        w[k] = score[be];
+        denom += score[be];
+    }
+    for (int k = 0; k < K; k++) {
+        if (renorm)
+            w[k] /= denom;
+        w[k] *= rsf;
+    }
+    return 0;
+}
+
+int or_route(int64_t T, int E, int K, const float *logits, const float *bias,
+             int scoring, int renorm, int G, int TG, double rsf,
+             int32_t *ids, double *weights)
+{
+    if (E < 1 || E > OR_MAX_EXPERTS || K < 1 || K > E)
+        return -1;
+    if (G > 1 && (E % G != 0 || TG < 1 || TG > G || K > TG * (E / G)))
+        return -1;
+    for (int64_t t = 0; t < T; t++)
+        if (or_route_one(E, K, logits + t * E, bias, scoring, renorm, G, TG,
+                         rsf, ids + t * K, weights + t * K))
+            return -1;
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Expert-contiguous permutation ([SGL-layer] FusedMoE.forward_impl:          */
+/* dispatch to the experts and combine back)                                  */
+/* ------------------------------------------------------------------------ */
+
+/* Slots i = t*K + k are sorted stably by expert id (reading: within an
+ * expert, ascending slot index).  offsets[e] = number of slots with id < e
+ * (E+1 entries), sorted_slots[r] = slot at row r, slot_to_row = inverse. */
+int or_permute(int64_t N, int E, const int32_t *ids, int32_t *offsets,
+               int32_t *sorted_slots, int32_t *slot_to_row)
+{
+    int64_t *cursor = (int64_t *)calloc((size_t)E + 1, sizeof(int64_t));
+    if (!cursor)
+        return -1;
+    for (int64_t i = 0; i < N; i++) {
+        if (ids[i] < 0 || ids[i] >= E) {
+            free(cursor);
+            return -1;
+        }
+        cursor[ids[i] + 1]++;
+    }
+    for (int e = 0; e < E; e++)
+        cursor[e + 1] += cursor[e];
+    for (int e = 0; e <= E; e++)
+        offsets[e] = (int32_t)cursor[e];
+    for (int64_t i = 0; i < N; i++) {
+        int64_t r = cursor[ids[i]]++;
+        sorted_slots[r] = (int32_t)i;
+        slot_to_row[i] = (int32_t)r;
+    }
+    free(cursor);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Expert MLP and the full layer                                             */
+/* ------------------------------------------------------------------------ */
+
+/* Element (n, k) of an [N, Kd] weight matrix of one expert, exactly decoded.
+ * e4m3 weights carry one fp32 scale per 128 x 128 block ([SGL-DSV2]
+ * weight_block_size [128, 128], attribute weight_scale_inv read as the
+ * dequantisation multiplier). */
+static double or_weight(const void *data, const float *scale, int dtype,
+                        int64_t Kd, int64_t n, int64_t k)
+{
+    switch (dtype) {
+    case OR_F32:
+        return (double)((const float *)data)[n * Kd + k];
+    case OR_BF16:
+        return or_bf16_to_f64(((const uint16_t *)data)[n * Kd + k]);
+    default: {
+        int64_t kb = (Kd + 127) / 128;
+        double q = or_e4m3_to_f64(((const uint8_t *)data)[n * Kd + k]);
+        return q * (double)scale[(n / 128) * kb + (k / 128)];
+    }
+    }
+}
+
+static double or_silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* One expert's gated MLP ([vLLM-layer] FusedMoE w13 = [gate; up] along the
+ * output dimension per _load_w13, w2 = down; activation "silu" with
+ * is_act_and_mul; [SGL-DSV2] DeepseekV2MLP gate_up_proj -> SiluAndMul ->
+ * down_proj):
+ *   gu  = W13 x            (2I values; rows [0, I) gate, [I, 2I) up)
+ *   act = silu(gu[0:I]) * gu[I:2I]
+ *   y   = W2 act           (H values)
+ * fp8 layers quantise act per group of 128 in fp32 before W2 (the
+ * DeepseekV2MLP fp8 path quantises the SiLU-and-mul output with group 128). */
+static void or_expert_mlp(const or_layer *L, const void *w13, const float *s13,
+                          const void *w2, const float *s2, const double *x,
+                          double *gu, double *act, float *a32, uint8_t *aq,
+                          float *as, double *y)
+{
+    int64_t H = L->H, I = L->I;
+    for (int64_t n = 0; n < 2 * I; n++) {
+        double acc = 0.0;
+        for (int64_t h = 0; h < H; h++)
+            acc += x[h] * or_weight(w13, s13, L->w_dtype, H, n, h);
+        gu[n] = acc;
+    }
+    for (int64_t i = 0; i < I; i++)
+        act[i] = or_silu(gu[i]) * gu[I + i];
+    if (L->act_fp8) {
+        for (int64_t i = 0; i < I; i++)
+            a32[i] = (float)act[i];
+        or_quant_fp8_groups(1, I, 128, a32, aq, as);
+        for (int64_t i = 0; i < I; i++)
+            act[i] = or_e4m3_to_f64(aq[i]) * (double)as[i / 128];
+    }
+    for (int64_t h = 0; h < H; h++) {
+        double acc = 0.0;
+        for (int64_t i = 0; i < I; i++)
+            acc += act[i] * or_weight(w2, s2, L->w_dtype, I, h, i);
+        y[h] = acc;
+    }
+}
+
+/* Scratch of one worker. */
+typedef struct {
+    double *x, *gu, *act, *y;
+    float *x32, *a32, *xs, *as;
+    uint8_t *xq, *aq;
+} or_scratch;
+
+static int or_scratch_alloc(const or_layer *L, or_scratch *s)
+{
+    int64_t H = L->H, I = L->I;
+    s->x = malloc(sizeof(double) * H);
+    s->gu = malloc(sizeof(double) * 2 * I);
+    s->act = malloc(sizeof(double) * I);
+    s->y = malloc(sizeof(double) * H);
+    s->x32 = malloc(sizeof(float) * H);
+    s->a32 = malloc(sizeof(float) * I);
+    s->xs = malloc(sizeof(float) * (H / 128 + 1));
+    s->as = malloc(sizeof(float) * (I / 128 + 1));
+    s->xq = malloc(H);
+    s->aq = malloc(I);
+    return (s->x && s->gu && s->act && s->y && s->x32 && s->a32 && s->xs &&
+            s->as && s->xq && s->aq) ? 0 : -1;
+}
+
+static void or_scratch_free(or_scratch *s)
+{
+    free(s->x); free(s->gu); free(s->act); free(s->y); free(s->x32);
+    free(s->a32); free(s->xs); free(s->as); free(s->xq); free(s->aq);
+}
+
+/* The layer output of one token t into out[0:H]:
+ *   out = sum_k w_k * MLP_{id_k}(x_t)  +  MLP_shared(x_t)
+ * where routing gives (id_k, w_k) with rsf already folded into w_k, and the
+ * shared expert is added with weight 1, never scaled by rsf ([SGL-DSV2]
+ * DeepseekV2MoE: shared output plus routed output times
+ * routed_scaling_factor).  fp8 layers use the group-128 quantised x for both
+ * the routed and the shared experts (quantise once). */
+static int or_token(const or_layer *L, int64_t t, or_scratch *s, double *out)
+{
+    int64_t H = L->H;
+    int32_t ids[OR_MAX_EXPERTS];
+    double w[OR_MAX_EXPERTS];
+    if (or_route_one(L->E, L->K, L->logits + t * L->E, L->bias, L->scoring,
+                     L->renormalize, L->n_group, L->topk_group,
+                     L->routed_scaling_factor, ids, w))
+        return -1;
+    for (int64_t h = 0; h < H; h++) {
+        if (L->x_dtype == OR_F32)
+            s->x32[h] = ((const float *)L->hidden)[t * H + h];
+        else
+            s->x32[h] = (float)or_bf16_to_f64(((const uint16_t *)L->hidden)[t * H + h]);
+        s->x[h] = (double)s->x32[h];
+    }
+    if (L->act_fp8) {
+        or_quant_fp8_groups(1, H, 128, s->x32, s->xq, s->xs);
+        for (int64_t h = 0; h < H; h++)
+            s->x[h] = or_e4m3_to_f64(s->xq[h]) * (double)s->xs[h / 128];
+    }
+    for (int64_t h = 0; h < H; h++)
+        out[h] = 0.0;
+    for (int k = 0; k < L->K; k++) {
+        int e = ids[k];
+        if (!L->w13[e] || !L->w2[e])
+            return -2; /* caller did not supply this expert's weights */
+        or_expert_mlp(L, L->w13[e], L->w13_scale ? L->w13_scale[e] : NULL,
+                      L->w2[e], L->w2_scale ? L->w2_scale[e] : NULL, s->x,
+                      s->gu, s->act, s->a32, s->aq, s->as, s->y);
+        for (int64_t h = 0; h < H; h++)
+            out[h] += w[k] * s->y[h];
+    }
+    if (L->shared_w13) {
+        or_expert_mlp(L, L->shared_w13, L->shared_w13_scale, L->shared_w2,
+                      L->shared_w2_scale, s->x, s->gu, s->act, s->a32, s->aq,
+                      s->as, s->y);
+        for (int64_t h = 0; h < H; h++)
+            out[h] += s->y[h];
+    }
+    return 0;
+}
+
+typedef struct {
+    const or_layer *L;
+    const int64_t *tokens;
+    double *out;
+    int64_t begin, end;
+    int status;
+} or_job;
+
+static void *or_worker(void *arg)
+{
+    or_job *j = (or_job *)arg;
+    or_scratch s;
+    j->status = 0;
+    if (or_scratch_alloc(j->L, &s)) {
+        j->status = -3;
+        or_scratch_free(&s);
+        return NULL;
+    }
+    for (int64_t i = j->begin; i < j->end && !j->status; i++)
+        j->status = or_token(j->L, j->tokens[i], &s, j->out + i * j->L->H);
+    or_scratch_free(&s);
+    return NULL;
+}
+
+/* Layer output for the listed tokens (out: ntok x H doubles).  Tokens are
+ * independent, so a worker pool over tokens gives bitwise the same result
+ * for any thread count. */
+int or_moe_forward_tokens(const or_layer *L, int64_t ntok,
+                          const int64_t *tokens, double *out, int nthreads)
+{
+    or_job jobs[OR_MAX_THREADS];
+    pthread_t th[OR_MAX_THREADS];
+    int status = 0;
+    if (L->E < 1 || L->E > OR_MAX_EXPERTS || L->K < 1 || L->K > L->E)
+        return -1;
+    if (L->act_fp8 && (L->H % 128 || L->I % 128))
+        return -1;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > OR_MAX_THREADS)
+        nthreads = OR_MAX_THREADS;
+    if (nthreads > ntok)
+        nthreads = ntok > 0 ? (int)ntok : 1;
+    for (int i = 0; i < nthreads; i++) {
+        jobs[i].L = L;
+        jobs[i].tokens = tokens;
+        jobs[i].out = out;
+        jobs[i].begin = ntok * i / nthreads;
+        jobs[i].end = ntok * (i + 1) / nthreads;
+        jobs[i].status = 0;
+    }
+    if (nthreads == 1) {
+        or_worker(&jobs[0]);
+        return jobs[0].status;
+    }
+    for (int i = 0; i < nthreads; i++)
+        pthread_create(&th[i], NULL, or_worker, &jobs[i]);
+    for (int i = 0; i < nthreads; i++) {
+        pthread_join(th[i], NULL);
+        if (jobs[i].status && !status)
+            status = jobs[i].status;
+    }
+    return status;
+}

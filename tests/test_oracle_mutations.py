@@ -1,0 +1,72 @@
+"""Planted mistakes in the oracle, on the CPU: each edit below is a plausible
+slip (a dropped term, a wrong sign or index, a transposed operand, a wrong
+constant, a wrong tie rule).  Every edited build must fail at least one of the
+oracle's pins, which shows the pins are strong enough to trust the oracle.
+
+Every edit keeps all memory accesses in bounds, so a broken build fails a
+check instead of crashing the test process.
+"""
+import os
+import subprocess
+
+import pytest
+
+from oracle import oracle as O
+from tests import oracle_pins as P
+
+MUTANTS = {
+    "swap_gate_up": ("act[i] = or_silu(gu[i]) * gu[I + i];",
+                     "act[i] = or_silu(gu[I + i]) * gu[i];"),
+    "silu_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
+    "sigmoid_sign": ("score[e] = 1.0 / (1.0 + exp(-(double)l[e]));",
+                     "score[e] = 1.0 / (1.0 + exp((double)l[e]));"),
+    "no_renormalize": ("w[k] /= denom;", "w[k] /= 1.0;"),
+    "no_rsf": ("w[k] *= rsf;", "w[k] *= 1.0;"),
+    "bias_in_weight": ("w[k] = score[be];", "w[k] = key[be];"),
+    "group_score_max_only": ("gscore[j] = (bias && per >= 2) ? best1 + best2 : best1;",
+                             "gscore[j] = best1;"),
+    "tie_to_higher": ("if (eligible[e] && !taken[e] && (be < 0 || key[e] > key[be]))",
+                      "if (eligible[e] && !taken[e] && (be < 0 || key[e] >= key[be]))"),
+    "strided_groups": ("eligible[e] = gkeep[e / per];", "eligible[e] = gkeep[e % G];"),
+    "unstable_permutation": ("int64_t r = cursor[ids[i]]++;",
+                             "int64_t r = offsets[ids[i]] + offsets[ids[i] + 1] - 1 - cursor[ids[i]]++;"),
+    "shared_scaled_by_rsf": ("            out[h] += s->y[h];",
+                             "            out[h] += L->routed_scaling_factor * s->y[h];"),
+    "combine_wrong_weight": ("out[h] += w[k] * s->y[h];", "out[h] += w[0] * s->y[h];"),
+    "w13_transposed": ("acc += x[h] * or_weight(w13, s13, L->w_dtype, H, n, h);",
+                       "acc += x[h] * or_weight(w13, s13, L->w_dtype, 2 * I, h, n);"),
+    "w2_transposed": ("acc += act[i] * or_weight(w2, s2, L->w_dtype, I, h, i);",
+                      "acc += act[i] * or_weight(w2, s2, L->w_dtype, H, i, h);"),
+    "e4m3_exponent_bias": ("mag = ldexp(1.0 + m / 8.0, e - 7);", "mag = ldexp(1.0 + m / 8.0, e - 8);"),
+    "e4m3_subnormal_scale": ("mag = ldexp((double)m, -9);", "mag = ldexp((double)m, -10);"),
+    "e4m3_ties_down": ("best = ((c - 1) & 1) ? c : c - 1; /* tie: even code */", "best = c - 1;"),
+    "fnuz_max": ("scale = fmaxf(amax, 1e-10f) / 448.0f;", "scale = fmaxf(amax, 1e-10f) / 240.0f;"),
+    "no_act_quant": ("    if (L->act_fp8) {\n        for (int64_t i = 0; i < I; i++)",
+                     "    if (0) {\n        for (int64_t i = 0; i < I; i++)"),
+    "no_input_quant": ("    if (L->act_fp8) {\n        or_quant_fp8_groups(1, H, 128",
+                       "    if (0) {\n        or_quant_fp8_groups(1, H, 128"),
+    "bf16_shift": ("uint32_t u = (uint32_t)v << 16;", "uint32_t u = (uint32_t)v << 15;"),
+    "block_scale_index": ("return q * (double)scale[(n / 128) * kb + (k / 128)];",
+                          "return q * (double)scale[(k / 128) * kb + (n / 128)];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(O.SRC).read()
+    assert src.count(old) == 1, "mutation anchor not found exactly once: %s" % name
+    mutated = tmp_path / "moe_oracle.c"
+    mutated.write_text(src.replace(old, new))
+    hdr = os.path.join(os.path.dirname(O.SRC), "moe_oracle.h")
+    (tmp_path / "moe_oracle.h").write_text(open(hdr).read())
+    so = tmp_path / ("libmut_%s.so" % name)
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+                           str(mutated), "-o", str(so), "-lm"])
+    lib_ = O.load_variant(str(so))
+    for check in P.ALL_CHECKS:
+        try:
+            check(lib_=lib_)
+        except (AssertionError, ValueError):
+            return  # caught
+    pytest.fail("planted mistake %r passed every pin" % name)
