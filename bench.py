@@ -1,0 +1,211 @@
+"""Benchmark of the fused MoE layer forward on one MI355X.
+
+Default workload: the Mixtral-shape layer (E=8, top_k=2, hidden=4096,
+intermediate=14336, bf16 weights, softmax + renormalize) at prefill size
+T=4096 tokens, with the decode-size T=32 measured beside it.  A step is one
+pass of the whole layer (routing, permutation, w13 + SiLU-and-mul, w2 +
+weighted combine) over one batch of synthetic inputs already resident in
+HBM.  Prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--config mixtral] [--cpu-sample N]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FusedMoE fwd tokens/s + TFLOP/s (prefill) / HBM GB/s (decode), 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector/matrix
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def _weight_bytes(cfg):
+    return {"f32": 4, "bf16": 2, "fp8": 1}[cfg.w_dtype]
+
+
+def algorithmic_bytes(cfg, T, active_experts):
+    """Weights of the experts that received rows (+ fp8 scales, + shared
+    expert), hidden in, out, router logits, routing ids and weights."""
+    wb = _weight_bytes(cfg)
+    per_expert = 3 * cfg.H * cfg.I * wb
+    if cfg.fp8:
+        per_expert += (2 * cfg.I // 128) * (cfg.H // 128) * 4 + (cfg.H // 128) * (cfg.I // 128) * 4
+    act_b = 4 if cfg.act_dtype == "f32" else 2
+    return (per_expert * (active_experts + cfg.shared) + 2 * T * cfg.H * act_b
+            + T * cfg.E * 4 + T * cfg.K * 8)
+
+
+def w13_flops(cfg, T):
+    return 4.0 * T * (cfg.K + cfg.shared) * cfg.H * cfg.I
+
+
+def time_layer(cfg, T, steps, warmup):
+    """Time `steps` passes of the whole layer through the library's entry
+    points, with HIP events around the w13 GEMM on the stream it runs on."""
+    import torch
+
+    from mixture_experts_layer_14_amd import synth
+    from mixture_experts_layer_14_amd.layer import FusedMoE, Stages, params_for
+
+    inp = synth.make_inputs(cfg, T, device="cuda")
+    layer = FusedMoE(params_for(cfg, T), inp)
+    st = Stages(layer, T)
+    hidden, logits = inp["hidden"], inp["router_logits"]
+    bias = inp.get("e_score_correction_bias")
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+
+    def step(i=None):
+        st.topk(logits, bias)
+        st.align()
+        if st.xq is not None:
+            st.quant(hidden)
+        if i is not None:
+            ev[i][0].record(stream)
+        st.w13(hidden)
+        if i is not None:
+            ev[i][1].record(stream)
+        st.w2()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    w13_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    active = int((st.offsets[1:] - st.offsets[:-1] > 0).sum().item())
+    # the product entry point (one call for the whole layer), timed alone
+    out = torch.empty_like(st.out)
+    for _ in range(max(1, warmup)):
+        layer.forward(hidden, logits, bias, out=out)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(steps):
+        layer.forward(hidden, logits, bias, out=out)
+    torch.cuda.synchronize()
+    fwd_ms = (time.perf_counter() - t1) / steps * 1e3
+    del layer, st, inp
+    torch.cuda.empty_cache()
+    return {"ms_per_step": elapsed / steps * 1e3, "w13_ms": w13_ms, "active_experts": active,
+            "forward_ms_per_step": fwd_ms}
+
+
+def cpu_baseline(cfg, T, sample_tokens):
+    """The CPU oracle, as it stands, on the first `sample_tokens` tokens of
+    the same workload, on all host threads."""
+    import torch
+
+    from mixture_experts_layer_14_amd import synth
+    from oracle import oracle as O
+
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    threads = max(1, min(threads, 16))
+    inp = synth.make_inputs(cfg, sample_tokens, device="cpu",
+                            weight_device="cuda" if torch.cuda.is_available() else "cpu")
+    bits = synth.tensor_bits
+    L = dict(T=sample_tokens, E=cfg.E, K=cfg.K, H=cfg.H, I=cfg.I,
+             scoring=O.SIGMOID if cfg.scoring == "sigmoid" else O.SOFTMAX,
+             renormalize=cfg.renormalize, n_group=cfg.n_group, topk_group=cfg.topk_group,
+             routed_scaling_factor=cfg.rsf,
+             x_dtype=O.F32 if cfg.act_dtype == "f32" else O.BF16,
+             w_dtype={"f32": O.F32, "bf16": O.BF16, "fp8": O.E4M3}[cfg.w_dtype],
+             act_fp8=cfg.fp8, hidden=bits(inp["hidden"]), logits=bits(inp["router_logits"]),
+             bias=bits(inp.get("e_score_correction_bias")),
+             w13=bits(inp["w13"]), w2=bits(inp["w2"]),
+             w13_scale=bits(inp.get("w13_scale")), w2_scale=bits(inp.get("w2_scale")))
+    del inp
+    t0 = time.perf_counter()
+    O.moe_forward_tokens(L, range(sample_tokens), nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "first %d tokens of the %s workload, full layer in float64, %.1f s"
+                      % (sample_tokens, cfg.name, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="mixtral")
+    ap.add_argument("--decode-config", default="mixtral_decode")
+    ap.add_argument("--cpu-sample", type=int, default=32)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build runs the whole expert set on a single "
+              "MI355X (no expert/tensor parallelism); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from mixture_experts_layer_14_amd import binding, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    binding.load()
+    cfg = synth.CONFIGS[args.config]
+    T = cfg.T
+    r = time_layer(cfg, T, args.steps, args.warmup)
+    flops = cfg.flops()
+    peak = {"bf16": PEAK_BF16_TFLOPS, "fp8": PEAK_FP8_TFLOPS, "f32": PEAK_F32_TFLOPS}[cfg.w_dtype]
+    w13_tflops = w13_flops(cfg, T) / (r["w13_ms"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": T / (r["ms_per_step"] * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3", "f32": "f32"}[cfg.w_dtype],
+        "data": "synthetic (seeded N(0,1) hidden and logits, N(0,0.02) weights)",
+        "config": {"workload": "%s MoE layer forward, prefill T=%d" % (cfg.name, T), "E": cfg.E,
+                   "top_k": cfg.K, "hidden": cfg.H, "intermediate": cfg.I, "T": T,
+                   "routing": "%s%s" % (cfg.scoring, "+renormalize" if cfg.renormalize else "")},
+        "tflops": flops / (r["ms_per_step"] * 1e-3) / 1e12,
+        "mfma_frac": flops / (r["ms_per_step"] * 1e-3) / 1e12 / peak,
+        "forward_ms_per_step": r["forward_ms_per_step"],
+        "active_experts": r["active_experts"],
+        "roofline": {"kernel": "w13 grouped GEMM + SiLU-and-mul", "bound": "mfma",
+                     "achieved": w13_tflops, "peak": peak, "unit": "TFLOP/s",
+                     "frac": w13_tflops / peak, "traffic": None,
+                     "avg_kernel_ms": r["w13_ms"]},
+    }
+    if args.decode_config:
+        dcfg = synth.CONFIGS[args.decode_config]
+        d = time_layer(dcfg, dcfg.T, max(args.steps, 50), args.warmup)
+        byts = algorithmic_bytes(dcfg, dcfg.T, d["active_experts"])
+        gbs = byts / (d["ms_per_step"] * 1e-3) / 1e9
+        line["decode"] = {"workload": "%s T=%d" % (dcfg.name, dcfg.T), "T": dcfg.T,
+                          "ms_per_step": d["ms_per_step"],
+                          "tokens_per_s": dcfg.T / (d["ms_per_step"] * 1e-3),
+                          "hbm_GBps": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
+                          "algorithmic_bytes": byts, "active_experts": d["active_experts"],
+                          "forward_ms_per_step": d["forward_ms_per_step"]}
+    if not args.no_cpu and args.cpu_sample > 0:
+        line["cpu_baseline"] = cpu_baseline(cfg, T, args.cpu_sample)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,222 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) fused mixture-of-experts forward.
+ *
+ * The layer routes each token to top_k of num_experts expert MLPs and sums
+ * their outputs with the routing weights:
+ *
+ *   (ids, w)  = route(router_logits_t)                        moe_topk
+ *   rows      = tokens grouped expert by expert               moe_align_permute
+ *   act_r     = silu(x W1_e^T) * (x W3_e^T)                   moe_grouped_gemm_w13_act
+ *   out_t     = sum_k w_{t,k} * act_{r(t,k)} W2_{e}^T          moe_grouped_gemm_w2_combine
+ *             (+ shared expert MLP with weight 1)
+ *
+ * Sources of the operation (three web pages):
+ *   vLLM API docs page "vllm.model_executor.layers.fused_moe.layer",
+ *     class FusedMoE: constructor arguments (num_experts, top_k, hidden_size,
+ *     intermediate_size, renormalize, use_grouped_topk, num_expert_group,
+ *     topk_group, scoring_func, routed_scaling_factor,
+ *     e_score_correction_bias, activation "silu", is_act_and_mul),
+ *     select_experts, forward_native, _load_w13 / _load_w2 (weight layout);
+ *   SGLang page "srt/layers/moe/fused_moe_triton/layer.py", class FusedMoE:
+ *     forward / forward_impl (dispatch -> run_moe_core -> combine);
+ *   SGLang page "srt/models/deepseek_v2.py": MoEGate (fp32 router logits,
+ *     fp32 correction bias), DeepseekV2MoE (grouped top-k arguments, shared
+ *     expert added unscaled, routed output scaled by routed_scaling_factor,
+ *     quantise-once of the input to per-token-group-128 fp8),
+ *     DeepseekV2MLP (gate_up -> SiluAndMul -> down, fp8 block [128, 128]).
+ *
+ * Conventions for every call
+ *   - Every pointer argument is DEVICE memory unless marked "host".  The
+ *     caller owns all buffers; the library never allocates in a call.
+ *   - All arrays are dense row-major.  bf16 = IEEE binary32 upper half;
+ *     fp8 = OCP e4m3 ("e4m3fn", max 448) stored one byte per value.
+ *   - `stream` is a hipStream_t passed as void* (NULL: the null stream).
+ *     Calls only enqueue work: no host synchronisation, no allocation, so a
+ *     sequence of calls may be captured into a HIP graph.
+ *   - Inputs are read-only; outputs never alias inputs (no in-place mode).
+ *   - Arguments are validated on the host before anything is launched; on
+ *     error nothing is enqueued and a negative status is returned.
+ *   - num_tokens == 0 is valid: the call returns MOE_OK and launches nothing.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID = -1,     /* bad shape, parameter or NULL pointer        */
+    MOE_ERR_UNSUPPORTED = -2, /* valid but not built: dtype combination etc. */
+    MOE_ERR_WORKSPACE = -3,   /* workspace smaller than required             */
+    MOE_ERR_HIP = -4          /* a HIP launch failed                         */
+};
+
+/* Router scoring (FusedMoE scoring_func). */
+enum { MOE_SCORING_SOFTMAX = 0, MOE_SCORING_SIGMOID = 1 };
+
+/* Element types. */
+enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1, MOE_DTYPE_FP8_E4M3 = 2 };
+
+/* Layer description (host struct, read during the call only).
+ *
+ * Supported (act_dtype, weight_dtype, out_dtype):
+ *   (F32, F32, F32), (BF16, BF16, BF16), (BF16, FP8_E4M3, BF16).
+ * fp8 weights carry one fp32 dequantisation scale per 128 x 128 block of each
+ * [N, K] weight matrix (w ~= code * scale); fp8 layers quantise the input
+ * and the SiLU-and-mul output per (row, group of 128) with
+ * scale = max(amax, 1e-10) / 448, code = e4m3(x / scale), in fp32.
+ */
+typedef struct moe_params {
+    int64_t num_tokens;          /* T >= 0                                     */
+    int32_t num_experts;         /* E, 1..512                                  */
+    int32_t top_k;               /* K, 1..min(E, 32)                           */
+    int32_t hidden_size;         /* H, multiple of 64 (of 128 for fp8)         */
+    int32_t intermediate_size;   /* I, multiple of 64 (of 128 for fp8)         */
+    int32_t scoring_func;        /* MOE_SCORING_*                              */
+    int32_t renormalize;         /* 1: weights / sum of the K selected scores  */
+    int32_t num_expert_group;    /* G; 0 or 1 = ungrouped; else E % G == 0     */
+    int32_t topk_group;          /* TG, 1..G, with K <= TG * E / G             */
+    float routed_scaling_factor; /* multiplies every routed weight (1.0)       */
+    int32_t act_dtype;           /* dtype of hidden                            */
+    int32_t weight_dtype;        /* dtype of w13 / w2                          */
+    int32_t out_dtype;           /* dtype of out                               */
+    int32_t num_shared_experts;  /* 0, or 1: a shared expert (same format as  */
+                                 /* the routed ones) of intermediate size I   */
+                                 /* added to every token with weight 1        */
+} moe_params;
+
+/* Bytes of device workspace that moe_forward needs for `p` (the decomposed
+ * calls need no more than this).  Returns 0 for invalid parameters. */
+size_t moe_workspace_size(const moe_params *p);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *moe_status_string(int status);
+
+/* Router: top-k expert selection and routing weights per token.
+ * Passage: FusedMoE.select_experts (vLLM page), grouped top-k and
+ * e_score_correction_bias (vLLM page; DeepseekV2MoE TopK arguments and
+ * MoEGate on the SGLang deepseek_v2 page).
+ *   router_logits  [T, E] fp32.
+ *   e_score_correction_bias  [E] fp32 or NULL (sigmoid scoring only; it moves
+ *                  the selection, never the weights).
+ *   topk_ids       [T, K] int32 out: selected experts in descending key
+ *                  order; exact ties go to the lower expert index.
+ *   topk_weights   [T, K] fp32 out: score of each selected expert (softmax
+ *                  probability or sigmoid), divided by the K scores' sum if
+ *                  renormalize, times routed_scaling_factor.
+ * Selection key: the logit (softmax) or sigmoid(logit) + bias (sigmoid).
+ * Grouped (G > 1): group j = experts [j*E/G, (j+1)*E/G); a group scores the
+ * sum of its two largest keys with a bias, else its largest key; only the
+ * TG best groups are eligible.
+ * Errors: MOE_ERR_INVALID for K > E, E % G != 0, TG outside 1..G,
+ * K > TG*E/G, a bias with softmax scoring, NULL pointers. */
+int moe_topk(const moe_params *p, const float *router_logits,
+             const float *e_score_correction_bias, int32_t *topk_ids,
+             float *topk_weights, void *stream);
+
+/* Expert-contiguous permutation of the T*K slots (slot i = t*K + k).
+ * Passage: the dispatch step of FusedMoE.forward_impl (SGLang layer page:
+ * dispatcher.dispatch -> run_moe_core -> dispatcher.combine).
+ *   topk_ids       [T*K] int32, each in [0, E).
+ *   expert_offsets [E+1] int32 out: expert e owns rows
+ *                  [expert_offsets[e], expert_offsets[e+1]).
+ *   sorted_slots   [T*K] int32 out: slot placed at each row; within an
+ *                  expert, slots ascend (a stable sort, bit-exact).
+ *   slot_to_row    [T*K] int32 out: inverse of sorted_slots.
+ *   workspace      >= moe_workspace_size(p) bytes of device scratch.
+ * Errors: MOE_ERR_INVALID (ids out of range are not detected on the
+ * device: they are a precondition), MOE_ERR_WORKSPACE. */
+int moe_align_permute(const moe_params *p, const int32_t *topk_ids,
+                      int32_t *expert_offsets, int32_t *sorted_slots,
+                      int32_t *slot_to_row, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/* Per-token-group-128 fp8 quantisation of the layer input, computed once and
+ * fed to both the routed and the shared experts.
+ * Passage: DeepseekV2MoE._maybe_quant_moe_input_once (SGLang deepseek_v2
+ * page).
+ *   hidden   [T, H] bf16.
+ *   q        [T, H] e4m3 codes out;  scale  [T, H/128] fp32 out.
+ * Errors: MOE_ERR_INVALID (H % 128, NULL), MOE_ERR_UNSUPPORTED (act dtype
+ * not bf16). */
+int moe_quant_act_fp8(const moe_params *p, const void *hidden, uint8_t *q,
+                      float *scale, void *stream);
+
+/* Gate/up grouped GEMM with SiLU-and-mul, row by row of the permutation.
+ * Passage: FusedMoE w13 = [w1 (gate); w3 (up)] along the output dimension
+ * (_load_w13, vLLM page), activation "silu" with is_act_and_mul;
+ * DeepseekV2MLP gate_up_proj -> SiluAndMul (SGLang deepseek_v2 page).
+ *   hidden       [T, H]: act dtype; for fp8 weights the e4m3 codes from
+ *                moe_quant_act_fp8 with hidden_scale [T, H/128].
+ *   w13          [E, 2I, H] (+ w13_scale [E, 2I/128, H/128] for fp8).
+ *   shared_w13   [2I, H] (+ scale) when num_shared_experts == 1, else NULL.
+ *   expert_offsets, sorted_slots: from moe_align_permute.
+ *   act          [T*K + T*S, I] out (S = num_shared_experts): row r holds
+ *                silu(g) * u for the token of sorted_slots[r] (rows
+ *                T*K + t: token t through the shared expert).  bf16 for
+ *                bf16 layers, fp32 for fp32 layers, e4m3 codes for fp8
+ *                layers with act_scale [T*K + T*S, I/128] fp32 out.
+ * Errors: MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE. */
+int moe_grouped_gemm_w13_act(const moe_params *p, const void *hidden,
+                             const float *hidden_scale, const void *w13,
+                             const float *w13_scale, const void *shared_w13,
+                             const float *shared_w13_scale,
+                             const int32_t *expert_offsets,
+                             const int32_t *sorted_slots, void *act,
+                             float *act_scale, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/* Down grouped GEMM and the weighted combine back to token order.
+ * Passage: FusedMoE w2 = down_proj (vLLM page), combine_output /
+ * dispatcher.combine (both layer pages); DeepseekV2MoE adds the shared
+ * expert with weight 1 and the routed part scaled by routed_scaling_factor
+ * (already folded into topk_weights here).
+ *   act, act_scale  from moe_grouped_gemm_w13_act.
+ *   w2         [E, H, I] (+ w2_scale [E, H/128, I/128] for fp8).
+ *   shared_w2  [H, I] (+ scale) or NULL.
+ *   topk_weights [T, K] fp32 from moe_topk; slot_to_row [T*K].
+ *   out        [T, H] out_dtype:  out_t = sum_k w_{t,k} y_{row(t,k)}
+ *              (+ y_{T*K+t} of the shared expert).  The sum over k runs in a
+ *              fixed order in fp32, so results are bitwise reproducible.
+ * Errors: MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE. */
+int moe_grouped_gemm_w2_combine(const moe_params *p, const void *act,
+                                const float *act_scale, const void *w2,
+                                const float *w2_scale, const void *shared_w2,
+                                const float *shared_w2_scale,
+                                const int32_t *expert_offsets,
+                                const int32_t *sorted_slots,
+                                const int32_t *slot_to_row,
+                                const float *topk_weights, void *out,
+                                void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+/* The whole layer: routing, permutation, (fp8: input quantisation),
+ * w13 + SiLU-and-mul, w2 + weighted combine (+ shared expert).
+ * Passage: FusedMoE.forward_native(hidden_states, router_logits) (vLLM
+ * page); DeepseekV2MoE.forward_normal (SGLang deepseek_v2 page).
+ *   hidden [T, H] act dtype; router_logits [T, E] fp32; weights as above.
+ *   out [T, H] out_dtype.
+ *   topk_ids_out [T, K] int32 / topk_weights_out [T, K] fp32: optional
+ *   copies of the routing (NULL to skip).
+ *   workspace >= moe_workspace_size(p) bytes.
+ * Errors: as the calls it is made of. */
+int moe_forward(const moe_params *p, const void *hidden,
+                const float *router_logits,
+                const float *e_score_correction_bias, const void *w13,
+                const float *w13_scale, const void *w2, const float *w2_scale,
+                const void *shared_w13, const float *shared_w13_scale,
+                const void *shared_w2, const float *shared_w2_scale,
+                void *out, int32_t *topk_ids_out, float *topk_weights_out,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

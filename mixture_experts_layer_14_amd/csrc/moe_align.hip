@@ -1,0 +1,140 @@
+// moe_align.hip -- expert-contiguous, stable permutation of the T*K routing
+// slots (the dispatch step of FusedMoE.forward_impl on the SGLang layer
+// page: tokens grouped expert by expert before the expert GEMMs, combined
+// back to token order afterwards).
+//
+// A deterministic counting sort in three launches; no atomic decides an
+// order, so the result is bit-exact and independent of scheduling:
+//   1. histogram: one wave per chunk of slots counts the chunk's experts in
+//      LDS and writes counts[e][chunk];
+//   2. scan: one block turns the expert-major count matrix into exclusive
+//      prefix sums (the start of every (expert, chunk) run) and writes
+//      expert_offsets;
+//   3. scatter: one wave per chunk walks its slots 64 at a time, in order;
+//      equal experts inside a 64-slot step are matched with one ballot per
+//      bit of the expert id, so each slot learns how many earlier slots of
+//      the step share its expert (stable rank), and a per-chunk cursor in
+//      LDS carries the count from step to step.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int kAlignMaxExperts = 512;
+
+__global__ __launch_bounds__(64) void align_hist_kernel(const int32_t* __restrict__ ids, int64_t n,
+                                                        int E, int64_t chunk, int nchunks,
+                                                        int32_t* __restrict__ counts) {
+    __shared__ int32_t cnt[kAlignMaxExperts];
+    const int lane = threadIdx.x;
+    const int c = blockIdx.x;
+    for (int e = lane; e < E; e += kWave) cnt[e] = 0;
+    __syncthreads();
+    const int64_t begin = static_cast<int64_t>(c) * chunk;
+    const int64_t end = begin + chunk < n ? begin + chunk : n;
+    for (int64_t i = begin + lane; i < end; i += kWave) {
+        const int e = ids[i];
+        if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+    for (int e = lane; e < E; e += kWave) counts[static_cast<int64_t>(e) * nchunks + c] = cnt[e];
+}
+
+// Exclusive scan over the E*nchunks counts in expert-major order, in place.
+__global__ __launch_bounds__(1024) void align_scan_kernel(int32_t* __restrict__ counts, int E,
+                                                          int nchunks,
+                                                          int32_t* __restrict__ offsets) {
+    __shared__ int32_t partial[1024];
+    const int tid = threadIdx.x;
+    const int64_t m = static_cast<int64_t>(E) * nchunks;
+    const int64_t per = (m + blockDim.x - 1) / blockDim.x;
+    const int64_t b = tid * per;
+    const int64_t e_ = b + per < m ? b + per : m;
+    int32_t s = 0;
+    for (int64_t i = b; i < e_; ++i) s += counts[i];
+    partial[tid] = s;
+    __syncthreads();
+    // Hillis-Steele inclusive scan of the per-thread sums
+    for (int off = 1; off < static_cast<int>(blockDim.x); off <<= 1) {
+        const int32_t v = tid >= off ? partial[tid - off] : 0;
+        __syncthreads();
+        partial[tid] += v;
+        __syncthreads();
+    }
+    int32_t run = tid > 0 ? partial[tid - 1] : 0;
+    for (int64_t i = b; i < e_; ++i) {
+        const int32_t c = counts[i];
+        counts[i] = run;
+        if (i % nchunks == 0) offsets[i / nchunks] = run;
+        run += c;
+    }
+    if (tid == static_cast<int>(blockDim.x) - 1) offsets[E] = partial[tid];
+}
+
+__global__ __launch_bounds__(64) void align_scatter_kernel(const int32_t* __restrict__ ids,
+                                                           int64_t n, int E, int64_t chunk,
+                                                           int nchunks,
+                                                           const int32_t* __restrict__ starts,
+                                                           int32_t* __restrict__ sorted_slots,
+                                                           int32_t* __restrict__ slot_to_row) {
+    __shared__ int32_t cursor[kAlignMaxExperts];
+    const int lane = threadIdx.x;
+    const int c = blockIdx.x;
+    for (int e = lane; e < E; e += kWave) cursor[e] = starts[static_cast<int64_t>(e) * nchunks + c];
+    __syncthreads();
+    const int64_t begin = static_cast<int64_t>(c) * chunk;
+    const int64_t end = begin + chunk < n ? begin + chunk : n;
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
+    for (int64_t base = begin; base < end; base += kWave) {
+        const int64_t i = base + lane;
+        int e = i < end ? ids[i] : -1;
+        const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(E);
+        if (!valid) e = kAlignMaxExperts;  // matches only other invalid lanes
+        uint64_t same = __ballot(valid) ;
+        same = valid ? same : ~same;
+#pragma unroll
+        for (int bit = 0; bit < 10; ++bit) {
+            const bool on = (e >> bit) & 1;
+            const uint64_t bal = __ballot(on);
+            same &= on ? bal : ~bal;
+        }
+        const int before = __popcll(same & lt_mask);
+        const int total = __popcll(same);
+        int32_t row = 0;
+        if (valid) row = cursor[e] + before;
+        __syncthreads();
+        if (valid) {
+            sorted_slots[row] = static_cast<int32_t>(i);
+            slot_to_row[i] = row;
+            if (before == total - 1) cursor[e] = row + 1;
+        }
+        __syncthreads();
+    }
+}
+
+int64_t align_chunk(int64_t n) {
+    // one wave per chunk, at most 256 chunks (keeps the scan matrix small)
+    int64_t chunk = 1024;
+    while ((n + chunk - 1) / chunk > 256) chunk *= 2;
+    return chunk;
+}
+
+size_t align_workspace_bytes(int64_t n, int E) {
+    const int64_t chunk = align_chunk(n);
+    const int64_t nchunks = n > 0 ? (n + chunk - 1) / chunk : 1;
+    return static_cast<size_t>(nchunks) * E * sizeof(int32_t);
+}
+
+hipError_t launch_align(const int32_t* ids, int64_t n, int E, int32_t* offsets,
+                        int32_t* sorted_slots, int32_t* slot_to_row, void* ws, hipStream_t stream) {
+    const int64_t chunk = align_chunk(n);
+    const int nchunks = static_cast<int>((n + chunk - 1) / chunk);
+    int32_t* counts = static_cast<int32_t*>(ws);
+    align_hist_kernel<<<nchunks, kWave, 0, stream>>>(ids, n, E, chunk, nchunks, counts);
+    align_scan_kernel<<<1, 1024, 0, stream>>>(counts, E, nchunks, offsets);
+    align_scatter_kernel<<<nchunks, kWave, 0, stream>>>(ids, n, E, chunk, nchunks, counts,
+                                                        sorted_slots, slot_to_row);
+    return hipGetLastError();
+}
+
+}  // namespace moe

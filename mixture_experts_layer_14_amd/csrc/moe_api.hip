@@ -1,0 +1,276 @@
+// moe_api.hip -- the C ABI (include/moe.h): host-side validation, workspace
+// layout and kernel launches.  Nothing here synchronises with the device or
+// allocates memory.
+#include <stdint.h>
+
+#include "../../include/moe.h"
+#include "moe_internal.h"
+
+namespace {
+
+constexpr int kMaxExperts = 512;
+constexpr int kMaxTopK = 32;
+constexpr int kMaxGroups = 64;
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+bool fp8_layer(const moe_params* p) { return p->weight_dtype == MOE_DTYPE_FP8_E4M3; }
+
+size_t act_elt(const moe_params* p) {
+    if (fp8_layer(p)) return 1;
+    return p->act_dtype == MOE_DTYPE_F32 ? 4 : 2;
+}
+
+int64_t routed_rows(const moe_params* p) { return p->num_tokens * p->top_k; }
+int64_t all_rows(const moe_params* p) {
+    return routed_rows(p) + (p->num_shared_experts ? p->num_tokens : 0);
+}
+
+// Shape/parameter checks shared by every call.
+int check_params(const moe_params* p) {
+    if (!p) return MOE_ERR_INVALID;
+    if (p->num_tokens < 0 || p->num_experts < 1 || p->num_experts > kMaxExperts) return MOE_ERR_INVALID;
+    if (p->top_k < 1 || p->top_k > p->num_experts) return MOE_ERR_INVALID;
+    if (p->top_k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
+    if (p->hidden_size <= 0 || p->intermediate_size <= 0) return MOE_ERR_INVALID;
+    if (p->scoring_func != MOE_SCORING_SOFTMAX && p->scoring_func != MOE_SCORING_SIGMOID)
+        return MOE_ERR_INVALID;
+    if (p->num_shared_experts < 0) return MOE_ERR_INVALID;
+    if (p->num_shared_experts > 1) return MOE_ERR_UNSUPPORTED;
+    const int G = p->num_expert_group;
+    if (G < 0) return MOE_ERR_INVALID;
+    if (G > 1) {
+        if (p->num_experts % G != 0) return MOE_ERR_INVALID;
+        if (p->topk_group < 1 || p->topk_group > G) return MOE_ERR_INVALID;
+        if (p->top_k > p->topk_group * (p->num_experts / G)) return MOE_ERR_INVALID;
+        if (G > kMaxGroups) return MOE_ERR_UNSUPPORTED;
+    }
+    const int a = p->act_dtype, w = p->weight_dtype, o = p->out_dtype;
+    const bool ok = (a == MOE_DTYPE_F32 && w == MOE_DTYPE_F32 && o == MOE_DTYPE_F32) ||
+                    (a == MOE_DTYPE_BF16 && w == MOE_DTYPE_BF16 && o == MOE_DTYPE_BF16) ||
+                    (a == MOE_DTYPE_BF16 && w == MOE_DTYPE_FP8_E4M3 && o == MOE_DTYPE_BF16);
+    if (a < 0 || a > 2 || w < 0 || w > 2 || o < 0 || o > 2) return MOE_ERR_INVALID;
+    if (!ok) return MOE_ERR_UNSUPPORTED;
+    const int mult = fp8_layer(p) ? 128 : 64;
+    if (p->hidden_size % mult || p->intermediate_size % mult) return MOE_ERR_INVALID;
+    // rows and element offsets held in int32 on the device
+    if (all_rows(p) >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+moe::GroupedProblem problem(const moe_params* p) {
+    moe::GroupedProblem g;
+    g.dtype = p->weight_dtype;
+    g.T = p->num_tokens;
+    g.K = p->top_k;
+    g.E = p->num_experts;
+    g.shared = p->num_shared_experts;
+    g.H = p->hidden_size;
+    g.I = p->intermediate_size;
+    return g;
+}
+
+size_t w13_scratch(const moe_params* p) { return moe::gemm_tile_workspace_bytes(problem(p)); }
+size_t w2_scratch(const moe_params* p) {
+    const moe::GroupedProblem g = problem(p);
+    return moe::gemm_tile_workspace_bytes(g) + moe::w2_rows_workspace_bytes(g);
+}
+size_t align_scratch(const moe_params* p) {
+    return align256(moe::align_workspace_bytes(routed_rows(p), p->num_experts));
+}
+
+// Workspace of moe_forward: routing, permutation, quantised input,
+// activations, then a scratch region reused by each stage.
+struct ForwardLayout {
+    size_t ids, weights, offsets, sorted, inv, xq, xs, act, act_scale, scratch, total;
+};
+
+ForwardLayout forward_layout(const moe_params* p) {
+    ForwardLayout L{};
+    const size_t TK = static_cast<size_t>(routed_rows(p));
+    const size_t T = static_cast<size_t>(p->num_tokens);
+    const size_t H = p->hidden_size, I = p->intermediate_size;
+    const size_t R = static_cast<size_t>(all_rows(p));
+    size_t off = 0;
+    L.ids = off; off += align256(TK * 4);
+    L.weights = off; off += align256(TK * 4);
+    L.offsets = off; off += align256((p->num_experts + 1) * 4);
+    L.sorted = off; off += align256(TK * 4);
+    L.inv = off; off += align256(TK * 4);
+    L.xq = off; off += fp8_layer(p) ? align256(T * H) : 0;
+    L.xs = off; off += fp8_layer(p) ? align256(T * (H / 128) * 4) : 0;
+    L.act = off; off += align256(R * I * act_elt(p));
+    L.act_scale = off; off += fp8_layer(p) ? align256(R * (I / 128) * 4) : 0;
+    L.scratch = off;
+    size_t s = align_scratch(p);
+    if (w13_scratch(p) > s) s = w13_scratch(p);
+    if (w2_scratch(p) > s) s = w2_scratch(p);
+    L.total = off + s;
+    return L;
+}
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return MOE_OK;
+    if (e == hipErrorNotSupported) return MOE_ERR_UNSUPPORTED;
+    return MOE_ERR_HIP;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+int check_topk_args(const moe_params* p, const float* logits, const float* bias, const int32_t* ids,
+                    const float* w) {
+    if (!logits || !ids || !w) return MOE_ERR_INVALID;
+    if (bias && p->scoring_func != MOE_SCORING_SIGMOID) return MOE_ERR_INVALID;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+        case MOE_ERR_WORKSPACE: return "workspace too small";
+        case MOE_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+size_t moe_workspace_size(const moe_params* p) {
+    if (check_params(p) != MOE_OK) return 0;
+    return forward_layout(p).total;
+}
+
+int moe_topk(const moe_params* p, const float* router_logits, const float* e_score_correction_bias,
+             int32_t* topk_ids, float* topk_weights, void* stream) {
+    int st = check_params(p);
+    if (st != MOE_OK) return st;
+    if (p->num_tokens == 0) return MOE_OK;  // empty batch: nothing to do
+    st = check_topk_args(p, router_logits, e_score_correction_bias, topk_ids, topk_weights);
+    if (st != MOE_OK) return st;
+    const int G = p->num_expert_group > 1 ? p->num_expert_group : 1;
+    return hip_status(moe::launch_topk(router_logits, e_score_correction_bias, p->num_tokens,
+                                       p->num_experts, p->top_k, p->scoring_func,
+                                       p->renormalize ? 1 : 0, G, G > 1 ? p->topk_group : 1,
+                                       p->routed_scaling_factor, topk_ids, topk_weights,
+                                       as_stream(stream)));
+}
+
+int moe_align_permute(const moe_params* p, const int32_t* topk_ids, int32_t* expert_offsets,
+                      int32_t* sorted_slots, int32_t* slot_to_row, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    int st = check_params(p);
+    if (st != MOE_OK) return st;
+    if (p->num_tokens == 0) return MOE_OK;  // empty batch: nothing to do
+    if (!topk_ids || !expert_offsets || !sorted_slots || !slot_to_row) return MOE_ERR_INVALID;
+    if (!workspace || workspace_bytes < align_scratch(p)) return MOE_ERR_WORKSPACE;
+    return hip_status(moe::launch_align(topk_ids, routed_rows(p), p->num_experts, expert_offsets,
+                                        sorted_slots, slot_to_row, workspace, as_stream(stream)));
+}
+
+int moe_quant_act_fp8(const moe_params* p, const void* hidden, uint8_t* q, float* scale,
+                      void* stream) {
+    int st = check_params(p);
+    if (st != MOE_OK) return st;
+    if (p->num_tokens == 0) return MOE_OK;  // empty batch: nothing to do
+    if (!hidden || !q || !scale) return MOE_ERR_INVALID;
+    if (p->act_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (p->hidden_size % 128) return MOE_ERR_INVALID;
+    return hip_status(moe::launch_quant_fp8(hidden, p->num_tokens, p->hidden_size, q, scale,
+                                            as_stream(stream)));
+}
+
+int moe_grouped_gemm_w13_act(const moe_params* p, const void* hidden, const float* hidden_scale,
+                             const void* w13, const float* w13_scale, const void* shared_w13,
+                             const float* shared_w13_scale, const int32_t* expert_offsets,
+                             const int32_t* sorted_slots, void* act, float* act_scale,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_params(p);
+    if (st != MOE_OK) return st;
+    if (p->num_tokens == 0) return MOE_OK;  // empty batch: nothing to do
+    if (!hidden || !w13 || !expert_offsets || !sorted_slots || !act) return MOE_ERR_INVALID;
+    if (p->num_shared_experts && !shared_w13) return MOE_ERR_INVALID;
+    if (fp8_layer(p) && (!hidden_scale || !w13_scale || !act_scale ||
+                         (p->num_shared_experts && !shared_w13_scale)))
+        return MOE_ERR_INVALID;
+    if (!workspace || workspace_bytes < w13_scratch(p)) return MOE_ERR_WORKSPACE;
+    return hip_status(moe::launch_w13(problem(p), hidden, hidden_scale, w13, w13_scale, shared_w13,
+                                      shared_w13_scale, expert_offsets, sorted_slots, act,
+                                      act_scale, workspace, as_stream(stream)));
+}
+
+int moe_grouped_gemm_w2_combine(const moe_params* p, const void* act, const float* act_scale,
+                                const void* w2, const float* w2_scale, const void* shared_w2,
+                                const float* shared_w2_scale, const int32_t* expert_offsets,
+                                const int32_t* sorted_slots, const int32_t* slot_to_row,
+                                const float* topk_weights, void* out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    int st = check_params(p);
+    if (st != MOE_OK) return st;
+    if (p->num_tokens == 0) return MOE_OK;  // empty batch: nothing to do
+    if (!act || !w2 || !expert_offsets || !sorted_slots || !slot_to_row || !topk_weights || !out)
+        return MOE_ERR_INVALID;
+    if (p->num_shared_experts && !shared_w2) return MOE_ERR_INVALID;
+    if (fp8_layer(p) && (!act_scale || !w2_scale || (p->num_shared_experts && !shared_w2_scale)))
+        return MOE_ERR_INVALID;
+    if (!workspace || workspace_bytes < w2_scratch(p)) return MOE_ERR_WORKSPACE;
+    return hip_status(moe::launch_w2_combine(problem(p), act, act_scale, w2, w2_scale, shared_w2,
+                                             shared_w2_scale, expert_offsets, sorted_slots,
+                                             slot_to_row, topk_weights, out, workspace,
+                                             as_stream(stream)));
+}
+
+int moe_forward(const moe_params* p, const void* hidden, const float* router_logits,
+                const float* e_score_correction_bias, const void* w13, const float* w13_scale,
+                const void* w2, const float* w2_scale, const void* shared_w13,
+                const float* shared_w13_scale, const void* shared_w2,
+                const float* shared_w2_scale, void* out, int32_t* topk_ids_out,
+                float* topk_weights_out, void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_params(p);
+    if (st != MOE_OK) return st;
+    if (p->num_tokens == 0) return MOE_OK;  // empty batch: nothing to do
+    if (!hidden || !router_logits || !w13 || !w2 || !out) return MOE_ERR_INVALID;
+    if (e_score_correction_bias && p->scoring_func != MOE_SCORING_SIGMOID) return MOE_ERR_INVALID;
+    if (p->num_shared_experts && (!shared_w13 || !shared_w2)) return MOE_ERR_INVALID;
+    if (fp8_layer(p) && (!w13_scale || !w2_scale ||
+                         (p->num_shared_experts && (!shared_w13_scale || !shared_w2_scale))))
+        return MOE_ERR_INVALID;
+    const ForwardLayout L = forward_layout(p);
+    if (!workspace || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
+    float* wts = topk_weights_out ? topk_weights_out : reinterpret_cast<float*>(ws + L.weights);
+    int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+    int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.sorted);
+    int32_t* inv = reinterpret_cast<int32_t*>(ws + L.inv);
+    void* scratch = ws + L.scratch;
+    const size_t scratch_bytes = L.total - L.scratch;
+
+    st = moe_topk(p, router_logits, e_score_correction_bias, ids, wts, stream);
+    if (st != MOE_OK) return st;
+    st = moe_align_permute(p, ids, offsets, sorted, inv, scratch, scratch_bytes, stream);
+    if (st != MOE_OK) return st;
+    const void* a1 = hidden;
+    const float* a1_scale = nullptr;
+    if (fp8_layer(p)) {
+        uint8_t* xq = ws + L.xq;
+        float* xs = reinterpret_cast<float*>(ws + L.xs);
+        st = moe_quant_act_fp8(p, hidden, xq, xs, stream);
+        if (st != MOE_OK) return st;
+        a1 = xq;
+        a1_scale = xs;
+    }
+    void* act = ws + L.act;
+    float* act_scale = fp8_layer(p) ? reinterpret_cast<float*>(ws + L.act_scale) : nullptr;
+    st = moe_grouped_gemm_w13_act(p, a1, a1_scale, w13, w13_scale, shared_w13, shared_w13_scale,
+                                  offsets, sorted, act, act_scale, scratch, scratch_bytes, stream);
+    if (st != MOE_OK) return st;
+    return moe_grouped_gemm_w2_combine(p, act, act_scale, w2, w2_scale, shared_w2, shared_w2_scale,
+                                       offsets, sorted, inv, wts, out, scratch, scratch_bytes,
+                                       stream);
+}
+
+}  // extern "C"

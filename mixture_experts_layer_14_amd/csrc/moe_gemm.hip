@@ -1,0 +1,448 @@
+// moe_gemm.hip -- the two grouped expert GEMMs of the fused MoE forward on
+// CDNA4 matrix cores, plus the tile schedule and the weighted combine.
+//
+// Operation (vLLM docs page "vllm.model_executor.layers.fused_moe.layer",
+// FusedMoE: w13 [E, 2I, H] holds w1 (gate) rows then w3 (up) rows per
+// _load_w13, w2 [E, H, I] is down_proj, activation "silu" with
+// is_act_and_mul; SGLang page "srt/models/deepseek_v2.py", DeepseekV2MLP:
+// gate_up_proj -> SiluAndMul -> down_proj):
+//   w13:  act[r, n] = silu(x_t . w13[e, n, :]) * (x_t . w13[e, I + n, :])
+//         for row r of expert e's segment, t = token of sorted_slots[r];
+//   w2:   y[r, h]   = w_r * (act[r, :] . w2[e, h, :]),  w_r = routing weight;
+//   combine: out[t, h] = sum_k y[row(t, k), h]  (+ shared expert row).
+//
+// Both GEMMs are "NT": A rows and B rows are contiguous along the reduction
+// dimension, which is what the MFMA operand layout wants (each lane holds a
+// 16-byte run of one row).  A block computes a BM x BN tile with WM x WN
+// waves; every k-iteration stages 128 bytes of each A row and each B row in
+// LDS (rows padded to 144 bytes), double-buffered through registers so the
+// next iteration's global loads are in flight during the MFMAs.  The w13
+// tile loads gate rows and up rows in interleaved 16-row blocks, so the
+// MFMA tile holding gate columns and the one holding the matching up
+// columns sit in the same lanes and SiLU-and-mul happens in registers.
+#include "moe_device.h"
+#include "moe_internal.h"
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// tile schedule: the m-tiles of every expert segment, built on the device
+// from expert_offsets so no host synchronisation is needed.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets,
+                                                           int E, int32_t shared_rows,
+                                                           int32_t shared_base, int BM,
+                                                           Tile* __restrict__ tiles,
+                                                           int32_t* __restrict__ num_tiles) {
+    __shared__ int32_t scan[1024];
+    const int g = threadIdx.x;  // group: expert g, or the shared expert at g == E
+    int32_t r0 = 0, r1 = 0;
+    if (g < E) {
+        // clamp to [0, routed rows] so the table can never outgrow its buffer
+        r0 = min(max(offsets[g], 0), shared_base);
+        r1 = min(max(offsets[g + 1], r0), shared_base);
+    } else if (g == E) {
+        r0 = shared_base;
+        r1 = shared_base + shared_rows;
+    }
+    const int32_t nt = (r1 - r0 + BM - 1) / BM;
+    scan[g] = nt;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int32_t v = g >= off ? scan[g - off] : 0;
+        __syncthreads();
+        scan[g] += v;
+        __syncthreads();
+    }
+    const int32_t start = scan[g] - nt;
+    for (int32_t j = 0; j < nt; ++j) {
+        Tile t;
+        t.expert = g;
+        t.row0 = r0 + j * BM;
+        t.row1 = r0 + (j + 1) * BM < r1 ? r0 + (j + 1) * BM : r1;
+        t.pad = 0;
+        tiles[start + j] = t;
+    }
+    if (g == 1023) *num_tiles = scan[1023];
+}
+
+// ---------------------------------------------------------------------------
+// MFMA policies: how two 16-byte fragments per lane (bytes [0,64) and
+// [64,128) of a 128-byte k-slab, lane group l/16 owning 16 bytes of each)
+// feed the matrix core.  A and B use the same lane->k mapping, so the dot
+// products are exact whatever order the hardware sums k in.
+// ---------------------------------------------------------------------------
+
+struct PolBF16 {
+    static constexpr int kElt = 2;
+    __device__ static __forceinline__ void mma(f32x4& acc, const uint4 (&a)[2], const uint4 (&b)[2]) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[s]),
+                                                          __builtin_bit_cast(bf16x8, b[s]), acc,
+                                                          0, 0, 0);
+    }
+    __device__ static __forceinline__ void store(void* base, int64_t idx, float v) {
+        static_cast<uint16_t*>(base)[idx] = f32_to_bf16_bits(v);
+    }
+    __device__ static __forceinline__ float load(const void* base, int64_t idx) {
+        return bf16_bits_to_f32(static_cast<const uint16_t*>(base)[idx]);
+    }
+};
+
+struct PolF32 {
+    static constexpr int kElt = 4;
+    __device__ static __forceinline__ void mma(f32x4& acc, const uint4 (&a)[2], const uint4 (&b)[2]) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const f32x4 av = __builtin_bit_cast(f32x4, a[s]);
+            const f32x4 bv = __builtin_bit_cast(f32x4, b[s]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], bv[j], acc, 0, 0, 0);
+        }
+    }
+    __device__ static __forceinline__ void store(void* base, int64_t idx, float v) {
+        static_cast<float*>(base)[idx] = v;
+    }
+    __device__ static __forceinline__ float load(const void* base, int64_t idx) {
+        return static_cast<const float*>(base)[idx];
+    }
+};
+
+enum { kModeW13 = 0, kModeW2 = 1 };
+
+struct GemmArgs {
+    const uint8_t* A;           // hidden [T, H] (w13) or act [R, I] (w2)
+    const int32_t* sorted_slots;
+    const uint8_t* B;           // expert weights [E, N, Kd]
+    const uint8_t* B_shared;    // shared expert weights [N, Kd] or null
+    const Tile* tiles;
+    const int32_t* num_tiles;
+    const float* topk_weights;  // w2: routing weight of each slot
+    void* C;                    // act [R, I] (w13) or y [R, H] (w2)
+    int64_t T;
+    int64_t routed_rows;        // T * K
+    int32_t topk;
+    int32_t Kd;                 // reduction length (elements)
+    int32_t N;                  // rows of one expert's weight matrix (2I or H)
+    int32_t I;
+    int32_t E;
+    int32_t n_tiles_n;          // tiles along N
+    int32_t max_m_tiles;
+};
+
+constexpr int kRowBytes = 128;               // bytes of one row per k-iteration
+constexpr int kLdsStride = kRowBytes + 16;   // padded row pitch in LDS
+constexpr int kChunks = kRowBytes / 16;      // 16-byte chunks per row
+
+template <class Pol, int BM, int BN, int WM, int WN, int MODE>
+__global__ __launch_bounds__(WM* WN* kWave) void grouped_gemm_kernel(GemmArgs g) {
+    constexpr int NT = WM * WN * kWave;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int TM = WTM / 16, TN = WTN / 16;
+    constexpr int A_ITEMS = (BM * kChunks + NT - 1) / NT;
+    constexpr int B_ITEMS = (BN * kChunks + NT - 1) / NT;
+    static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be a multiple of 16");
+    static_assert(MODE != kModeW13 || TN % 2 == 0, "w13 wave tile holds gate/up pairs");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2][(BM + BN) * kLdsStride];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int wm = wave / WN, wn = wave % WN;
+
+    // block -> (m-tile, n-tile); m-tiles of one n-tile are adjacent so the
+    // blocks sharing a weight tile run close together in time
+    const int m_tile = blockIdx.x % g.max_m_tiles;
+    const int n_tile = blockIdx.x / g.max_m_tiles;
+    if (m_tile >= *g.num_tiles) return;
+    const Tile tl = g.tiles[m_tile];
+    const int64_t eltK = static_cast<int64_t>(g.Kd) * Pol::kElt;  // bytes per row
+    const uint8_t* Bexp = tl.expert < g.E
+                              ? g.B + static_cast<int64_t>(tl.expert) * g.N * eltK
+                              : g.B_shared;
+
+    // fixed global row addresses of this thread's load chunks
+    const uint8_t* a_ptr[A_ITEMS];
+    const uint8_t* b_ptr[B_ITEMS];
+    bool a_on[A_ITEMS], b_on[B_ITEMS];
+#pragma unroll
+    for (int q = 0; q < A_ITEMS; ++q) {
+        const int c = tid + q * NT;
+        a_on[q] = c < BM * kChunks;
+        const int row = c / kChunks, c16 = c % kChunks;
+        int64_t r = tl.row0 + row;
+        if (r >= tl.row1) r = tl.row0;  // ragged tail: load a valid row, never stored
+        int64_t src;
+        if (MODE == kModeW13) {
+            src = r >= g.routed_rows ? r - g.routed_rows : g.sorted_slots[r] / g.topk;
+            src = src < 0 ? 0 : (src >= g.T ? g.T - 1 : src);
+        } else {
+            src = r;
+        }
+        a_ptr[q] = g.A + src * eltK + c16 * 16;
+    }
+#pragma unroll
+    for (int q = 0; q < B_ITEMS; ++q) {
+        const int c = tid + q * NT;
+        b_on[q] = c < BN * kChunks;
+        const int row = c / kChunks, c16 = c % kChunks;
+        int64_t wrow;
+        if (MODE == kModeW13) {
+            const int blk = row / 16, pair = blk / 2, up = blk % 2;
+            const int64_t col = static_cast<int64_t>(n_tile) * (BN / 2) + pair * 16 + row % 16;
+            wrow = up ? g.I + col : col;
+        } else {
+            wrow = static_cast<int64_t>(n_tile) * BN + row;
+        }
+        b_ptr[q] = Bexp + wrow * eltK + c16 * 16;
+    }
+
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    uint4 ra[A_ITEMS], rb[B_ITEMS];
+#pragma unroll
+    for (int q = 0; q < A_ITEMS; ++q)
+        if (a_on[q]) ra[q] = *reinterpret_cast<const uint4*>(a_ptr[q]);
+#pragma unroll
+    for (int q = 0; q < B_ITEMS; ++q)
+        if (b_on[q]) rb[q] = *reinterpret_cast<const uint4*>(b_ptr[q]);
+
+    const int nk = static_cast<int>(eltK / kRowBytes);
+    for (int it = 0; it < nk; ++it) {
+        uint8_t* sA = smem[it & 1];
+        uint8_t* sB = sA + BM * kLdsStride;
+#pragma unroll
+        for (int q = 0; q < A_ITEMS; ++q) {
+            const int c = tid + q * NT;
+            if (a_on[q]) *reinterpret_cast<uint4*>(sA + (c / kChunks) * kLdsStride + (c % kChunks) * 16) = ra[q];
+        }
+#pragma unroll
+        for (int q = 0; q < B_ITEMS; ++q) {
+            const int c = tid + q * NT;
+            if (b_on[q]) *reinterpret_cast<uint4*>(sB + (c / kChunks) * kLdsStride + (c % kChunks) * 16) = rb[q];
+        }
+        __syncthreads();
+        if (it + 1 < nk) {
+            const int64_t off = static_cast<int64_t>(it + 1) * kRowBytes;
+#pragma unroll
+            for (int q = 0; q < A_ITEMS; ++q)
+                if (a_on[q]) ra[q] = *reinterpret_cast<const uint4*>(a_ptr[q] + off);
+#pragma unroll
+            for (int q = 0; q < B_ITEMS; ++q)
+                if (b_on[q]) rb[q] = *reinterpret_cast<const uint4*>(b_ptr[q] + off);
+        }
+        uint4 af[TM][2], bf[TN][2];
+        const int lrow = lane % 16, lk = (lane / 16) * 16;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                af[i][s] = *reinterpret_cast<const uint4*>(sA + (wm * WTM + i * 16 + lrow) * kLdsStride + s * 64 + lk);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                bf[j][s] = *reinterpret_cast<const uint4*>(sB + (wn * WTN + j * 16 + lrow) * kLdsStride + s * 64 + lk);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) Pol::mma(acc[i][j], af[i], bf[j]);
+    }
+
+    // epilogue: lane holds rows 4*(lane/16)+q, column lane%16 of each 16x16 tile
+    const int ccol = lane % 16;
+    const int crow = (lane / 16) * 4;
+    if (MODE == kModeW13) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int p = 0; p < TN / 2; ++p) {
+                const int64_t col = static_cast<int64_t>(n_tile) * (BN / 2) + (wn * (TN / 2) + p) * 16 + ccol;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t r = tl.row0 + wm * WTM + i * 16 + crow + q;
+                    if (r < tl.row1)
+                        Pol::store(g.C, r * g.I + col, silu_mul(acc[i][2 * p][q], acc[i][2 * p + 1][q]));
+                }
+            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t r = tl.row0 + wm * WTM + i * 16 + crow + q;
+                if (r >= tl.row1) continue;
+                const float w = r < g.routed_rows ? g.topk_weights[g.sorted_slots[r]] : 1.0f;
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int64_t col = static_cast<int64_t>(n_tile) * BN + wn * WTN + j * 16 + ccol;
+                    Pol::store(g.C, r * g.N + col, acc[i][j][q] * w);
+                }
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// combine: out[t, :] = sum_k y[row(t,k), :] (+ y[T*K + t, :]), fixed order
+// ---------------------------------------------------------------------------
+
+template <class Pol>
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y,
+                                                      const int32_t* __restrict__ slot_to_row,
+                                                      int64_t T, int K, int H, int shared,
+                                                      int64_t rows, void* __restrict__ out) {
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t t = idx / H;
+    const int h = static_cast<int>(idx % H);
+    if (t >= T) return;
+    float s = 0.0f;
+    for (int k = 0; k < K; ++k) {
+        int64_t r = slot_to_row[t * K + k];
+        r = r < 0 ? 0 : (r >= rows ? rows - 1 : r);
+        s += Pol::load(y, r * H + h);
+    }
+    if (shared) s += Pol::load(y, (T * K + t) * H + h);
+    Pol::store(out, t * H + h, s);
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+
+namespace {
+
+int64_t total_rows(const GroupedProblem& p) { return p.T * p.K + (p.shared ? p.T : 0); }
+
+int max_m_tiles(const GroupedProblem& p, int BM) {
+    return static_cast<int>((total_rows(p) + BM - 1) / BM + p.E + 1);
+}
+
+// rows per active expert decides between weight-streaming and MFMA tiles
+bool small_m(const GroupedProblem& p) {
+    const int64_t slots = p.T * p.K;
+    const int64_t active = slots < p.E ? slots : p.E;
+    return slots <= 32 * active;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace
+
+size_t gemm_tile_workspace_bytes(const GroupedProblem& p) {
+    return align_up(256) + align_up(sizeof(Tile) * static_cast<size_t>(max_m_tiles(p, 16)));
+}
+
+size_t w2_rows_workspace_bytes(const GroupedProblem& p) {
+    const size_t elt = p.dtype == MOE_DTYPE_F32 ? 4 : 2;
+    return align_up(static_cast<size_t>(total_rows(p)) * p.H * elt);
+}
+
+template <class Pol, int BM, int BN, int WM, int WN, int MODE>
+static hipError_t launch_grouped(const GroupedProblem& p, GemmArgs g, const int32_t* offsets,
+                                 void* ws, hipStream_t stream) {
+    int32_t* num_tiles = static_cast<int32_t*>(ws);
+    Tile* tiles = reinterpret_cast<Tile*>(static_cast<uint8_t*>(ws) + 256);
+    build_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, p.E, p.shared ? static_cast<int32_t>(p.T) : 0,
+                                               static_cast<int32_t>(p.T * p.K), BM, tiles, num_tiles);
+    g.tiles = tiles;
+    g.num_tiles = num_tiles;
+    g.max_m_tiles = max_m_tiles(p, BM);
+    g.n_tiles_n = MODE == kModeW13 ? (2 * p.I) / BN : p.H / BN;
+    const int64_t blocks = static_cast<int64_t>(g.max_m_tiles) * g.n_tiles_n;
+    grouped_gemm_kernel<Pol, BM, BN, WM, WN, MODE><<<static_cast<unsigned>(blocks), WM * WN * kWave, 0, stream>>>(g);
+    return hipGetLastError();
+}
+
+template <class Pol>
+static hipError_t w13_for(const GroupedProblem& p, GemmArgs g, const int32_t* offsets, void* ws,
+                          hipStream_t stream) {
+    if (small_m(p) && (2 * p.I) % 128 == 0)
+        return launch_grouped<Pol, 16, 128, 1, 4, kModeW13>(p, g, offsets, ws, stream);
+    return launch_grouped<Pol, 128, 128, 2, 2, kModeW13>(p, g, offsets, ws, stream);
+}
+
+template <class Pol>
+static hipError_t w2_for(const GroupedProblem& p, GemmArgs g, const int32_t* offsets, void* ws,
+                         hipStream_t stream) {
+    if (p.H % 128 != 0) return launch_grouped<Pol, 16, 64, 1, 4, kModeW2>(p, g, offsets, ws, stream);
+    if (small_m(p)) return launch_grouped<Pol, 16, 128, 1, 4, kModeW2>(p, g, offsets, ws, stream);
+    return launch_grouped<Pol, 128, 128, 2, 2, kModeW2>(p, g, offsets, ws, stream);
+}
+
+hipError_t launch_w13(const GroupedProblem& p, const void* hidden, const float* hidden_scale,
+                      const void* w13, const float* w13_scale, const void* shared_w13,
+                      const float* shared_w13_scale, const int32_t* offsets,
+                      const int32_t* sorted_slots, void* act, float* act_scale, void* ws,
+                      hipStream_t stream) {
+    (void)hidden_scale; (void)w13_scale; (void)shared_w13_scale; (void)act_scale;
+    GemmArgs g{};
+    g.A = static_cast<const uint8_t*>(hidden);
+    g.sorted_slots = sorted_slots;
+    g.B = static_cast<const uint8_t*>(w13);
+    g.B_shared = static_cast<const uint8_t*>(shared_w13);
+    g.C = act;
+    g.T = p.T;
+    g.routed_rows = p.T * p.K;
+    g.topk = p.K;
+    g.Kd = p.H;
+    g.N = 2 * p.I;
+    g.I = p.I;
+    g.E = p.E;
+    if (p.dtype == MOE_DTYPE_BF16) return w13_for<PolBF16>(p, g, offsets, ws, stream);
+    if (p.dtype == MOE_DTYPE_F32) return w13_for<PolF32>(p, g, offsets, ws, stream);
+    return hipErrorNotSupported;
+}
+
+hipError_t launch_w2_combine(const GroupedProblem& p, const void* act, const float* act_scale,
+                             const void* w2, const float* w2_scale, const void* shared_w2,
+                             const float* shared_w2_scale, const int32_t* offsets,
+                             const int32_t* sorted_slots, const int32_t* slot_to_row,
+                             const float* topk_weights, void* out, void* ws,
+                             hipStream_t stream) {
+    (void)act_scale; (void)w2_scale; (void)shared_w2_scale;
+    const size_t tile_bytes = gemm_tile_workspace_bytes(p);
+    void* y = static_cast<uint8_t*>(ws) + tile_bytes;
+    GemmArgs g{};
+    g.A = static_cast<const uint8_t*>(act);
+    g.sorted_slots = sorted_slots;
+    g.B = static_cast<const uint8_t*>(w2);
+    g.B_shared = static_cast<const uint8_t*>(shared_w2);
+    g.topk_weights = topk_weights;
+    g.C = y;
+    g.T = p.T;
+    g.routed_rows = p.T * p.K;
+    g.topk = p.K;
+    g.Kd = p.I;
+    g.N = p.H;
+    g.I = p.I;
+    g.E = p.E;
+    hipError_t err;
+    if (p.dtype == MOE_DTYPE_BF16)
+        err = w2_for<PolBF16>(p, g, offsets, ws, stream);
+    else if (p.dtype == MOE_DTYPE_F32)
+        err = w2_for<PolF32>(p, g, offsets, ws, stream);
+    else
+        return hipErrorNotSupported;
+    if (err != hipSuccess) return err;
+    const int64_t n = p.T * p.H;
+    const unsigned blocks = static_cast<unsigned>((n + 255) / 256);
+    if (p.dtype == MOE_DTYPE_BF16)
+        combine_kernel<PolBF16><<<blocks, 256, 0, stream>>>(y, slot_to_row, p.T, p.K, p.H, p.shared, total_rows(p), out);
+    else
+        combine_kernel<PolF32><<<blocks, 256, 0, stream>>>(y, slot_to_row, p.T, p.K, p.H, p.shared, total_rows(p), out);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_fp8(const void*, int64_t, int, uint8_t*, float*, hipStream_t) {
+    return hipErrorNotSupported;
+}
+
+}  // namespace moe

@@ -1,0 +1,61 @@
+// moe_internal.h -- host-side interface between the kernel translation units
+// and the C ABI layer (not installed; the public interface is include/moe.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// One m-tile of the grouped GEMMs: rows [row0, row1) of the permuted order,
+// all owned by `expert` (expert == E denotes the shared expert).
+struct Tile {
+    int32_t expert;
+    int32_t row0;
+    int32_t row1;
+    int32_t pad;
+};
+
+hipError_t launch_topk(const float* logits, const float* bias, int64_t T, int E, int K,
+                       int scoring, int renorm, int G, int TG, float rsf, int32_t* ids,
+                       float* weights, hipStream_t stream);
+
+int64_t align_chunk(int64_t n);
+size_t align_workspace_bytes(int64_t n, int E);
+hipError_t launch_align(const int32_t* ids, int64_t n, int E, int32_t* offsets,
+                        int32_t* sorted_slots, int32_t* slot_to_row, void* ws,
+                        hipStream_t stream);
+
+// Grouped GEMM problem shared by the two expert GEMMs.
+struct GroupedProblem {
+    int dtype;             // MOE_DTYPE_* of A and B (F32, BF16, FP8_E4M3)
+    int64_t T;             // tokens
+    int K;                 // top_k
+    int E;                 // routed experts
+    int shared;            // 0/1 shared expert (rows T*K .. T*K+T-1)
+    int H, I;              // hidden, intermediate
+};
+
+// Scratch bytes of one grouped GEMM launch (tile table).
+size_t gemm_tile_workspace_bytes(const GroupedProblem& p);
+// Scratch bytes of the w2 GEMM's per-row outputs before the combine.
+size_t w2_rows_workspace_bytes(const GroupedProblem& p);
+
+hipError_t launch_w13(const GroupedProblem& p, const void* hidden, const float* hidden_scale,
+                      const void* w13, const float* w13_scale, const void* shared_w13,
+                      const float* shared_w13_scale, const int32_t* offsets,
+                      const int32_t* sorted_slots, void* act, float* act_scale, void* ws,
+                      hipStream_t stream);
+
+hipError_t launch_w2_combine(const GroupedProblem& p, const void* act, const float* act_scale,
+                             const void* w2, const float* w2_scale, const void* shared_w2,
+                             const float* shared_w2_scale, const int32_t* offsets,
+                             const int32_t* sorted_slots, const int32_t* slot_to_row,
+                             const float* topk_weights, void* out, void* ws,
+                             hipStream_t stream);
+
+hipError_t launch_quant_fp8(const void* hidden, int64_t T, int H, uint8_t* q, float* scale,
+                            hipStream_t stream);
+
+}  // namespace moe

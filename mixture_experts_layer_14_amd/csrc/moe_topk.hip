@@ -1,0 +1,169 @@
+// moe_topk.hip -- router: top-k selection and routing weights, one 64-lane
+// wavefront per token.
+//
+// Operation (vLLM docs page "vllm.model_executor.layers.fused_moe.layer",
+// FusedMoE.select_experts; SGLang page "srt/models/deepseek_v2.py",
+// DeepseekV2MoE grouped top-k arguments and MoEGate correction bias):
+//   softmax: score = softmax(logits), selection key = logit (same order);
+//   sigmoid: score = sigmoid(logit), key = score + e_score_correction_bias;
+//   grouped: experts split into G contiguous groups; a group scores the sum
+//            of its two largest keys (with a bias) or its largest key; the TG
+//            best groups stay eligible;
+//   select K keys, descending, exact ties to the lower index;
+//   weight = score (renormalised over the K selected if asked) * rsf.
+//
+// Layout: lane l holds experts e = l + 64*v, v < VPL, so every row load is
+// a run of coalesced 256-byte wave accesses.  A selection round is one wave
+// arg-max over packed (ordered key bits << 32 | ~expert) 64-bit values.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+template <int VPL>
+__global__ __launch_bounds__(256) void topk_kernel(
+    const float* __restrict__ logits, const float* __restrict__ bias, int64_t T, int E, int K,
+    int scoring, int renorm, int G, int TG, float rsf, int32_t* __restrict__ ids,
+    float* __restrict__ weights) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (t >= T) return;  // wave-uniform exit
+    const float* row = logits + t * E;
+
+    float key[VPL], score[VPL];
+    bool cand[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+        const int e = lane + kWave * v;
+        cand[v] = e < E;
+        key[v] = cand[v] ? row[e] : -INFINITY;
+    }
+
+    float softmax_sum = 0.0f, softmax_max = 0.0f;
+    if (scoring == 0) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) m = fmaxf(m, key[v]);
+        m = wave_max_f32(m);
+        float s = 0.0f;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            score[v] = cand[v] ? expf(key[v] - m) : 0.0f;  // unnormalised
+            s += score[v];
+        }
+        softmax_sum = wave_sum_f32(s);
+        softmax_max = m;
+    } else {
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            const int e = lane + kWave * v;
+            score[v] = cand[v] ? 1.0f / (1.0f + expf(-key[v])) : 0.0f;
+            key[v] = cand[v] ? score[v] + (bias ? bias[e] : 0.0f) : -INFINITY;
+        }
+    }
+    (void)softmax_max;
+
+    if (G > 1) {
+        const int per = E / G;
+        float my_gscore = -INFINITY;
+        for (int g = 0; g < G; ++g) {
+            float b1 = -INFINITY, b2 = -INFINITY;
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) {
+                const int e = lane + kWave * v;
+                if (cand[v] && e / per == g) {
+                    const float k = key[v];
+                    if (k > b1) { b2 = b1; b1 = k; } else if (k > b2) { b2 = k; }
+                }
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                const float o1 = __shfl_xor(b1, o, kWave);
+                const float o2 = __shfl_xor(b2, o, kWave);
+                const float n1 = fmaxf(b1, o1);
+                const float n2 = fmaxf(fminf(b1, o1), fmaxf(b2, o2));
+                b1 = n1;
+                b2 = n2;
+            }
+            const float gs = (bias != nullptr && per >= 2) ? b1 + b2 : b1;
+            if (lane == g) my_gscore = gs;
+        }
+        uint64_t keep = 0;
+        for (int r = 0; r < TG; ++r) {
+            uint64_t packed = 0;
+            if (lane < G && !((keep >> lane) & 1ull))
+                packed = (static_cast<uint64_t>(ordered_bits(my_gscore)) << 32) |
+                         static_cast<uint32_t>(~static_cast<uint32_t>(lane));
+            packed = wave_max_u64(packed);
+            keep |= 1ull << (~static_cast<uint32_t>(packed));
+        }
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            const int e = lane + kWave * v;
+            cand[v] = cand[v] && ((keep >> (e / per)) & 1ull);
+        }
+    }
+
+    int my_id = 0;
+    float my_w = 0.0f, sel_sum = 0.0f;
+    for (int k = 0; k < K; ++k) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            const int e = lane + kWave * v;
+            if (cand[v]) {
+                const uint64_t p = (static_cast<uint64_t>(ordered_bits(key[v])) << 32) |
+                                   static_cast<uint32_t>(~static_cast<uint32_t>(e));
+                best = p > best ? p : best;
+            }
+        }
+        best = wave_max_u64(best);
+        const int e_sel = static_cast<int>(~static_cast<uint32_t>(best));
+        const int owner = e_sel & (kWave - 1);
+        const int v_sel = e_sel / kWave;
+        float s_mine = 0.0f;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            if (v == v_sel) {
+                s_mine = score[v];
+                if (lane == owner) cand[v] = false;
+            }
+        }
+        const float s_sel = __shfl(s_mine, owner, kWave);
+        sel_sum += s_sel;
+        if (lane == k) {
+            my_id = e_sel;
+            my_w = s_sel;
+        }
+    }
+
+    if (lane < K) {
+        float w;
+        if (renorm)
+            w = my_w / sel_sum;
+        else
+            w = scoring == 0 ? my_w / softmax_sum : my_w;
+        ids[t * K + lane] = my_id;
+        weights[t * K + lane] = w * rsf;
+    }
+}
+
+hipError_t launch_topk(const float* logits, const float* bias, int64_t T, int E, int K,
+                       int scoring, int renorm, int G, int TG, float rsf, int32_t* ids,
+                       float* weights, hipStream_t stream) {
+    const int waves_per_block = 4;
+    const dim3 block(kWave * waves_per_block);
+    const dim3 grid(static_cast<unsigned>((T + waves_per_block - 1) / waves_per_block));
+    const int vpl = (E + kWave - 1) / kWave;
+    if (vpl <= 1)
+        topk_kernel<1><<<grid, block, 0, stream>>>(logits, bias, T, E, K, scoring, renorm, G, TG, rsf, ids, weights);
+    else if (vpl <= 2)
+        topk_kernel<2><<<grid, block, 0, stream>>>(logits, bias, T, E, K, scoring, renorm, G, TG, rsf, ids, weights);
+    else if (vpl <= 4)
+        topk_kernel<4><<<grid, block, 0, stream>>>(logits, bias, T, E, K, scoring, renorm, G, TG, rsf, ids, weights);
+    else
+        topk_kernel<8><<<grid, block, 0, stream>>>(logits, bias, T, E, K, scoring, renorm, G, TG, rsf, ids, weights);
+    return hipGetLastError();
+}
+
+}  // namespace moe
