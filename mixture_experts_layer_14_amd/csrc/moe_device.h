@@ -15,6 +15,7 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;  // 16 bytes, kept in VGPRs
 
 // Order-preserving map of an fp32 value onto uint32 (larger float -> larger
 // integer; -inf maps above 0, so 0 is below every real key).

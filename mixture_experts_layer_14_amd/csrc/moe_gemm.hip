@@ -21,6 +21,7 @@
 // MFMA tile holding gate columns and the one holding the matching up
 // columns sit in the same lanes and SiLU-and-mul happens in registers.
 #include "moe_device.h"
+#include "moe_gemm_kernels.h"
 #include "moe_internal.h"
 #include "../../include/moe.h"
 
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
 
 struct PolBF16 {
     static constexpr int kElt = 2;
-    __device__ static __forceinline__ void mma(f32x4& acc, const uint4 (&a)[2], const uint4 (&b)[2]) {
+    __device__ static __forceinline__ void mma(f32x4& acc, const u32x4 (&a)[2], const u32x4 (&b)[2]) {
 #pragma unroll
         for (int s = 0; s < 2; ++s)
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[s]),
@@ -94,7 +95,7 @@ struct PolBF16 {
 
 struct PolF32 {
     static constexpr int kElt = 4;
-    __device__ static __forceinline__ void mma(f32x4& acc, const uint4 (&a)[2], const uint4 (&b)[2]) {
+    __device__ static __forceinline__ void mma(f32x4& acc, const u32x4 (&a)[2], const u32x4 (&b)[2]) {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const f32x4 av = __builtin_bit_cast(f32x4, a[s]);
@@ -111,32 +112,6 @@ struct PolF32 {
         return static_cast<const float*>(base)[idx];
     }
 };
-
-enum { kModeW13 = 0, kModeW2 = 1 };
-
-struct GemmArgs {
-    const uint8_t* A;           // hidden [T, H] (w13) or act [R, I] (w2)
-    const int32_t* sorted_slots;
-    const uint8_t* B;           // expert weights [E, N, Kd]
-    const uint8_t* B_shared;    // shared expert weights [N, Kd] or null
-    const Tile* tiles;
-    const int32_t* num_tiles;
-    const float* topk_weights;  // w2: routing weight of each slot
-    void* C;                    // act [R, I] (w13) or y [R, H] (w2)
-    int64_t T;
-    int64_t routed_rows;        // T * K
-    int32_t topk;
-    int32_t Kd;                 // reduction length (elements)
-    int32_t N;                  // rows of one expert's weight matrix (2I or H)
-    int32_t I;
-    int32_t E;
-    int32_t n_tiles_n;          // tiles along N
-    int32_t max_m_tiles;
-};
-
-constexpr int kRowBytes = 128;               // bytes of one row per k-iteration
-constexpr int kLdsStride = kRowBytes + 16;   // padded row pitch in LDS
-constexpr int kChunks = kRowBytes / 16;      // 16-byte chunks per row
 
 template <class Pol, int BM, int BN, int WM, int WN, int MODE>
 __global__ __launch_bounds__(WM* WN* kWave) void grouped_gemm_kernel(GemmArgs g) {
@@ -207,13 +182,13 @@ __global__ __launch_bounds__(WM* WN* kWave) void grouped_gemm_kernel(GemmArgs g)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    uint4 ra[A_ITEMS], rb[B_ITEMS];
+    u32x4 ra[A_ITEMS], rb[B_ITEMS];
 #pragma unroll
     for (int q = 0; q < A_ITEMS; ++q)
-        if (a_on[q]) ra[q] = *reinterpret_cast<const uint4*>(a_ptr[q]);
+        if (a_on[q]) ra[q] = *reinterpret_cast<const u32x4*>(a_ptr[q]);
 #pragma unroll
     for (int q = 0; q < B_ITEMS; ++q)
-        if (b_on[q]) rb[q] = *reinterpret_cast<const uint4*>(b_ptr[q]);
+        if (b_on[q]) rb[q] = *reinterpret_cast<const u32x4*>(b_ptr[q]);
 
     const int nk = static_cast<int>(eltK / kRowBytes);
     for (int it = 0; it < nk; ++it) {
@@ -222,35 +197,35 @@ __global__ __launch_bounds__(WM* WN* kWave) void grouped_gemm_kernel(GemmArgs g)
 #pragma unroll
         for (int q = 0; q < A_ITEMS; ++q) {
             const int c = tid + q * NT;
-            if (a_on[q]) *reinterpret_cast<uint4*>(sA + (c / kChunks) * kLdsStride + (c % kChunks) * 16) = ra[q];
+            if (a_on[q]) *reinterpret_cast<u32x4*>(sA + (c / kChunks) * kLdsStride + (c % kChunks) * 16) = ra[q];
         }
 #pragma unroll
         for (int q = 0; q < B_ITEMS; ++q) {
             const int c = tid + q * NT;
-            if (b_on[q]) *reinterpret_cast<uint4*>(sB + (c / kChunks) * kLdsStride + (c % kChunks) * 16) = rb[q];
+            if (b_on[q]) *reinterpret_cast<u32x4*>(sB + (c / kChunks) * kLdsStride + (c % kChunks) * 16) = rb[q];
         }
         __syncthreads();
         if (it + 1 < nk) {
             const int64_t off = static_cast<int64_t>(it + 1) * kRowBytes;
 #pragma unroll
             for (int q = 0; q < A_ITEMS; ++q)
-                if (a_on[q]) ra[q] = *reinterpret_cast<const uint4*>(a_ptr[q] + off);
+                if (a_on[q]) ra[q] = *reinterpret_cast<const u32x4*>(a_ptr[q] + off);
 #pragma unroll
             for (int q = 0; q < B_ITEMS; ++q)
-                if (b_on[q]) rb[q] = *reinterpret_cast<const uint4*>(b_ptr[q] + off);
+                if (b_on[q]) rb[q] = *reinterpret_cast<const u32x4*>(b_ptr[q] + off);
         }
-        uint4 af[TM][2], bf[TN][2];
+        u32x4 af[TM][2], bf[TN][2];
         const int lrow = lane % 16, lk = (lane / 16) * 16;
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int s = 0; s < 2; ++s)
-                af[i][s] = *reinterpret_cast<const uint4*>(sA + (wm * WTM + i * 16 + lrow) * kLdsStride + s * 64 + lk);
+                af[i][s] = *reinterpret_cast<const u32x4*>(sA + (wm * WTM + i * 16 + lrow) * kLdsStride + s * 64 + lk);
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int s = 0; s < 2; ++s)
-                bf[j][s] = *reinterpret_cast<const uint4*>(sB + (wn * WTN + j * 16 + lrow) * kLdsStride + s * 64 + lk);
+                bf[j][s] = *reinterpret_cast<const u32x4*>(sB + (wn * WTN + j * 16 + lrow) * kLdsStride + s * 64 + lk);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -325,11 +300,12 @@ int max_m_tiles(const GroupedProblem& p, int BM) {
     return static_cast<int>((total_rows(p) + BM - 1) / BM + p.E + 1);
 }
 
-// rows per active expert decides between weight-streaming and MFMA tiles
-bool small_m(const GroupedProblem& p) {
+// Average rows per expert that receives any: few rows -> weight streaming,
+// many rows -> MFMA tiles.
+int64_t rows_per_active_expert(const GroupedProblem& p) {
     const int64_t slots = p.T * p.K;
     const int64_t active = slots < p.E ? slots : p.E;
-    return slots <= 32 * active;
+    return (slots + active - 1) / active;
 }
 
 size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -345,9 +321,42 @@ size_t w2_rows_workspace_bytes(const GroupedProblem& p) {
     return align_up(static_cast<size_t>(total_rows(p)) * p.H * elt);
 }
 
-template <class Pol, int BM, int BN, int WM, int WN, int MODE>
-static hipError_t launch_grouped(const GroupedProblem& p, GemmArgs g, const int32_t* offsets,
-                                 void* ws, hipStream_t stream) {
+// Prefill tile configuration: block tile BM x BN on WM x WN waves, GM m-tiles
+// per L2 group, ROWB bytes of every row per pipeline stage.  Measured on
+// MI355X: 8 waves (two per SIMD) beat 4; 256 x 256 tiles pay off for the
+// gate/up GEMM once experts hold several hundred rows.
+#ifndef MOE_TILE_BM
+#define MOE_TILE_BM 128
+#endif
+#ifndef MOE_TILE_BN
+#define MOE_TILE_BN 256
+#endif
+#ifndef MOE_TILE_WM
+#define MOE_TILE_WM 2
+#endif
+#ifndef MOE_TILE_WN
+#define MOE_TILE_WN 4
+#endif
+#ifndef MOE_TILE_GM
+#define MOE_TILE_GM 8
+#endif
+#ifndef MOE_TILE_ROWB
+#define MOE_TILE_ROWB 128
+#endif
+#ifndef MOE_BIG_TILE_MIN_ROWS
+#define MOE_BIG_TILE_MIN_ROWS 768
+#endif
+// k-steps each streaming wave keeps in flight, and the largest average rows
+// per expert that still uses the streaming kernel.
+#ifndef MOE_STREAM_U
+#define MOE_STREAM_U 8
+#endif
+#ifndef MOE_STREAM_MAX_ROWS
+#define MOE_STREAM_MAX_ROWS 64
+#endif
+
+static void build_tiles(const GroupedProblem& p, const int32_t* offsets, int BM, GemmArgs& g,
+                        void* ws, hipStream_t stream) {
     int32_t* num_tiles = static_cast<int32_t*>(ws);
     Tile* tiles = reinterpret_cast<Tile*>(static_cast<uint8_t*>(ws) + 256);
     build_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, p.E, p.shared ? static_cast<int32_t>(p.T) : 0,
@@ -355,16 +364,62 @@ static hipError_t launch_grouped(const GroupedProblem& p, GemmArgs g, const int3
     g.tiles = tiles;
     g.num_tiles = num_tiles;
     g.max_m_tiles = max_m_tiles(p, BM);
+}
+
+// generic 16x16 MFMA kernel (the fp32 layers)
+template <class Pol, int BM, int BN, int WM, int WN, int MODE>
+static hipError_t launch_grouped(const GroupedProblem& p, GemmArgs g, const int32_t* offsets,
+                                 void* ws, hipStream_t stream) {
+    build_tiles(p, offsets, BM, g, ws, stream);
     g.n_tiles_n = MODE == kModeW13 ? (2 * p.I) / BN : p.H / BN;
     const int64_t blocks = static_cast<int64_t>(g.max_m_tiles) * g.n_tiles_n;
     grouped_gemm_kernel<Pol, BM, BN, WM, WN, MODE><<<static_cast<unsigned>(blocks), WM * WN * kWave, 0, stream>>>(g);
     return hipGetLastError();
 }
 
+template <int BM, int BN, int WM, int WN, int MODE>
+static hipError_t launch_tile(const GroupedProblem& p, GemmArgs g, const int32_t* offsets, void* ws,
+                              hipStream_t stream) {
+    build_tiles(p, offsets, BM, g, ws, stream);
+    g.n_tiles_n = MODE == kModeW13 ? (2 * p.I) / BN : p.H / BN;
+    const int64_t total = static_cast<int64_t>(g.max_m_tiles) * g.n_tiles_n;
+    const int64_t blocks = 8 * ((total + 7) / 8);
+    tile_kernel<BM, BN, WM, WN, (BM + BN >= 512 ? 64 : MOE_TILE_ROWB), MODE, MOE_TILE_GM><<<static_cast<unsigned>(blocks), WM * WN * kWave, 0, stream>>>(g);
+    return hipGetLastError();
+}
+
+template <int TM, int MODE>
+static hipError_t launch_stream(const GroupedProblem& p, GemmArgs g, const int32_t* offsets, void* ws,
+                                hipStream_t stream) {
+    build_tiles(p, offsets, TM * 16, g, ws, stream);
+    const int groups = MODE == kModeW13 ? p.I / 16 : p.H / 32;
+    const int64_t blocks = static_cast<int64_t>(g.max_m_tiles) * groups;
+    stream_kernel<TM, 2, MODE, MOE_STREAM_U><<<static_cast<unsigned>(blocks), 4 * kWave, 0, stream>>>(g);
+    return hipGetLastError();
+}
+
+template <int MODE>
+static hipError_t bf16_gemm(const GroupedProblem& p, GemmArgs g, const int32_t* offsets, void* ws,
+                            hipStream_t stream) {
+    const int64_t m = rows_per_active_expert(p);
+    if (m <= MOE_STREAM_MAX_ROWS) {
+        if (m <= 16) return launch_stream<1, MODE>(p, g, offsets, ws, stream);
+        if (m <= 32) return launch_stream<2, MODE>(p, g, offsets, ws, stream);
+        return launch_stream<4, MODE>(p, g, offsets, ws, stream);
+    }
+    const int n = MODE == kModeW13 ? 2 * p.I : p.H;
+    if (MODE == kModeW13 && m >= MOE_BIG_TILE_MIN_ROWS && n % 256 == 0)
+        return launch_tile<256, 256, 2, 4, MODE>(p, g, offsets, ws, stream);
+    if (n % MOE_TILE_BN == 0)
+        return launch_tile<MOE_TILE_BM, MOE_TILE_BN, MOE_TILE_WM, MOE_TILE_WN, MODE>(p, g, offsets, ws, stream);
+    if (n % 128 == 0) return launch_tile<128, 128, 2, 2, MODE>(p, g, offsets, ws, stream);  // 64 x 64 per wave
+    return launch_tile<128, 64, 2, 1, MODE>(p, g, offsets, ws, stream);
+}
+
 template <class Pol>
 static hipError_t w13_for(const GroupedProblem& p, GemmArgs g, const int32_t* offsets, void* ws,
                           hipStream_t stream) {
-    if (small_m(p) && (2 * p.I) % 128 == 0)
+    if (rows_per_active_expert(p) <= 16 && (2 * p.I) % 128 == 0)
         return launch_grouped<Pol, 16, 128, 1, 4, kModeW13>(p, g, offsets, ws, stream);
     return launch_grouped<Pol, 128, 128, 2, 2, kModeW13>(p, g, offsets, ws, stream);
 }
@@ -373,7 +428,7 @@ template <class Pol>
 static hipError_t w2_for(const GroupedProblem& p, GemmArgs g, const int32_t* offsets, void* ws,
                          hipStream_t stream) {
     if (p.H % 128 != 0) return launch_grouped<Pol, 16, 64, 1, 4, kModeW2>(p, g, offsets, ws, stream);
-    if (small_m(p)) return launch_grouped<Pol, 16, 128, 1, 4, kModeW2>(p, g, offsets, ws, stream);
+    if (rows_per_active_expert(p) <= 16) return launch_grouped<Pol, 16, 128, 1, 4, kModeW2>(p, g, offsets, ws, stream);
     return launch_grouped<Pol, 128, 128, 2, 2, kModeW2>(p, g, offsets, ws, stream);
 }
 
@@ -396,7 +451,7 @@ hipError_t launch_w13(const GroupedProblem& p, const void* hidden, const float* 
     g.N = 2 * p.I;
     g.I = p.I;
     g.E = p.E;
-    if (p.dtype == MOE_DTYPE_BF16) return w13_for<PolBF16>(p, g, offsets, ws, stream);
+    if (p.dtype == MOE_DTYPE_BF16) return bf16_gemm<kModeW13>(p, g, offsets, ws, stream);
     if (p.dtype == MOE_DTYPE_F32) return w13_for<PolF32>(p, g, offsets, ws, stream);
     return hipErrorNotSupported;
 }
@@ -426,7 +481,7 @@ hipError_t launch_w2_combine(const GroupedProblem& p, const void* act, const flo
     g.E = p.E;
     hipError_t err;
     if (p.dtype == MOE_DTYPE_BF16)
-        err = w2_for<PolBF16>(p, g, offsets, ws, stream);
+        err = bf16_gemm<kModeW2>(p, g, offsets, ws, stream);
     else if (p.dtype == MOE_DTYPE_F32)
         err = w2_for<PolF32>(p, g, offsets, ws, stream);
     else
