@@ -22,6 +22,7 @@
 // columns sit in the same lanes and SiLU-and-mul happens in registers.
 #include "moe_device.h"
 #include "moe_gemm_kernels.h"
+#include "moe_gemm_fp8.h"
 #include "moe_internal.h"
 #include "../../include/moe.h"
 
@@ -416,6 +417,28 @@ static hipError_t bf16_gemm(const GroupedProblem& p, GemmArgs g, const int32_t* 
     return launch_tile<128, 64, 2, 1, MODE>(p, g, offsets, ws, stream);
 }
 
+template <int BM, int BN, int WM, int WN, int MODE>
+static hipError_t launch_tile_fp8(const GroupedProblem& p, GemmArgs g, const int32_t* offsets,
+                                  void* ws, hipStream_t stream) {
+    build_tiles(p, offsets, BM, g, ws, stream);
+    g.n_tiles_n = MODE == kModeW13 ? (2 * p.I) / BN : p.H / BN;
+    const int64_t total = static_cast<int64_t>(g.max_m_tiles) * g.n_tiles_n;
+    const int64_t blocks = 8 * ((total + 7) / 8);
+    tile_kernel_fp8<BM, BN, WM, WN, MODE, MOE_TILE_GM><<<static_cast<unsigned>(blocks), WM * WN * kWave, 0, stream>>>(g);
+    return hipGetLastError();
+}
+
+template <int MODE>
+static hipError_t fp8_gemm(const GroupedProblem& p, GemmArgs g, const int32_t* offsets, void* ws,
+                           hipStream_t stream) {
+    if constexpr (MODE == kModeW13) {
+        return launch_tile_fp8<128, 256, 2, 4, MODE>(p, g, offsets, ws, stream);
+    } else {
+        if (p.H % 256 == 0) return launch_tile_fp8<128, 256, 2, 4, MODE>(p, g, offsets, ws, stream);
+        return launch_tile_fp8<128, 128, 2, 4, MODE>(p, g, offsets, ws, stream);
+    }
+}
+
 template <class Pol>
 static hipError_t w13_for(const GroupedProblem& p, GemmArgs g, const int32_t* offsets, void* ws,
                           hipStream_t stream) {
@@ -437,8 +460,11 @@ hipError_t launch_w13(const GroupedProblem& p, const void* hidden, const float* 
                       const float* shared_w13_scale, const int32_t* offsets,
                       const int32_t* sorted_slots, void* act, float* act_scale, void* ws,
                       hipStream_t stream) {
-    (void)hidden_scale; (void)w13_scale; (void)shared_w13_scale; (void)act_scale;
     GemmArgs g{};
+    g.A_scale = hidden_scale;
+    g.B_scale = w13_scale;
+    g.B_shared_scale = shared_w13_scale;
+    g.C_scale = act_scale;
     g.A = static_cast<const uint8_t*>(hidden);
     g.sorted_slots = sorted_slots;
     g.B = static_cast<const uint8_t*>(w13);
@@ -453,6 +479,7 @@ hipError_t launch_w13(const GroupedProblem& p, const void* hidden, const float* 
     g.E = p.E;
     if (p.dtype == MOE_DTYPE_BF16) return bf16_gemm<kModeW13>(p, g, offsets, ws, stream);
     if (p.dtype == MOE_DTYPE_F32) return w13_for<PolF32>(p, g, offsets, ws, stream);
+    if (p.dtype == MOE_DTYPE_FP8_E4M3) return fp8_gemm<kModeW13>(p, g, offsets, ws, stream);
     return hipErrorNotSupported;
 }
 
@@ -462,7 +489,6 @@ hipError_t launch_w2_combine(const GroupedProblem& p, const void* act, const flo
                              const int32_t* sorted_slots, const int32_t* slot_to_row,
                              const float* topk_weights, void* out, void* ws,
                              hipStream_t stream) {
-    (void)act_scale; (void)w2_scale; (void)shared_w2_scale;
     const size_t tile_bytes = gemm_tile_workspace_bytes(p);
     void* y = static_cast<uint8_t*>(ws) + tile_bytes;
     GemmArgs g{};
@@ -479,25 +505,27 @@ hipError_t launch_w2_combine(const GroupedProblem& p, const void* act, const flo
     g.N = p.H;
     g.I = p.I;
     g.E = p.E;
+    g.A_scale = act_scale;
+    g.B_scale = w2_scale;
+    g.B_shared_scale = shared_w2_scale;
     hipError_t err;
     if (p.dtype == MOE_DTYPE_BF16)
         err = bf16_gemm<kModeW2>(p, g, offsets, ws, stream);
     else if (p.dtype == MOE_DTYPE_F32)
         err = w2_for<PolF32>(p, g, offsets, ws, stream);
+    else if (p.dtype == MOE_DTYPE_FP8_E4M3)
+        err = fp8_gemm<kModeW2>(p, g, offsets, ws, stream);
     else
         return hipErrorNotSupported;
     if (err != hipSuccess) return err;
     const int64_t n = p.T * p.H;
     const unsigned blocks = static_cast<unsigned>((n + 255) / 256);
-    if (p.dtype == MOE_DTYPE_BF16)
+    if (p.dtype != MOE_DTYPE_F32)
         combine_kernel<PolBF16><<<blocks, 256, 0, stream>>>(y, slot_to_row, p.T, p.K, p.H, p.shared, total_rows(p), out);
     else
         combine_kernel<PolF32><<<blocks, 256, 0, stream>>>(y, slot_to_row, p.T, p.K, p.H, p.shared, total_rows(p), out);
     return hipGetLastError();
 }
 
-hipError_t launch_quant_fp8(const void*, int64_t, int, uint8_t*, float*, hipStream_t) {
-    return hipErrorNotSupported;
-}
 
 }  // namespace moe

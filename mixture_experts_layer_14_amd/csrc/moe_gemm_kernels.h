@@ -38,6 +38,12 @@ struct GemmArgs {
     int32_t E;
     int32_t n_tiles_n;          // tiles along N
     int32_t max_m_tiles;
+    // fp8 layers: per-(row, 128-group) scales of A, 128 x 128 block scales of
+    // B, and the per-(row, 128-group) scales written with the w13 output
+    const float* A_scale;       // [rows of A, Kd/128]
+    const float* B_scale;       // [E, N/128, Kd/128]
+    const float* B_shared_scale;  // [N/128, Kd/128]
+    float* C_scale;             // w13: [R, I/128]
 };
 
 constexpr int kRowBytes = 128;               // bytes of one row per k-iteration
