@@ -50,6 +50,20 @@ def w13_flops(cfg, T):
     return 4.0 * T * (cfg.K + cfg.shared) * cfg.H * cfg.I
 
 
+def w13_bytes(cfg, T, active_experts):
+    """Algorithmic bytes of one w13 launch: the gate/up weights of the experts
+    that received rows (+ block scales), each token's hidden row once, and the
+    activation rows written."""
+    wb = _weight_bytes(cfg)
+    per_expert = 2 * cfg.I * cfg.H * wb
+    if cfg.fp8:
+        per_expert += (2 * cfg.I // 128) * (cfg.H // 128) * 4
+    act_b = 1 if cfg.fp8 else (4 if cfg.act_dtype == "f32" else 2)
+    x_b = 4 if cfg.act_dtype == "f32" else 2
+    return (per_expert * (active_experts + cfg.shared) + T * cfg.H * x_b
+            + T * (cfg.K + cfg.shared) * cfg.I * act_b)
+
+
 def time_layer(cfg, T, steps, warmup):
     """Time `steps` passes of the whole layer through the library's entry
     points, with HIP events around the w13 GEMM on the stream it runs on."""
@@ -105,6 +119,53 @@ def time_layer(cfg, T, steps, warmup):
             "forward_ms_per_step": fwd_ms}
 
 
+def source_digest():
+    """sha256 over the HIP sources: identifies the kernels a stored counter
+    measurement belongs to."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mixture_experts_layer_14_amd", "csrc")
+    for path in sorted(glob.glob(os.path.join(csrc, "*"))):
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode())
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(kernel_key):
+    """HBM bytes per launch of `kernel_key` from profiles/hbm_traffic.md, if
+    that file was measured on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        line = line.strip().lstrip("-").strip()
+        if ":" in line and line.split(":", 1)[0].strip().replace("_", "").isalnum():
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("source_sha256") != source_digest():
+        return None
+    v = fields.get("%s_bytes_per_launch" % kernel_key)
+    return float(v) if v else None
+
+
+def calibrate_copy(nbytes=1 << 30, reps=3):
+    """A plain device-to-device copy of known size, for scaling the HBM byte
+    counters (FETCH_SIZE / WRITE_SIZE) of a profiler run."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}))
+
+
 def cpu_baseline(cfg, T, sample_tokens):
     """The CPU oracle, as it stands, on the first `sample_tokens` tokens of
     the same workload, on all host threads."""
@@ -146,6 +207,8 @@ def main():
     ap.add_argument("--decode-config", default="mixtral_decode")
     ap.add_argument("--cpu-sample", type=int, default=256)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build runs the whole expert set on a single "
@@ -159,6 +222,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     binding.load()
     cfg = synth.CONFIGS[args.config]
     T = cfg.T
@@ -188,7 +254,7 @@ def main():
         "active_experts": r["active_experts"],
         "roofline": {"kernel": "w13 grouped GEMM + SiLU-and-mul", "bound": "mfma",
                      "achieved": w13_tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": w13_tflops / peak, "traffic": None,
+                     "frac": w13_tflops / peak, "traffic": stored_traffic("%s_w13" % cfg.name),
                      "avg_kernel_ms": r["w13_ms"]},
     }
     if args.decode_config:
@@ -202,6 +268,13 @@ def main():
                           "hbm_GBps": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
                           "algorithmic_bytes": byts, "active_experts": d["active_experts"],
                           "forward_ms_per_step": d["forward_ms_per_step"]}
+        wb = w13_bytes(dcfg, dcfg.T, d["active_experts"])
+        ach = wb / (d["w13_ms"] * 1e-3) / 1e9
+        line["decode"]["roofline"] = {"kernel": "w13 weight-streaming GEMM + SiLU-and-mul",
+                                      "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
+                                      "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+                                      "traffic": stored_traffic("%s_w13" % dcfg.name),
+                                      "avg_kernel_ms": d["w13_ms"], "algorithmic_bytes": wb}
     if not args.no_cpu and args.cpu_sample > 0:
         line["cpu_baseline"] = cpu_baseline(cfg, T, args.cpu_sample)
     print(json.dumps(line), flush=True)
