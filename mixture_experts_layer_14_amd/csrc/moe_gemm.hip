@@ -389,13 +389,27 @@ static hipError_t launch_tile(const GroupedProblem& p, GemmArgs g, const int32_t
     return hipGetLastError();
 }
 
+// weight-streaming configuration: 16-column tiles per n-group for w13
+// (gate/up pairs) and w2, and waves splitting K inside a block
+#ifndef MOE_STREAM_NPW13
+#define MOE_STREAM_NPW13 2
+#endif
+#ifndef MOE_STREAM_NPW2
+#define MOE_STREAM_NPW2 2
+#endif
+#ifndef MOE_STREAM_WAVES
+#define MOE_STREAM_WAVES 4
+#endif
+
 template <int TM, int MODE>
 static hipError_t launch_stream(const GroupedProblem& p, GemmArgs g, const int32_t* offsets, void* ws,
                                 hipStream_t stream) {
+    constexpr int NPW = MODE == kModeW13 ? MOE_STREAM_NPW13 : MOE_STREAM_NPW2;
     build_tiles(p, offsets, TM * 16, g, ws, stream);
-    const int groups = MODE == kModeW13 ? p.I / 16 : p.H / 32;
+    const int groups = MODE == kModeW13 ? p.I / (NPW / 2 * 16) : p.H / (NPW * 16);
     const int64_t blocks = static_cast<int64_t>(g.max_m_tiles) * groups;
-    stream_kernel<TM, 2, MODE, MOE_STREAM_U><<<static_cast<unsigned>(blocks), 4 * kWave, 0, stream>>>(g);
+    stream_kernel<TM, NPW, MOE_STREAM_WAVES, MODE, MOE_STREAM_U>
+        <<<static_cast<unsigned>(blocks), MOE_STREAM_WAVES * kWave, 0, stream>>>(g);
     return hipGetLastError();
 }
 

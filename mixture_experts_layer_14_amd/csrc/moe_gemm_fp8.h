@@ -36,6 +36,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
     constexpr int STAGES = 3 * STAGE <= LDS_MAX ? 3 : 2;
     static_assert(ROWS % (RPC * NW) == 0 && BM % RPC == 0 && BM % NW == 0 && SROWS <= kWave, "copy split");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
+    static_assert(MODE != kModeW2 || NW * kWave >= BM, "one thread per row weight");
     static_assert(MODE != kModeW13 || (TN == 2 && BN == 256 && WN == 4),
                   "w13 fp8: each wave holds one 32-column gate/up pair, a block one 128-column group");
     static_assert(PER_STAGE * (STAGES - 2) <= 63, "vmcnt immediate range");
@@ -120,6 +121,14 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
     const int lrow = lane % 32, khalf = lane / 32;
     const int crow = khalf * 4;
 
+    // w2: the tile's routing weights, loaded into a register before the main
+    // loop and moved to LDS after it (no copy left in flight to wait for)
+    __shared__ float row_w[MODE == kModeW2 ? BM : 1];
+    float my_w = 1.0f;
+    if (MODE == kModeW2 && tid < BM) {
+        const int64_t r = tl.row0 + tid;
+        if (r < tl.row1) my_w = row_weight(g, r);
+    }
 #pragma unroll
     for (int st = 0; st < STAGES - 1; ++st)
         if (st < nkb) issue_stage(st);
@@ -221,14 +230,17 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
                 }
             }
     } else {
+        if (tid < BM) row_w[tid] = my_w;
+        __syncthreads();
         uint16_t* y = static_cast<uint16_t*>(g.C);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int64_t r = tl.row0 + wm * WTM + i * 32 + 8 * (v / 4) + crow + (v % 4);
+                const int lr = wm * WTM + i * 32 + 8 * (v / 4) + crow + (v % 4);
+                const int64_t r = tl.row0 + lr;
                 if (r >= tl.row1) continue;
-                const float w = r < g.routed_rows ? g.topk_weights[g.sorted_slots[r]] : 1.0f;
+                const float w = row_w[lr];
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     const int64_t c = static_cast<int64_t>(n_tile) * BN + wn * WTN + j * 32 + ccol;

@@ -59,6 +59,11 @@ __device__ __forceinline__ int64_t a_source_row(const GemmArgs& g, int64_t r) {
     return src < 0 ? 0 : (src >= g.T ? g.T - 1 : src);
 }
 
+// Routing weight of permuted row r for the w2 epilogue (shared rows: 1).
+__device__ __forceinline__ float row_weight(const GemmArgs& g, int64_t r) {
+    return r < g.routed_rows ? g.topk_weights[g.sorted_slots[r]] : 1.0f;
+}
+
 // Weight row of local B-tile row `row` for an n-tile of width BN.  w13 tiles
 // interleave gate and up rows in blocks of `blk` so that the accumulator
 // tile of gate column c and the one of up column c land in the same lanes.
@@ -137,7 +142,11 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
     constexpr int COPIES = ROWS / RPC / NW;        // copy instructions per wave per stage
     constexpr int KSTEPS = ROWB / 32;              // 16-k MFMA steps per k-iteration
     constexpr int LDS_MAX = 160 * 1024;
-    constexpr int STAGES = 4 * STAGE <= LDS_MAX ? 4 : (3 * STAGE <= LDS_MAX ? 3 : 2);
+#ifndef MOE_TILE_MAX_STAGES
+#define MOE_TILE_MAX_STAGES 4
+#endif
+    constexpr int STAGES_FIT = 4 * STAGE <= LDS_MAX ? 4 : (3 * STAGE <= LDS_MAX ? 3 : 2);
+    constexpr int STAGES = STAGES_FIT < MOE_TILE_MAX_STAGES ? STAGES_FIT : MOE_TILE_MAX_STAGES;
     static_assert(ROWB == 64 || ROWB == 128, "row slab of 64 or 128 bytes");
     static_assert(ROWS % (RPC * NW) == 0, "stage rows split evenly over the waves");
     static_assert(BM % RPC == 0, "copy instructions never straddle A and B");
@@ -145,6 +154,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
     static_assert(MODE != kModeW13 || TN % 2 == 0, "w13 wave tile holds gate/up pairs");
     static_assert(COPIES * (STAGES - 2) <= 63, "vmcnt immediate range");
     static_assert(STAGES * STAGE <= LDS_MAX, "LDS budget");
+    static_assert(MODE != kModeW2 || NW * kWave >= BM, "one thread per row weight");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE];
 
     const int tid = threadIdx.x;
@@ -211,6 +221,15 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
 
     const int lrow = lane % 32, khalf = lane / 32;
 
+    // w2: the tile's routing weights, loaded into a register now so that
+    // their dependent loads (slot, then weight) overlap the main loop; they
+    // reach LDS only after it, where no copy is left in flight to wait for
+    __shared__ float row_w[MODE == kModeW2 ? BM : 1];
+    float my_w = 1.0f;
+    if (MODE == kModeW2 && tid < BM) {
+        const int64_t r = tl.row0 + tid;
+        if (r < tl.row1) my_w = row_weight(g, r);
+    }
 #pragma unroll
     for (int st = 0; st < STAGES - 1; ++st)
         if (st < nk) issue_stage(st);
@@ -278,6 +297,10 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     }
 
+    if (MODE == kModeW2) {
+        if (tid < BM) row_w[tid] = my_w;
+        __syncthreads();
+    }
     const int ccol = lane % 32;
     const int crow = (lane / 32) * 4;
     if (MODE == kModeW13) {
@@ -300,9 +323,10 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int64_t r = tl.row0 + wm * WTM + i * 32 + 8 * (v / 4) + crow + (v % 4);
+                const int lr = wm * WTM + i * 32 + 8 * (v / 4) + crow + (v % 4);
+                const int64_t r = tl.row0 + lr;
                 if (r >= tl.row1) continue;
-                const float w = r < g.routed_rows ? g.topk_weights[g.sorted_slots[r]] : 1.0f;
+                const float w = row_w[lr];
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     const int64_t col = static_cast<int64_t>(n_tile) * BN + wn * WTN + j * 32 + ccol;
@@ -317,14 +341,13 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
 // ---------------------------------------------------------------------------
 //
 // Block = one m-tile of TM*16 rows x one n-group of NPW 16-column tiles; its
-// 4 waves split the k-steps (64 bytes = 32 k each) evenly.  A lane holds 16
-// bytes of row l%16 at byte (l/16)*16 of the k-step (the 16x16x32 operand
+// WAVES waves split the k-steps (64 bytes = 32 k each) evenly.  A lane holds
+// 16 bytes of row l%16 at byte (l/16)*16 of the k-step (the 16x16x32 operand
 // layout); U k-steps of every operand are loaded before they are consumed.
-// For w13 the n-group is one 16-column gate tile plus the matching up tile.
-template <int TM, int NPW, int MODE, int U>
-__global__ __launch_bounds__(4 * kWave) void stream_kernel(GemmArgs g) {
-    constexpr int WAVES = 4;
-    static_assert(MODE != kModeW13 || NPW == 2, "w13 n-group is one gate/up pair");
+// For w13 the n-group is NPW/2 gate tiles each followed by its up tile.
+template <int TM, int NPW, int WAVES, int MODE, int U>
+__global__ __launch_bounds__(WAVES * kWave) void stream_kernel(GemmArgs g) {
+    static_assert(MODE != kModeW13 || NPW % 2 == 0, "w13 n-group holds gate/up pairs");
     __shared__ f32x4 red[WAVES][TM][NPW][kWave];
 
     const int tid = threadIdx.x;
@@ -358,6 +381,17 @@ __global__ __launch_bounds__(4 * kWave) void stream_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < NPW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // w2: routing weights of the 4 rows per m-subtile this lane stores,
+    // loaded up front so the dependent loads overlap the k-loop
+    float rw[TM][4];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t r = tl.row0 + i * 16 + (lane / 16) * 4 + q;
+            rw[i][q] = (MODE == kModeW2 && wave == 0 && r < tl.row1) ? row_weight(g, r) : 1.0f;
+        }
+
     const int ks = static_cast<int>(eltK / 64);
     const int s0 = wave * ks / WAVES, s1 = (wave + 1) * ks / WAVES;
     for (int s = s0; s < s1; s += U) {
@@ -386,34 +420,40 @@ __global__ __launch_bounds__(4 * kWave) void stream_kernel(GemmArgs g) {
         }
     }
 
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < NPW; ++j) red[wave][i][j][lane] = acc[i][j];
-    __syncthreads();
-    if (wave != 0) return;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < NPW; ++j) {
-            f32x4 s = red[0][i][j][lane];
-#pragma unroll
-            for (int w = 1; w < WAVES; ++w) s += red[w][i][j][lane];
-            acc[i][j] = s;
-        }
-
-    const int ccol = lane % 16;
-    const int crow = (lane / 16) * 4;
-    if (MODE == kModeW13) {
-        uint16_t* act = static_cast<uint16_t*>(g.C);
-        const int64_t col = static_cast<int64_t>(n_grp) * 16 + ccol;
+    if (WAVES > 1) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t r = tl.row0 + i * 16 + crow + q;
-                if (r < tl.row1) act[r * g.I + col] = f32_to_bf16_bits(silu_mul(acc[i][0][q], acc[i][1][q]));
+            for (int j = 0; j < NPW; ++j) red[wave][i][j][lane] = acc[i][j];
+        __syncthreads();
+        if (wave != 0) return;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < NPW; ++j) {
+                f32x4 sum = red[0][i][j][lane];
+#pragma unroll
+                for (int w = 1; w < WAVES; ++w) sum += red[w][i][j][lane];
+                acc[i][j] = sum;
             }
+    }
+
+    const int ccol = lane % 16;
+    const int crow = (lane / 16) * 4;
+    if constexpr (MODE == kModeW13) {
+        uint16_t* act = static_cast<uint16_t*>(g.C);
+#pragma unroll
+        for (int p = 0; p < NPW / 2; ++p) {
+            const int64_t col = static_cast<int64_t>(n_grp) * (NPW / 2) * 16 + p * 16 + ccol;
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t r = tl.row0 + i * 16 + crow + q;
+                    if (r < tl.row1)
+                        act[r * g.I + col] = f32_to_bf16_bits(silu_mul(acc[i][2 * p][q], acc[i][2 * p + 1][q]));
+                }
+        }
     } else {
         uint16_t* y = static_cast<uint16_t*>(g.C);
 #pragma unroll
@@ -422,7 +462,7 @@ __global__ __launch_bounds__(4 * kWave) void stream_kernel(GemmArgs g) {
             for (int q = 0; q < 4; ++q) {
                 const int64_t r = tl.row0 + i * 16 + crow + q;
                 if (r >= tl.row1) continue;
-                const float w = r < g.routed_rows ? g.topk_weights[g.sorted_slots[r]] : 1.0f;
+                const float w = rw[i][q];
 #pragma unroll
                 for (int j = 0; j < NPW; ++j) {
                     const int64_t col = static_cast<int64_t>(n_grp) * (NPW * 16) + j * 16 + ccol;
