@@ -40,7 +40,12 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
     static_assert(MODE != kModeW13 || (TN == 2 && BN == 256 && WN == 4),
                   "w13 fp8: each wave holds one 32-column gate/up pair, a block one 128-column group");
     static_assert(PER_STAGE * (STAGES - 2) <= 63, "vmcnt immediate range");
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE];
+    // one LDS object: the stage buffers, then (w2) the tile's routing
+    // weights.  A second __shared__ array would make the compiler wait for
+    // every copy in flight before each LDS read of the main loop.
+    constexpr int ROW_W_BYTES = MODE == kModeW2 ? BM * 4 : 0;
+    static_assert(STAGES * STAGE + ROW_W_BYTES <= LDS_MAX, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE + ROW_W_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -123,7 +128,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
 
     // w2: the tile's routing weights, loaded into a register before the main
     // loop and moved to LDS after it (no copy left in flight to wait for)
-    __shared__ float row_w[MODE == kModeW2 ? BM : 1];
+    float* row_w = reinterpret_cast<float*>(smem + STAGES * STAGE);
     float my_w = 1.0f;
     if (MODE == kModeW2 && tid < BM) {
         const int64_t r = tl.row0 + tid;

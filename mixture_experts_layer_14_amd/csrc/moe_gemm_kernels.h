@@ -11,6 +11,8 @@
 //                 splitting K and reducing through LDS at the end.
 #pragma once
 
+#include <utility>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -118,16 +120,55 @@ __device__ __forceinline__ TilePos map_block(int bid, int num_m, int n_tiles, in
 // (see lds_slot) so that the MFMA operand reads are free of bank conflicts:
 // LDS serves a 128-bit read 16 lanes at a time from 64 four-byte banks, and
 // the 16 lanes read 16 consecutive rows at the same logical chunk.  STAGES
-// LDS buffers keep the copies of the next STAGES-1 k-iterations in flight
-// while the current one multiplies; stage handoff is an explicit vmcnt wait
-// plus a bare barrier (a __syncthreads fence would also wait for the copies
-// that should stay in flight).
+// LDS buffers keep the copies of STAGES-2 later k-iterations in flight while
+// one multiplies; stage handoff is an explicit vmcnt wait plus a bare
+// barrier (a __syncthreads fence would also wait for the copies that should
+// stay in flight), one per k-iteration.
 template <int ROWB>
 __device__ __forceinline__ int lds_slot(int row, int chunk) {
     // 128-byte rows: even/odd rows fill opposite bank halves, the 8 rows of a
     // parity get 8 slots.  64-byte rows: rows r, r+4, r+8, r+12 share a bank
     // quarter and get 4 slots.
     return ROWB == 128 ? chunk ^ ((row >> 1) & 7) : chunk ^ ((row >> 2) & 3);
+}
+
+// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1 (compile-time
+// loop index, so per-iteration counts can feed scheduling templates).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Scheduling groups for a region that holds LDS reads, then copies into
+// LDS (the compiler keeps LDS reads ahead of copies into LDS), then MFMAs:
+// the first MFMAs take two reads each so the reads land early, the
+// remaining ones share the copies.
+template <int MFMAS, int READS, int VMEM, int I = 0>
+__device__ __forceinline__ void mix_sched() {
+    constexpr int RSLOTS = (READS + 1) / 2 < MFMAS ? (READS + 1) / 2 : MFMAS;
+    constexpr int VSLOTS = MFMAS - RSLOTS;
+    if constexpr (I < MFMAS) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        if constexpr (I < RSLOTS) {
+            constexpr int rd = READS - 2 * I >= 2 ? 2 : READS - 2 * I;
+            __builtin_amdgcn_sched_group_barrier(0x100, rd, 0);  // DS read
+        } else {
+            constexpr int vper = (VMEM + VSLOTS - 1) / VSLOTS;
+            constexpr int v0 = vper * (I - RSLOTS);
+            constexpr int vm = VMEM - v0 >= vper ? vper : (VMEM - v0 > 0 ? VMEM - v0 : 0);
+            if constexpr (vm > 0) __builtin_amdgcn_sched_group_barrier(0x020, vm, 0);  // copies
+        }
+        mix_sched<MFMAS, READS, VMEM, I + 1>();
+    } else {
+        constexpr int rleft = READS - 2 * RSLOTS;
+        constexpr int vleft = VSLOTS > 0 ? 0 : VMEM;
+        if constexpr (rleft > 0) __builtin_amdgcn_sched_group_barrier(0x100, rleft, 0);
+        if constexpr (vleft > 0) __builtin_amdgcn_sched_group_barrier(0x020, vleft, 0);
+    }
 }
 
 template <int BM, int BN, int WM, int WN, int ROWB, int MODE, int GM>
@@ -142,20 +183,22 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
     constexpr int COPIES = ROWS / RPC / NW;        // copy instructions per wave per stage
     constexpr int KSTEPS = ROWB / 32;              // 16-k MFMA steps per k-iteration
     constexpr int LDS_MAX = 160 * 1024;
-#ifndef MOE_TILE_MAX_STAGES
-#define MOE_TILE_MAX_STAGES 4
-#endif
-    constexpr int STAGES_FIT = 4 * STAGE <= LDS_MAX ? 4 : (3 * STAGE <= LDS_MAX ? 3 : 2);
-    constexpr int STAGES = STAGES_FIT < MOE_TILE_MAX_STAGES ? STAGES_FIT : MOE_TILE_MAX_STAGES;
+    constexpr int LDS_STAGES = LDS_MAX - (MODE == kModeW2 ? BM * 4 : 0);
+    constexpr int STAGES = 4 * STAGE <= LDS_STAGES ? 4 : (3 * STAGE <= LDS_STAGES ? 3 : 2);
     static_assert(ROWB == 64 || ROWB == 128, "row slab of 64 or 128 bytes");
     static_assert(ROWS % (RPC * NW) == 0, "stage rows split evenly over the waves");
     static_assert(BM % RPC == 0, "copy instructions never straddle A and B");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
     static_assert(MODE != kModeW13 || TN % 2 == 0, "w13 wave tile holds gate/up pairs");
+    static_assert(KSTEPS % 2 == 0, "a stage ends on fragment buffer 1");
     static_assert(COPIES * (STAGES - 2) <= 63, "vmcnt immediate range");
-    static_assert(STAGES * STAGE <= LDS_MAX, "LDS budget");
     static_assert(MODE != kModeW2 || NW * kWave >= BM, "one thread per row weight");
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE];
+    // one LDS object: the stage buffers, then (w2) the tile's routing
+    // weights.  A second __shared__ array would make the compiler wait for
+    // every copy in flight before each LDS read of the main loop.
+    constexpr int ROW_W_BYTES = MODE == kModeW2 ? BM * 4 : 0;
+    static_assert(STAGES * STAGE + ROW_W_BYTES <= LDS_MAX, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE + ROW_W_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -189,26 +232,18 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
     }
     const int nk = static_cast<int>(eltK / ROWB);
 
+    // copies of k-iteration `it` into its stage buffer; past the last
+    // k-iteration the source is clamped to it (a redundant in-bounds copy
+    // into a buffer nobody reads again keeps the copy count per k-iteration
+    // fixed and the loop free of branches)
     auto issue_stage = [&](int it) {
         uint8_t* dst = smem + (it % STAGES) * STAGE + wave * COPIES * 1024;
-        const int64_t off = static_cast<int64_t>(it) * ROWB;
+        const int64_t off = static_cast<int64_t>(it < nk ? it : nk - 1) * ROWB;
 #pragma unroll
         for (int q = 0; q < COPIES; ++q)
             __builtin_amdgcn_global_load_lds(
                 reinterpret_cast<const void*>(src[q] + off),
                 (__attribute__((address_space(3))) void*)(dst + q * 1024), 16, 0, 0);
-    };
-    // wait until at most `later` stages of this wave's copies are in flight
-    auto wait_copies = [&](int later) {
-        if (STAGES >= 4 && later >= 2) {
-            constexpr int n = 2 * COPIES;
-            __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
-        } else if (STAGES >= 3 && later >= 1) {
-            constexpr int n = COPIES;
-            __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
-        } else {
-            __builtin_amdgcn_s_waitcnt(0x0F70);
-        }
     };
 
     f32x16 acc[TM][TN];
@@ -224,78 +259,100 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
     // w2: the tile's routing weights, loaded into a register now so that
     // their dependent loads (slot, then weight) overlap the main loop; they
     // reach LDS only after it, where no copy is left in flight to wait for
-    __shared__ float row_w[MODE == kModeW2 ? BM : 1];
+    float* row_w = reinterpret_cast<float*>(smem + STAGES * STAGE);
     float my_w = 1.0f;
     if (MODE == kModeW2 && tid < BM) {
         const int64_t r = tl.row0 + tid;
         if (r < tl.row1) my_w = row_weight(g, r);
     }
-#pragma unroll
-    for (int st = 0; st < STAGES - 1; ++st)
-        if (st < nk) issue_stage(st);
-    for (int it = 0; it < nk; ++it) {
-        // stages it+1 .. it+STAGES-2 may still be in flight
-        const int later = min(STAGES - 2, nk - 1 - it);
-        wait_copies(later);
-        __builtin_amdgcn_s_barrier();
-        // every wave has finished reading stage it-1: refill its buffer
-        if (it + STAGES - 1 < nk) issue_stage(it + STAGES - 1);
-
-        const uint8_t* sA = smem + (it % STAGES) * STAGE;
+    // Operand fragments are double-buffered across k-steps, and across
+    // stages too: the first k-step of stage it+1 is read from LDS while the
+    // last MFMAs of stage it run, so the matrix core never waits for a
+    // stage's first reads.  The barrier that publishes stage it+1 sits in the
+    // middle of stage it's last k-step; after it every wave has finished
+    // reading stage it, whose buffer then takes the copies of stage
+    // it+STAGES.
+    auto read_step = [&](const uint8_t* sA, int s, u32x4 (&fa)[TM], u32x4 (&fb)[TN]) {
         const uint8_t* sB = sA + BM * ROWB;
-        // operand fragments double-buffered across the k-steps so the reads
-        // of step s+1 are in flight while step s multiplies
-        u32x4 af[2][TM], bfr[2][TN];
-        auto read_step = [&](int s, u32x4 (&fa)[TM], u32x4 (&fb)[TN]) {
-            const int chunk = s * 2 + khalf;
+        const int chunk = s * 2 + khalf;
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int r = wm * WTM + i * 32 + lrow;
-                fa[i] = *reinterpret_cast<const u32x4*>(sA + r * ROWB + lds_slot<ROWB>(r, chunk) * 16);
-            }
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int r = wn * WTN + j * 32 + lrow;
-                fb[j] = *reinterpret_cast<const u32x4*>(sB + r * ROWB + lds_slot<ROWB>(r, chunk) * 16);
-            }
-        };
-        read_step(0, af[0], bfr[0]);
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-            if (s + 1 < KSTEPS) read_step(s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8, af[s & 1][i]), __builtin_bit_cast(bf16x8, bfr[s & 1][j]),
-                        acc[i][j], 0, 0, 0);
+        for (int i = 0; i < TM; ++i) {
+            const int r = wm * WTM + i * 32 + lrow;
+            fa[i] = *reinterpret_cast<const u32x4*>(sA + r * ROWB + lds_slot<ROWB>(r, chunk) * 16);
         }
-        // Instruction order of the k-steps above: the first step's operand
-        // reads, then for every step its MFMAs with the next step's reads
-        // slotted between them, so reads are in flight while the matrix core
-        // is busy instead of after it has drained.
-        {
-            constexpr int kReads = TM + TN, kMfma = TM * TN;
-            constexpr int kPaired = kReads < kMfma ? kReads : kMfma;
-            constexpr int kRestMfma = kMfma - kPaired, kRestReads = kReads - kPaired;
-            __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);       // DS reads, step 0
 #pragma unroll
-            for (int s = 0; s + 1 < KSTEPS; ++s) {
-#pragma unroll
-                for (int r = 0; r < kPaired; ++r) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
-                }
-                if (kRestReads > 0) __builtin_amdgcn_sched_group_barrier(0x100, kRestReads, 0);
-                if (kRestMfma > 0) __builtin_amdgcn_sched_group_barrier(0x008, kRestMfma, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);        // last step
+        for (int j = 0; j < TN; ++j) {
+            const int r = wn * WTN + j * 32 + lrow;
+            fb[j] = *reinterpret_cast<const u32x4*>(sB + r * ROWB + lds_slot<ROWB>(r, chunk) * 16);
         }
-        // operand reads of this stage must land before another wave's copy
-        // may overwrite it (after the next barrier)
+    };
+    constexpr int kReads = TM + TN, kMfma = TM * TN;
+    // this wave's copies of all but the STAGES-2 most recent stages landed
+    auto wait_later_stages = [&]() {
+        constexpr int n = (STAGES - 2) * COPIES;
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
+    };
+    auto mfma_range = [&](int lo, int hi, const u32x4 (&fa)[TM], const u32x4 (&fb)[TN]) {
+#pragma unroll
+        for (int m = lo; m < hi; ++m)
+            acc[m / TN][m % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, fa[m / TN]), __builtin_bit_cast(bf16x8, fb[m % TN]),
+                acc[m / TN][m % TN], 0, 0, 0);
+    };
+    // copies q0 .. q1-1 of this wave's share of k-iteration `kit`
+    auto issue_copies = [&](int kit, int q0, int q1) {
+        uint8_t* dst = smem + (kit % STAGES) * STAGE + wave * COPIES * 1024;
+        const int64_t off = static_cast<int64_t>(kit < nk ? kit : nk - 1) * ROWB;
+#pragma unroll
+        for (int q = q0; q < q1; ++q)
+            __builtin_amdgcn_global_load_lds(
+                reinterpret_cast<const void*>(src[q] + off),
+                (__attribute__((address_space(3))) void*)(dst + q * 1024), 16, 0, 0);
+    };
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st) issue_stage(st);
+    wait_later_stages();
+    __builtin_amdgcn_s_barrier();
+    u32x4 af[2][TM], bfr[2][TN];
+    read_step(smem, 0, af[0], bfr[0]);
+    // copies per k-step when a stage's copies are spread over the k-steps
+    // that precede the next barrier
+    constexpr int CPS = (COPIES + KSTEPS - 2) / (KSTEPS - 1);
+    for (int it = 0; it < nk; ++it) {
+        const uint8_t* sA = smem + (it % STAGES) * STAGE;
+        static_for<KSTEPS - 1>([&](auto sc) {
+            constexpr int s = decltype(sc)::value;
+            read_step(sA, s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
+            // stage it+STAGES-1 goes to the buffer of stage it-1, free since
+            // the previous barrier
+            constexpr int q0 = s * CPS < COPIES ? s * CPS : COPIES;
+            constexpr int q1 = (s + 1) * CPS < COPIES ? (s + 1) * CPS : COPIES;
+            issue_copies(it + STAGES - 1, q0, q1);
+            mfma_range(0, kMfma, af[s & 1], bfr[s & 1]);
+            mix_sched<kMfma, kReads, q1 - q0>();
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        // the last k-step; in the last iteration the reads after the barrier
+        // fetch a buffer that is never used, so the loop body has no branch
+        constexpr int L = (KSTEPS - 1) & 1;
+        constexpr int H = kMfma / 2;
+        mfma_range(0, H, af[L], bfr[L]);
+        __builtin_amdgcn_sched_group_barrier(0x008, H, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        // this wave's reads of stage it have landed (the MFMAs above consumed
+        // the last of them); its copies of stage it+1 must land too, with
+        // those of stages it+2 .. it+STAGES-1 still in flight
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        wait_later_stages();
+        __builtin_amdgcn_s_barrier();
+        // reads first: the compiler keeps LDS reads behind copies into LDS
+        read_step(smem + ((it + 1) % STAGES) * STAGE, 0, af[L ^ 1], bfr[L ^ 1]);
+        mfma_range(H, kMfma, af[L], bfr[L]);
+        mix_sched<kMfma - H, kReads, 0>();
+        __builtin_amdgcn_sched_barrier(0);
     }
+    // no copy may still write LDS when the block ends
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
     if (MODE == kModeW2) {
         if (tid < BM) row_w[tid] = my_w;
