@@ -35,7 +35,7 @@ namespace moe {
 
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets,
                                                            int E, int32_t shared_rows,
-                                                           int32_t shared_base, int BM,
+                                                           int32_t shared_base, int BM, int gm_max,
                                                            Tile* __restrict__ tiles,
                                                            int32_t* __restrict__ num_tiles) {
     __shared__ int32_t scan[1024];
@@ -59,12 +59,18 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
         __syncthreads();
     }
     const int32_t start = scan[g] - nt;
+    // an expert's m-tiles form groups of at most gm_max, balanced in size; a
+    // group's tiles sweep the n-tiles together so they share each weight tile
+    const int32_t ngroups = (nt + gm_max - 1) / gm_max;
+    int32_t c = 0;
     for (int32_t j = 0; j < nt; ++j) {
+        while (j >= (c + 1) * nt / ngroups) ++c;
+        const int32_t first = c * nt / ngroups, last = (c + 1) * nt / ngroups;
         Tile t;
         t.expert = g;
         t.row0 = r0 + j * BM;
         t.row1 = r0 + (j + 1) * BM < r1 ? r0 + (j + 1) * BM : r1;
-        t.pad = 0;
+        t.group = (start + first) * 256 + (last - first);
         tiles[start + j] = t;
     }
     if (g == 1023) *num_tiles = scan[1023];
@@ -274,19 +280,61 @@ template <class Pol>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y,
                                                       const int32_t* __restrict__ slot_to_row,
                                                       int64_t T, int K, int H, int shared,
-                                                      int64_t rows, void* __restrict__ out) {
+                                                      int64_t rows, int parts, void* __restrict__ out) {
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t t = idx / H;
     const int h = static_cast<int>(idx % H);
     if (t >= T) return;
+    const int64_t part_stride = rows * H;
     float s = 0.0f;
     for (int k = 0; k < K; ++k) {
         int64_t r = slot_to_row[t * K + k];
         r = r < 0 ? 0 : (r >= rows ? rows - 1 : r);
-        s += Pol::load(y, r * H + h);
+        for (int q = 0; q < parts; ++q) s += Pol::load(y, q * part_stride + r * H + h);
     }
-    if (shared) s += Pol::load(y, (T * K + t) * H + h);
+    if (shared)
+        for (int q = 0; q < parts; ++q) s += Pol::load(y, q * part_stride + (T * K + t) * H + h);
     Pol::store(out, t * H + h, s);
+}
+
+// bf16 combine, 8 columns per thread (16-byte loads and stores).  y holds
+// `parts` partial outputs of every row (a K-split w2); the sum runs in fp32
+// in a fixed order: slot k = 0..K-1, then the shared row, each over parts.
+__global__ __launch_bounds__(256) void combine_bf16x8_kernel(const uint16_t* __restrict__ y,
+                                                             const int32_t* __restrict__ slot_to_row,
+                                                             int64_t T, int K, int H, int shared,
+                                                             int64_t rows, int parts,
+                                                             uint16_t* __restrict__ out) {
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int hv = H / 8;
+    const int64_t t = idx / hv;
+    const int h = static_cast<int>(idx % hv) * 8;
+    if (t >= T) return;
+    const int64_t part_stride = rows * H;
+    float s[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] = 0.0f;
+    auto add_row = [&](int64_t r) {
+        for (int q = 0; q < parts; ++q) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(y + q * part_stride + r * H + h);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                s[2 * e] += __uint_as_float(v[e] << 16);
+                s[2 * e + 1] += __uint_as_float(v[e] & 0xFFFF0000u);
+            }
+        }
+    };
+    for (int k = 0; k < K; ++k) {
+        int64_t r = slot_to_row[t * K + k];
+        add_row(r < 0 ? 0 : (r >= rows ? rows - 1 : r));
+    }
+    if (shared) add_row(T * K + t);
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        o[e] = static_cast<uint32_t>(f32_to_bf16_bits(s[2 * e])) |
+               (static_cast<uint32_t>(f32_to_bf16_bits(s[2 * e + 1])) << 16);
+    *reinterpret_cast<u32x4*>(out + t * H + h) = o;
 }
 
 // ---------------------------------------------------------------------------
@@ -313,14 +361,6 @@ size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 }  // namespace
 
-size_t gemm_tile_workspace_bytes(const GroupedProblem& p) {
-    return align_up(256) + align_up(sizeof(Tile) * static_cast<size_t>(max_m_tiles(p, 16)));
-}
-
-size_t w2_rows_workspace_bytes(const GroupedProblem& p) {
-    const size_t elt = p.dtype == MOE_DTYPE_F32 ? 4 : 2;
-    return align_up(static_cast<size_t>(total_rows(p)) * p.H * elt);
-}
 
 // Prefill tile configuration: block tile BM x BN on WM x WN waves, GM m-tiles
 // per L2 group, ROWB bytes of every row per pipeline stage.  Measured on
@@ -356,12 +396,37 @@ size_t w2_rows_workspace_bytes(const GroupedProblem& p) {
 #define MOE_STREAM_MAX_ROWS 64
 #endif
 
+// Split of the w2 GEMM's K across blocks (bf16 tile path): with few tiles the
+// last wave of tiles would leave most of the 256 compute units idle, so the
+// reduction is cut into parts whose bf16 partial outputs the combine sums.
+// A function of the problem alone, so workspace sizing and launch agree.
+static int w2_ksplit(const GroupedProblem& p) {
+    if (p.dtype != MOE_DTYPE_BF16 || rows_per_active_expert(p) <= MOE_STREAM_MAX_ROWS) return 1;
+    if (p.H % MOE_TILE_BN != 0) return 1;
+    constexpr int64_t kCUs = 256;
+    const int64_t tiles = static_cast<int64_t>(max_m_tiles(p, MOE_TILE_BM)) * (p.H / MOE_TILE_BN);
+    const int64_t nk_all = static_cast<int64_t>(p.I) * 2 / MOE_TILE_ROWB;
+    int ks = 1;
+    while (ks < 4 && tiles * ks < 8 * kCUs && nk_all / (ks + 1) >= 32) ++ks;
+    return ks;
+}
+
+size_t gemm_tile_workspace_bytes(const GroupedProblem& p) {
+    return align_up(256) + align_up(sizeof(Tile) * static_cast<size_t>(max_m_tiles(p, 16)));
+}
+
+size_t w2_rows_workspace_bytes(const GroupedProblem& p) {
+    const size_t elt = p.dtype == MOE_DTYPE_F32 ? 4 : 2;
+    return align_up(static_cast<size_t>(w2_ksplit(p)) * total_rows(p) * p.H * elt);
+}
+
 static void build_tiles(const GroupedProblem& p, const int32_t* offsets, int BM, GemmArgs& g,
                         void* ws, hipStream_t stream) {
     int32_t* num_tiles = static_cast<int32_t*>(ws);
     Tile* tiles = reinterpret_cast<Tile*>(static_cast<uint8_t*>(ws) + 256);
     build_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, p.E, p.shared ? static_cast<int32_t>(p.T) : 0,
-                                               static_cast<int32_t>(p.T * p.K), BM, tiles, num_tiles);
+                                               static_cast<int32_t>(p.T * p.K), BM, MOE_TILE_GM, tiles,
+                                               num_tiles);
     g.tiles = tiles;
     g.num_tiles = num_tiles;
     g.max_m_tiles = max_m_tiles(p, BM);
@@ -383,9 +448,9 @@ static hipError_t launch_tile(const GroupedProblem& p, GemmArgs g, const int32_t
                               hipStream_t stream) {
     build_tiles(p, offsets, BM, g, ws, stream);
     g.n_tiles_n = MODE == kModeW13 ? (2 * p.I) / BN : p.H / BN;
-    const int64_t total = static_cast<int64_t>(g.max_m_tiles) * g.n_tiles_n;
+    const int64_t total = static_cast<int64_t>(g.max_m_tiles) * g.n_tiles_n * (MODE == kModeW2 ? g.ksplit : 1);
     const int64_t blocks = 8 * ((total + 7) / 8);
-    tile_kernel<BM, BN, WM, WN, (BM + BN >= 512 ? 64 : MOE_TILE_ROWB), MODE, MOE_TILE_GM><<<static_cast<unsigned>(blocks), WM * WN * kWave, 0, stream>>>(g);
+    tile_kernel<BM, BN, WM, WN, (BM + BN >= 512 ? 64 : MOE_TILE_ROWB), MODE><<<static_cast<unsigned>(blocks), WM * WN * kWave, 0, stream>>>(g);
     return hipGetLastError();
 }
 
@@ -438,7 +503,7 @@ static hipError_t launch_tile_fp8(const GroupedProblem& p, GemmArgs g, const int
     g.n_tiles_n = MODE == kModeW13 ? (2 * p.I) / BN : p.H / BN;
     const int64_t total = static_cast<int64_t>(g.max_m_tiles) * g.n_tiles_n;
     const int64_t blocks = 8 * ((total + 7) / 8);
-    tile_kernel_fp8<BM, BN, WM, WN, MODE, MOE_TILE_GM><<<static_cast<unsigned>(blocks), WM * WN * kWave, 0, stream>>>(g);
+    tile_kernel_fp8<BM, BN, WM, WN, MODE><<<static_cast<unsigned>(blocks), WM * WN * kWave, 0, stream>>>(g);
     return hipGetLastError();
 }
 
@@ -522,6 +587,8 @@ hipError_t launch_w2_combine(const GroupedProblem& p, const void* act, const flo
     g.A_scale = act_scale;
     g.B_scale = w2_scale;
     g.B_shared_scale = shared_w2_scale;
+    g.ksplit = w2_ksplit(p);
+    g.part_stride = total_rows(p) * p.H;
     hipError_t err;
     if (p.dtype == MOE_DTYPE_BF16)
         err = bf16_gemm<kModeW2>(p, g, offsets, ws, stream);
@@ -533,11 +600,18 @@ hipError_t launch_w2_combine(const GroupedProblem& p, const void* act, const flo
         return hipErrorNotSupported;
     if (err != hipSuccess) return err;
     const int64_t n = p.T * p.H;
-    const unsigned blocks = static_cast<unsigned>((n + 255) / 256);
-    if (p.dtype != MOE_DTYPE_F32)
-        combine_kernel<PolBF16><<<blocks, 256, 0, stream>>>(y, slot_to_row, p.T, p.K, p.H, p.shared, total_rows(p), out);
-    else
-        combine_kernel<PolF32><<<blocks, 256, 0, stream>>>(y, slot_to_row, p.T, p.K, p.H, p.shared, total_rows(p), out);
+    if (p.dtype != MOE_DTYPE_F32 && p.H % 8 == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
+        const unsigned blocks = static_cast<unsigned>((n / 8 + 255) / 256);
+        combine_bf16x8_kernel<<<blocks, 256, 0, stream>>>(static_cast<const uint16_t*>(y), slot_to_row, p.T, p.K,
+                                                         p.H, p.shared, total_rows(p), g.ksplit,
+                                                         static_cast<uint16_t*>(out));
+    } else {
+        const unsigned blocks = static_cast<unsigned>((n + 255) / 256);
+        if (p.dtype != MOE_DTYPE_F32)
+            combine_kernel<PolBF16><<<blocks, 256, 0, stream>>>(y, slot_to_row, p.T, p.K, p.H, p.shared, total_rows(p), g.ksplit, out);
+        else
+            combine_kernel<PolF32><<<blocks, 256, 0, stream>>>(y, slot_to_row, p.T, p.K, p.H, p.shared, total_rows(p), g.ksplit, out);
+    }
     return hipGetLastError();
 }
 

@@ -19,7 +19,7 @@
 
 namespace moe {
 
-template <int BM, int BN, int WM, int WN, int MODE, int GM>
+template <int BM, int BN, int WM, int WN, int MODE>
 __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
     constexpr int ROWB = 128;                     // one 128-wide k block per stage
     constexpr int NW = WM * WN;
@@ -52,7 +52,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
     const int wave = tid / kWave;
     const int wm = wave / WN, wn = wave % WN;
 
-    const TilePos tp = map_block(blockIdx.x, *g.num_tiles, g.n_tiles_n, GM);
+    const TilePos tp = map_block(blockIdx.x, *g.num_tiles, g.n_tiles_n, g.tiles);
     if (!tp.ok) return;
     const Tile tl = g.tiles[tp.m];
     const int n_tile = tp.n;

@@ -46,6 +46,9 @@ struct GemmArgs {
     const float* B_scale;       // [E, N/128, Kd/128]
     const float* B_shared_scale;  // [N/128, Kd/128]
     float* C_scale;             // w13: [R, I/128]
+    // w2 split over K: ksplit parts, part p writing y + p * part_stride
+    int32_t ksplit;
+    int64_t part_stride;
 };
 
 constexpr int kRowBytes = 128;               // bytes of one row per k-iteration
@@ -79,15 +82,17 @@ __device__ __forceinline__ int64_t b_weight_row(const GemmArgs& g, int n_tile, i
 
 // Block -> (m-tile, n-tile).  Workgroups are handed to the 8 XCDs round-
 // robin, so block b runs on XCD b % 8.  Each XCD takes one contiguous eighth
-// of the tile order; inside it, groups of GM m-tiles sweep the n-tiles with
-// the m index fastest.  Blocks resident together on an XCD then share their
-// A rows (same m-tiles) and weight tiles (same n-tile, same expert) in L2.
+// of the tile order; inside it, groups of m-tiles of one expert (at most 8,
+// so an expert with many m-tiles forms several groups) sweep the n-tiles
+// with the m index fastest.  Blocks resident together on an XCD then share
+// their A rows (same m-tiles) and weight tiles (same n-tile of the same
+// expert) in L2, and each weight tile is streamed once per group.
 struct TilePos {
     int m, n;
     bool ok;
 };
 
-__device__ __forceinline__ TilePos map_block(int bid, int num_m, int n_tiles, int GM) {
+__device__ __forceinline__ TilePos map_block(int bid, int num_m, int n_tiles, const Tile* tiles) {
     TilePos p{0, 0, false};
     const int total = num_m * n_tiles;
     const int per = (total + 7) / 8;
@@ -95,12 +100,14 @@ __device__ __forceinline__ TilePos map_block(int bid, int num_m, int n_tiles, in
     if (local >= per) return p;
     const int t = xcd * per + local;
     if (t >= total) return p;
-    const int span = GM * n_tiles;
-    const int group = t / span, first = group * GM;
-    const int gm = num_m - first < GM ? num_m - first : GM;
-    const int w = t - group * span;
-    p.m = first + w % gm;
-    p.n = w / gm;
+    // group g (m-tiles first .. first+cnt-1) owns tile-order positions
+    // [first * n_tiles, (first + cnt) * n_tiles), so t / n_tiles is one of
+    // its m-tiles and that tile names the group
+    const int grp = tiles[t / n_tiles].group;
+    const int first = grp >> 8, cnt = grp & 255;
+    const int w = t - first * n_tiles;
+    p.m = first + w % cnt;
+    p.n = w / cnt;
     p.ok = true;
     return p;
 }
@@ -171,7 +178,7 @@ __device__ __forceinline__ void mix_sched() {
     }
 }
 
-template <int BM, int BN, int WM, int WN, int ROWB, int MODE, int GM>
+template <int BM, int BN, int WM, int WN, int ROWB, int MODE>
 __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -205,10 +212,14 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
     const int wave = tid / kWave;
     const int wm = wave / WN, wn = wave % WN;
 
-    const TilePos tp = map_block(blockIdx.x, *g.num_tiles, g.n_tiles_n, GM);
+    // w2 may split K: the n index runs over (part, n-tile), n-tile fastest,
+    // so blocks resident together share the part's A columns
+    const int nparts = MODE == kModeW2 ? g.ksplit : 1;
+    const TilePos tp = map_block(blockIdx.x, *g.num_tiles, g.n_tiles_n * nparts, g.tiles);
     if (!tp.ok) return;
     const Tile tl = g.tiles[tp.m];
-    const int n_tile = tp.n;
+    const int kpart = tp.n / g.n_tiles_n;
+    const int n_tile = tp.n - kpart * g.n_tiles_n;
     const int64_t eltK = static_cast<int64_t>(g.Kd) * 2;
     const uint8_t* Bexp = tl.expert < g.E
                               ? g.B + static_cast<int64_t>(tl.expert) * g.N * eltK
@@ -230,17 +241,26 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
         }
         src[q] = base + chunk * 16;
     }
-    const int nk = static_cast<int>(eltK / ROWB);
+    // this block's k-iterations: part kpart of the nk_all of a full row
+    const int nk_all = static_cast<int>(eltK / ROWB);
+    const int k_first = kpart * nk_all / nparts;
+    const int nk = (kpart + 1) * nk_all / nparts - k_first;
+#pragma unroll
+    for (int q = 0; q < COPIES; ++q) src[q] += static_cast<int64_t>(k_first) * ROWB;
 
     // copies of k-iteration `it` into its stage buffer; past the last
     // k-iteration the source is clamped to it (a redundant in-bounds copy
     // into a buffer nobody reads again keeps the copy count per k-iteration
     // fixed and the loop free of branches)
-    auto issue_stage = [&](int it) {
-        uint8_t* dst = smem + (it % STAGES) * STAGE + wave * COPIES * 1024;
-        const int64_t off = static_cast<int64_t>(it < nk ? it : nk - 1) * ROWB;
+    // copies q0 .. q1-1 of this wave's share of k-iteration `kit`; past the
+    // last k-iteration the source is clamped to it (a redundant in-bounds
+    // copy into a buffer nobody reads again keeps the copy count per
+    // k-iteration fixed and the loop free of branches)
+    auto issue_copies = [&](int kit, int q0, int q1) {
+        uint8_t* dst = smem + (kit % STAGES) * STAGE + wave * COPIES * 1024;
+        const int64_t off = static_cast<int64_t>(kit < nk ? kit : nk - 1) * ROWB;
 #pragma unroll
-        for (int q = 0; q < COPIES; ++q)
+        for (int q = q0; q < q1; ++q)
             __builtin_amdgcn_global_load_lds(
                 reinterpret_cast<const void*>(src[q] + off),
                 (__attribute__((address_space(3))) void*)(dst + q * 1024), 16, 0, 0);
@@ -299,18 +319,8 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
                 __builtin_bit_cast(bf16x8, fa[m / TN]), __builtin_bit_cast(bf16x8, fb[m % TN]),
                 acc[m / TN][m % TN], 0, 0, 0);
     };
-    // copies q0 .. q1-1 of this wave's share of k-iteration `kit`
-    auto issue_copies = [&](int kit, int q0, int q1) {
-        uint8_t* dst = smem + (kit % STAGES) * STAGE + wave * COPIES * 1024;
-        const int64_t off = static_cast<int64_t>(kit < nk ? kit : nk - 1) * ROWB;
 #pragma unroll
-        for (int q = q0; q < q1; ++q)
-            __builtin_amdgcn_global_load_lds(
-                reinterpret_cast<const void*>(src[q] + off),
-                (__attribute__((address_space(3))) void*)(dst + q * 1024), 16, 0, 0);
-    };
-#pragma unroll
-    for (int st = 0; st < STAGES - 1; ++st) issue_stage(st);
+    for (int st = 0; st < STAGES - 1; ++st) issue_copies(st, 0, COPIES);
     wait_later_stages();
     __builtin_amdgcn_s_barrier();
     u32x4 af[2][TM], bfr[2][TN];
@@ -375,7 +385,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
                 }
             }
     } else {
-        uint16_t* y = static_cast<uint16_t*>(g.C);
+        uint16_t* y = static_cast<uint16_t*>(g.C) + kpart * g.part_stride;
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll

@@ -14,7 +14,7 @@ struct Tile {
     int32_t expert;
     int32_t row0;
     int32_t row1;
-    int32_t pad;
+    int32_t group;  // (index of the group's first m-tile) * 256 + m-tiles in the group
 };
 
 hipError_t launch_topk(const float* logits, const float* bias, int64_t T, int E, int K,

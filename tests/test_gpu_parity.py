@@ -41,6 +41,9 @@ SMALL = {
     "single_expert": MC("single_expert", E=1, K=1, H=128, I=128, T=33, seed=17, weight_seed=17),
     "f32_ragged": MC("f32_ragged", E=6, K=3, H=192, I=320, T=97, act_dtype="f32", w_dtype="f32",
                      seed=18, weight_seed=18),
+    # few w2 tiles and a long reduction: the down projection splits K in two
+    # parts whose partial outputs the combine sums
+    "w2_split_k": MC("w2_split_k", E=4, K=2, H=256, I=4096, T=257, seed=19, weight_seed=19),
 }
 
 
