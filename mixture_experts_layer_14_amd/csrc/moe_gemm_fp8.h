@@ -10,9 +10,15 @@
 //   w2:   y[r, h] = w_r * sum_kb sa2[r, kb] * sw2[e, h/128, kb] * (...)
 // One k-iteration is exactly one 128-wide scale block: two 32x32x64 fp8 MFMAs
 // accumulate the raw block product, which is then scaled and added to the
-// fp32 accumulator.  Staging, swizzle and tile order follow tile_kernel; the
-// per-row A scales of each k-block ride in the same LDS stage, copied by a
-// 4-byte gathered global_load_lds.
+// fp32 accumulator.  The MFMAs take the weight rows as their first operand,
+// so an accumulator lane holds one token and 16 output features of one
+// 32-feature block: both scales of a block product are then one value per
+// lane and MFMA tile, and the promotion costs one FMA per element (with
+// tokens as the first operand every element would need its own scale
+// product, which makes the vector ALU, not the matrix core, the limit).
+// Staging, swizzle, tile order and the pipeline follow tile_kernel; each
+// stage also carries the k-block's per-token A scales and the weight block
+// scales, copied by 4-byte gathered global_load_lds.
 #pragma once
 
 #include "moe_gemm_kernels.h"
@@ -23,27 +29,38 @@ template <int BM, int BN, int WM, int WN, int MODE>
 __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
     constexpr int ROWB = 128;                     // one 128-wide k block per stage
     constexpr int NW = WM * WN;
-    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int WTM = BM / WM, WTN = BN / WN;   // tokens x features per wave
     constexpr int TM = WTM / 32, TN = WTN / 32;
     constexpr int ROWS = BM + BN;
     constexpr int SLOTS = ROWB / 16;
     constexpr int RPC = kWave / SLOTS;             // rows per 16-byte copy instruction
     constexpr int COPIES = ROWS / RPC / NW;
     constexpr int SROWS = BM / NW;                 // A-scale rows copied per wave
-    constexpr int STAGE = ROWS * ROWB + BM * 4;    // rows, then the A scales
+    // weight-scale blocks per stage: w13 tiles interleave gate and up rows in
+    // 32-row blocks (one 128-row scale block of each), w2 tiles hold BN/128
+    // consecutive scale blocks
+    constexpr int NBS = MODE == kModeW13 ? 2 : BN / 128;
+    // stage: A rows, B rows, then one 256-byte scale slot per wave (lane l of
+    // wave w at byte 4l: A scale of token w*SROWS+l for l < SROWS; wave 0
+    // also holds the weight block scales at lanes SROWS .. SROWS+NBS-1)
+    constexpr int SCALES = NW * 256;
+    constexpr int STAGE = ROWS * ROWB + SCALES;
     constexpr int PER_STAGE = COPIES + 1;          // copy instructions per wave per stage
     constexpr int LDS_MAX = 160 * 1024;
-    constexpr int STAGES = 3 * STAGE <= LDS_MAX ? 3 : 2;
-    static_assert(ROWS % (RPC * NW) == 0 && BM % RPC == 0 && BM % NW == 0 && SROWS <= kWave, "copy split");
+    constexpr int ROW_W_BYTES = MODE == kModeW2 ? BM * 4 : 0;
+    constexpr int STAGES = 4 * STAGE + ROW_W_BYTES <= LDS_MAX ? 4 : 3;
+    constexpr int KSTEPS = 2;                      // 64-value MFMA steps per k block
+    static_assert(ROWS % (RPC * NW) == 0 && BM % RPC == 0 && BM % NW == 0, "copy split");
+    static_assert(SROWS + NBS <= kWave, "scale slots of wave 0");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
     static_assert(MODE != kModeW2 || NW * kWave >= BM, "one thread per row weight");
     static_assert(MODE != kModeW13 || (TN == 2 && BN == 256 && WN == 4),
-                  "w13 fp8: each wave holds one 32-column gate/up pair, a block one 128-column group");
+                  "w13 fp8: each wave holds one 32-feature gate/up pair, a block one 128-feature group");
     static_assert(PER_STAGE * (STAGES - 2) <= 63, "vmcnt immediate range");
+    static_assert(MODE != kModeW13 || BM * WN * 4 <= STAGE, "w13 amax exchange fits one stage");
     // one LDS object: the stage buffers, then (w2) the tile's routing
     // weights.  A second __shared__ array would make the compiler wait for
     // every copy in flight before each LDS read of the main loop.
-    constexpr int ROW_W_BYTES = MODE == kModeW2 ? BM * 4 : 0;
     static_assert(STAGES * STAGE + ROW_W_BYTES <= LDS_MAX, "LDS budget");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE + ROW_W_BYTES];
 
@@ -78,42 +95,46 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
         }
         src[q] = base + chunk * 16;
     }
-    // A-scale row copied by this lane (lanes >= SROWS idle)
+    // scale copied by this lane: an A-scale row (lanes < SROWS) or, in wave
+    // 0, a weight-scale row (lanes SROWS .. SROWS+NBS-1).  The other lanes
+    // copy the wave's first A-scale row into slots nobody reads, so the copy
+    // needs no exec mask (a branch would split the loop's scheduling region)
     const float* ssrc;
     {
-        const int row = wave * SROWS + (lane < SROWS ? lane : 0);
-        int64_t r = tl.row0 + row;
+        const int l = lane < SROWS ? lane : 0;
+        int64_t r = tl.row0 + wave * SROWS + l;
         if (r >= tl.row1) r = tl.row0;
         ssrc = g.A_scale + a_source_row<MODE>(g, r) * nkb;
+        if (wave == 0 && lane >= SROWS && lane < SROWS + NBS) {
+            const int slot = lane - SROWS;
+            const int rep = MODE == kModeW13 ? slot * 32 : slot * 128;  // a local row of the block
+            const int b = static_cast<int>(b_weight_row<MODE, BN, 32>(g, n_tile, rep) / 128);
+            ssrc = Bsc + static_cast<int64_t>(b) * nkb;
+        }
     }
 
-    auto issue_stage = [&](int it) {
-        uint8_t* st = smem + (it % STAGES) * STAGE;
-        const int64_t off = static_cast<int64_t>(it) * ROWB;
+    // copies q0 .. q1-1 (and, with q1 == COPIES, the scales) of this wave's
+    // share of k-block `kit`; past the last k-block the source is clamped to
+    // it, keeping the copy count per k-block fixed and the loop branch-free
+    auto issue_copies = [&](int kit, int q0, int q1) {
+        uint8_t* st = smem + (kit % STAGES) * STAGE;
+        const int kc = kit < nkb ? kit : nkb - 1;
+        const int64_t off = static_cast<int64_t>(kc) * ROWB;
 #pragma unroll
-        for (int q = 0; q < COPIES; ++q)
+        for (int q = q0; q < q1; ++q)
             __builtin_amdgcn_global_load_lds(
                 reinterpret_cast<const void*>(src[q] + off),
                 (__attribute__((address_space(3))) void*)(st + (wave * COPIES + q) * 1024), 16, 0, 0);
-        if (lane < SROWS)
+        if (q1 == COPIES)
             __builtin_amdgcn_global_load_lds(
-                reinterpret_cast<const void*>(ssrc + it),
-                (__attribute__((address_space(3))) void*)(st + ROWS * ROWB + wave * SROWS * 4), 4, 0, 0);
+                reinterpret_cast<const void*>(ssrc + kc),
+                (__attribute__((address_space(3))) void*)(st + ROWS * ROWB + wave * 256), 4, 0, 0);
     };
-    auto wait_copies = [&](int later) {
-        if (STAGES >= 3 && later >= 1) {
-            constexpr int n = PER_STAGE;
-            __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
-        } else {
-            __builtin_amdgcn_s_waitcnt(0x0F70);
-        }
+    // this wave's copies of all but the STAGES-2 most recent stages landed
+    auto wait_later_stages = [&]() {
+        constexpr int n = (STAGES - 2) * PER_STAGE;
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
     };
-
-    // weight-scale row block of each 32-column tile of this wave
-    int nblk[TN];
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-        nblk[j] = static_cast<int>(b_weight_row<MODE, BN, 32>(g, n_tile, wn * WTN + j * 32) / 128);
 
     f32x16 acc[TM][TN];
 #pragma unroll
@@ -124,7 +145,6 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
     const int lrow = lane % 32, khalf = lane / 32;
-    const int crow = khalf * 4;
 
     // w2: the tile's routing weights, loaded into a register before the main
     // loop and moved to LDS after it (no copy left in flight to wait for)
@@ -134,124 +154,156 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
         const int64_t r = tl.row0 + tid;
         if (r < tl.row1) my_w = row_weight(g, r);
     }
-#pragma unroll
-    for (int st = 0; st < STAGES - 1; ++st)
-        if (st < nkb) issue_stage(st);
-    for (int it = 0; it < nkb; ++it) {
-        wait_copies(min(STAGES - 2, nkb - 1 - it));
-        __builtin_amdgcn_s_barrier();
-        if (it + STAGES - 1 < nkb) issue_stage(it + STAGES - 1);
 
-        const uint8_t* sA = smem + (it % STAGES) * STAGE;
+    // 32 bytes of row r for MFMA step s: 16-byte chunks 4s + 2*khalf, +1
+    auto read_frag = [&](const uint8_t* base, int r, int s) {
+        const int c0 = s * 4 + khalf * 2;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(base + r * ROWB + lds_slot<ROWB>(r, c0) * 16);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(base + r * ROWB + lds_slot<ROWB>(r, c0 + 1) * 16);
+        return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    };
+    auto read_step = [&](const uint8_t* sA, int s, i32x8 (&fa)[TM], i32x8 (&fb)[TN]) {
         const uint8_t* sB = sA + BM * ROWB;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[i] = read_frag(sA, wm * WTM + i * 32 + lrow, s);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[j] = read_frag(sB, wn * WTN + j * 32 + lrow, s);
+    };
+    constexpr int kReads = 2 * (TM + TN), kMfma = TM * TN;
+    // blk[i][j]: weight rows (features) x tokens; formats 0/0 are fp8 e4m3
+    // with unit (2^0) block scales
+    f32x16 blk[TM][TN];
+    auto mfma_range = [&](int lo, int hi, const i32x8 (&fa)[TM], const i32x8 (&fb)[TN], bool first) {
+#pragma unroll
+        for (int m = lo; m < hi; ++m) {
+            const f32x16 c = first ? f32x16{} : blk[m / TN][m % TN];
+            blk[m / TN][m % TN] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                fb[m % TN], fa[m / TN], c, 0, 0, 0, 127, 0, 127);
+        }
+    };
+
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st) issue_copies(st, 0, COPIES);
+    wait_later_stages();
+    __builtin_amdgcn_s_barrier();
+    i32x8 af[2][TM], bfr[2][TN];
+    read_step(smem, 0, af[0], bfr[0]);
+    for (int it = 0; it < nkb; ++it) {
+        const uint8_t* sA = smem + (it % STAGES) * STAGE;
         const float* sS = reinterpret_cast<const float*>(sA + ROWS * ROWB);
-        f32x16 blk[TM][TN];
+        // this k-block's scales: the A scale of each of the lane's tokens, the
+        // weight scale of each of its 32-feature blocks (read before the
+        // barrier below releases the buffer)
+        float sa[TM], sw[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int t = wm * WTM + i * 32 + lrow;
+            sa[i] = sS[(t / SROWS) * 64 + t % SROWS];
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int lr = wn * WTN + j * 32;
+            sw[j] = sS[SROWS + (MODE == kModeW13 ? (lr / 32) % 2 : lr / 128)];
+        }
+        // step 0: step-1 reads, then this wave's copies of k-block
+        // it+STAGES-1 (buffer of k-block it-1, free since the last barrier)
+        read_step(sA, 1, af[1], bfr[1]);
+        issue_copies(it + STAGES - 1, 0, COPIES);
+        mfma_range(0, kMfma, af[0], bfr[0], true);
+        mix_sched<kMfma, kReads, PER_STAGE>();
+        __builtin_amdgcn_sched_barrier(0);
+        // step 1, split around the barrier that publishes k-block it+1
+        constexpr int H = kMfma / 2;
+        mfma_range(0, H, af[1], bfr[1], false);
+        __builtin_amdgcn_sched_group_barrier(0x008, H, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage it landed
+        wait_later_stages();
+        __builtin_amdgcn_s_barrier();
+        read_step(smem + ((it + 1) % STAGES) * STAGE, 0, af[0], bfr[0]);
+        mfma_range(H, kMfma, af[1], bfr[1], false);
+        mix_sched<kMfma - H, kReads, 0>();
+        __builtin_amdgcn_sched_barrier(0);
+        // promote the block product: one scale per (token tile, feature tile)
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) blk[i][j][v] = 0.0f;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int c0 = s * 4 + khalf * 2;
-            i32x8 af[TM], bfr[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int r = wm * WTM + i * 32 + lrow;
-                const u32x4 lo = *reinterpret_cast<const u32x4*>(sA + r * ROWB + lds_slot<ROWB>(r, c0) * 16);
-                const u32x4 hi = *reinterpret_cast<const u32x4*>(sA + r * ROWB + lds_slot<ROWB>(r, c0 + 1) * 16);
-                af[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-            }
-#pragma unroll
             for (int j = 0; j < TN; ++j) {
-                const int r = wn * WTN + j * 32 + lrow;
-                const u32x4 lo = *reinterpret_cast<const u32x4*>(sB + r * ROWB + lds_slot<ROWB>(r, c0) * 16);
-                const u32x4 hi = *reinterpret_cast<const u32x4*>(sB + r * ROWB + lds_slot<ROWB>(r, c0 + 1) * 16);
-                bfr[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                const float sc = sa[i] * sw[j];
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = fmaf(blk[i][j][v], sc, acc[i][j][v]);
             }
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    // formats 0/0: both operands fp8 e4m3; unit (2^0) block scales
-                    blk[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bfr[j], blk[i][j],
-                                                                                0, 0, 0, 127, 0, 127);
-        }
-        // scale the block product: acc += blk * sa[row] * sw[n-block]
-        float sw[TN];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) sw[j] = Bsc[nblk[j] * nkb + it];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            f32x4 sa4[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                sa4[q] = *reinterpret_cast<const f32x4*>(sS + wm * WTM + i * 32 + 8 * q + crow);
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    acc[i][j][v] = fmaf(blk[i][j][v], sa4[v / 4][v % 4] * sw[j], acc[i][j][v]);
-        }
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): reads done before the buffer is refilled
     }
+    // no copy may still write LDS when the block ends or LDS is reused
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
-    const int ccol = lane % 32;
+    // lane holds token wm*WTM + i*32 + lrow and, of each 32-feature tile j,
+    // the features 8*(v/4) + 4*khalf + v%4
     if constexpr (MODE == kModeW13) {
-        // act = silu(g) * u; the block's 128 act columns are one quantisation
-        // group: per-row amax over this wave's 32 columns (lanes of equal
-        // khalf), then over the 4 waves of the row band through LDS
+        // act = silu(g) * u; the block's 128 act features are one quantisation
+        // group: per-token amax over this wave's 32 features (16 per lane,
+        // two lanes per token), then over the WN waves through LDS
         __syncthreads();
         float* red = reinterpret_cast<float*>(smem);  // [BM][WN]
         float act[TM][16];
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i) {
+            float m = 0.0f;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 act[i][v] = silu_mul(acc[i][0][v], acc[i][1][v]);
-                float m = fabsf(act[i][v]);
-#pragma unroll
-                for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
-                if (ccol == 0) red[(wm * WTM + i * 32 + 8 * (v / 4) + crow + (v % 4)) * WN + wn] = m;
+                m = fmaxf(m, fabsf(act[i][v]));
             }
+            m = fmaxf(m, __shfl_xor(m, 32, kWave));
+            if (khalf == 0) red[(wm * WTM + i * 32 + lrow) * WN + wn] = m;
+        }
         __syncthreads();
         uint8_t* q = static_cast<uint8_t*>(g.C);
-        const int64_t col = static_cast<int64_t>(n_tile) * 128 + wn * 32 + ccol;
         const int ngroups = g.I / 128;
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i) {
+            const int lt = wm * WTM + i * 32 + lrow;
+            float amax = red[lt * WN];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int lr = wm * WTM + i * 32 + 8 * (v / 4) + crow + (v % 4);
-                float amax = red[lr * WN];
+            for (int w = 1; w < WN; ++w) amax = fmaxf(amax, red[lt * WN + w]);
+            const float scale = fmaxf(amax, 1e-10f) / 448.0f;
+            const int64_t r = tl.row0 + lt;
+            if (r < tl.row1) {
+                uint8_t* qrow = q + r * g.I + static_cast<int64_t>(n_tile) * 128 + wn * 32 + 4 * khalf;
 #pragma unroll
-                for (int w = 1; w < WN; ++w) amax = fmaxf(amax, red[lr * WN + w]);
-                const float scale = fmaxf(amax, 1e-10f) / 448.0f;
-                const int64_t r = tl.row0 + lr;
-                if (r < tl.row1) {
-                    q[r * g.I + col] = f32_to_e4m3(act[i][v] / scale);
-                    if (wn == 0 && ccol == 0) g.C_scale[r * ngroups + n_tile] = scale;
+                for (int b = 0; b < 4; ++b) {
+                    uint32_t word = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        word |= static_cast<uint32_t>(f32_to_e4m3(act[i][4 * b + e] / scale)) << (8 * e);
+                    *reinterpret_cast<uint32_t*>(qrow + 8 * b) = word;
                 }
+                if (wn == 0 && khalf == 0) g.C_scale[r * ngroups + n_tile] = scale;
             }
+        }
     } else {
         if (tid < BM) row_w[tid] = my_w;
         __syncthreads();
         uint16_t* y = static_cast<uint16_t*>(g.C);
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i) {
+            const int lt = wm * WTM + i * 32 + lrow;
+            const int64_t r = tl.row0 + lt;
+            if (r >= tl.row1) continue;
+            const float w = row_w[lt];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int lr = wm * WTM + i * 32 + 8 * (v / 4) + crow + (v % 4);
-                const int64_t r = tl.row0 + lr;
-                if (r >= tl.row1) continue;
-                const float w = row_w[lr];
+            for (int j = 0; j < TN; ++j) {
+                uint16_t* yrow = y + r * g.N + static_cast<int64_t>(n_tile) * BN + wn * WTN + j * 32 + 4 * khalf;
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int64_t c = static_cast<int64_t>(n_tile) * BN + wn * WTN + j * 32 + ccol;
-                    y[r * g.N + c] = f32_to_bf16_bits(acc[i][j][v] * w);
+                for (int b = 0; b < 4; ++b) {
+                    const uint32_t lo = static_cast<uint32_t>(f32_to_bf16_bits(acc[i][j][4 * b] * w)) |
+                                        (static_cast<uint32_t>(f32_to_bf16_bits(acc[i][j][4 * b + 1] * w)) << 16);
+                    const uint32_t hi = static_cast<uint32_t>(f32_to_bf16_bits(acc[i][j][4 * b + 2] * w)) |
+                                        (static_cast<uint32_t>(f32_to_bf16_bits(acc[i][j][4 * b + 3] * w)) << 16);
+                    *reinterpret_cast<uint2*>(yrow + 8 * b) = make_uint2(lo, hi);
                 }
             }
+        }
     }
 }
 
