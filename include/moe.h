@@ -28,8 +28,11 @@
  * Conventions for every call
  *   - Every pointer argument is DEVICE memory unless marked "host".  The
  *     caller owns all buffers; the library never allocates in a call.
- *   - All arrays are dense row-major.  bf16 = IEEE binary32 upper half;
- *     fp8 = OCP e4m3 ("e4m3fn", max 448) stored one byte per value.
+ *   - All arrays are dense row-major, except the expert weight matrices
+ *     (w13, w2, shared_w13, shared_w2), which the GEMM calls take in the
+ *     packed layout written by moe_pack_weights.  bf16 = IEEE binary32 upper
+ *     half; fp8 = OCP e4m3 ("e4m3fn", max 448) stored one byte per value.
+ *     Weight block scales stay row-major.
  *   - `stream` is a hipStream_t passed as void* (NULL: the null stream).
  *     Calls only enqueue work: no host synchronisation, no allocation, so a
  *     sequence of calls may be captured into a HIP graph.
@@ -98,6 +101,21 @@ size_t moe_workspace_size(const moe_params *p);
 /* Human-readable name of a status code (static string, never NULL). */
 const char *moe_status_string(int status);
 
+/* Weight re-layout, done once when the weights are loaded.  Each of
+ * `matrices` row-major matrices of `rows` rows x `row_bytes` bytes (an
+ * expert's [2I, H] gate/up or [H, I] down matrix, any element type) is
+ * rewritten as [rows/16][row_bytes/64][16][64]: the 64-byte pieces of 16
+ * consecutive rows that share a k range become one contiguous KiB, which is
+ * the unit the GEMM kernels fetch.  Element values are copied bit for bit.
+ * Not a step of the pages' method: a storage layout of this library.
+ *   src  [matrices, rows, row_bytes] bytes, row-major.
+ *   dst  same size, packed out; must not overlap src.
+ * Errors: MOE_ERR_INVALID for negative sizes, rows % 16 != 0,
+ * row_bytes % 64 != 0, NULL pointers with a non-empty size, src or dst not
+ * 16-byte aligned, overlap. */
+int moe_pack_weights(const void *src, void *dst, int64_t matrices, int64_t rows,
+                     int64_t row_bytes, void *stream);
+
 /* Router: top-k expert selection and routing weights per token.
  * Passage: FusedMoE.select_experts (vLLM page), grouped top-k and
  * e_score_correction_bias (vLLM page; DeepseekV2MoE TopK arguments and
@@ -154,8 +172,10 @@ int moe_quant_act_fp8(const moe_params *p, const void *hidden, uint8_t *q,
  * DeepseekV2MLP gate_up_proj -> SiluAndMul (SGLang deepseek_v2 page).
  *   hidden       [T, H]: act dtype; for fp8 weights the e4m3 codes from
  *                moe_quant_act_fp8 with hidden_scale [T, H/128].
- *   w13          [E, 2I, H] (+ w13_scale [E, 2I/128, H/128] for fp8).
- *   shared_w13   [2I, H] (+ scale) when num_shared_experts == 1, else NULL.
+ *   w13          [E, 2I, H] packed by moe_pack_weights (+ w13_scale
+ *                [E, 2I/128, H/128] row-major for fp8).
+ *   shared_w13   [2I, H] packed (+ scale) when num_shared_experts == 1,
+ *                else NULL.
  *   expert_offsets, sorted_slots: from moe_align_permute.
  *   act          [T*K + T*S, I] out (S = num_shared_experts): row r holds
  *                silu(g) * u for the token of sorted_slots[r] (rows
@@ -178,8 +198,9 @@ int moe_grouped_gemm_w13_act(const moe_params *p, const void *hidden,
  * expert with weight 1 and the routed part scaled by routed_scaling_factor
  * (already folded into topk_weights here).
  *   act, act_scale  from moe_grouped_gemm_w13_act.
- *   w2         [E, H, I] (+ w2_scale [E, H/128, I/128] for fp8).
- *   shared_w2  [H, I] (+ scale) or NULL.
+ *   w2         [E, H, I] packed by moe_pack_weights (+ w2_scale
+ *              [E, H/128, I/128] row-major for fp8).
+ *   shared_w2  [H, I] packed (+ scale) or NULL.
  *   topk_weights [T, K] fp32 from moe_topk; slot_to_row [T*K].
  *   out        [T, H] out_dtype:  out_t = sum_k w_{t,k} y_{row(t,k)}
  *              (+ y_{T*K+t} of the shared expert).  The sum over k runs in a

@@ -22,9 +22,9 @@ F32, BF16, FP8_E4M3 = 0, 1, 2
 
 # every entry point that include/moe.h declares
 ENTRY_POINTS = (
-    "moe_workspace_size", "moe_status_string", "moe_topk", "moe_align_permute",
-    "moe_quant_act_fp8", "moe_grouped_gemm_w13_act", "moe_grouped_gemm_w2_combine",
-    "moe_forward",
+    "moe_workspace_size", "moe_status_string", "moe_pack_weights", "moe_topk",
+    "moe_align_permute", "moe_quant_act_fp8", "moe_grouped_gemm_w13_act",
+    "moe_grouped_gemm_w2_combine", "moe_forward",
 )
 
 
@@ -71,6 +71,7 @@ def load(path: str = LIB_PATH):
     L.moe_workspace_size.argtypes = [_P]
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_status_string.argtypes = [ctypes.c_int]
+    L.moe_pack_weights.argtypes = [_VP, _VP, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _VP]
     L.moe_topk.argtypes = [_P, _VP, _VP, _VP, _VP, _VP]
     L.moe_align_permute.argtypes = [_P, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]
     L.moe_quant_act_fp8.argtypes = [_P, _VP, _VP, _VP, _VP]
@@ -138,6 +139,23 @@ def moe_align_permute(p, topk_ids, expert_offsets, sorted_slots, slot_to_row, wo
                                   _ptr(sorted_slots), _ptr(slot_to_row), _ptr(workspace),
                                   _nbytes(workspace), _stream(stream))
     return _check("moe_align_permute", st, raise_on_error)
+
+
+def moe_pack_weights(src, dst, matrices, rows, row_bytes, stream=None, raise_on_error=True):
+    st = load().moe_pack_weights(_ptr(src), _ptr(dst), int(matrices), int(rows), int(row_bytes),
+                                 _stream(stream))
+    return _check("moe_pack_weights", st, raise_on_error)
+
+
+def pack_weights(w, stream=None):
+    """Packed copy of an expert weight tensor [..., rows, cols] (any dtype):
+    every trailing [rows, cols] matrix re-laid out for the GEMM calls."""
+    w = w.contiguous()
+    out = torch.empty_like(w)
+    rows, cols = w.shape[-2], w.shape[-1]
+    matrices = w.numel() // (rows * cols) if w.numel() else 0
+    moe_pack_weights(w, out, matrices, rows, cols * w.element_size(), stream)
+    return out
 
 
 def moe_quant_act_fp8(p, hidden, q, scale, stream=None, raise_on_error=True):

@@ -171,6 +171,21 @@ int moe_align_permute(const moe_params* p, const int32_t* topk_ids, int32_t* exp
                                         sorted_slots, slot_to_row, workspace, as_stream(stream)));
 }
 
+int moe_pack_weights(const void* src, void* dst, int64_t matrices, int64_t rows,
+                     int64_t row_bytes, void* stream) {
+    if (matrices < 0 || rows < 0 || row_bytes < 0) return MOE_ERR_INVALID;
+    if (rows % 16 != 0 || row_bytes % 64 != 0) return MOE_ERR_INVALID;
+    if (matrices == 0 || rows == 0 || row_bytes == 0) return MOE_OK;
+    if (!src || !dst) return MOE_ERR_INVALID;
+    // the product must fit the address space; then reject any overlap
+    if (rows > INT64_MAX / row_bytes || matrices > INT64_MAX / (rows * row_bytes)) return MOE_ERR_INVALID;
+    const uint64_t n = static_cast<uint64_t>(matrices * rows * row_bytes);
+    const uint64_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+    if (s0 < d0 + n && d0 < s0 + n) return MOE_ERR_INVALID;
+    if ((s0 | d0) & 15) return MOE_ERR_INVALID;
+    return hip_status(moe::launch_pack_weights(src, dst, matrices, rows, row_bytes, as_stream(stream)));
+}
+
 int moe_quant_act_fp8(const moe_params* p, const void* hidden, uint8_t* q, float* scale,
                       void* stream) {
     int st = check_params(p);

@@ -17,6 +17,14 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;  // 16 bytes, kept in VGPRs
 
+// Index of the calling thread's wave in its block, as a wave-uniform
+// (scalar) value.  Conditions built from it then compile to scalar branches:
+// an MFMA ignores EXEC, so an MFMA placed under a lane-mask branch would run
+// for the whole wave with stale operands.
+__device__ __forceinline__ int wave_index(int tid) {
+    return __builtin_amdgcn_readfirstlane(tid / kWave);
+}
+
 // Order-preserving map of an fp32 value onto uint32 (larger float -> larger
 // integer; -inf maps above 0, so 0 is below every real key).
 __device__ __forceinline__ uint32_t ordered_bits(float f) {

@@ -133,7 +133,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void grouped_gemm_kernel(GemmArgs g)
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
+    const int wave = wave_index(tid);
     const int wm = wave / WN, wn = wave % WN;
 
     // block -> (m-tile, n-tile); m-tiles of one n-tile are adjacent so the
@@ -180,7 +180,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void grouped_gemm_kernel(GemmArgs g)
         } else {
             wrow = static_cast<int64_t>(n_tile) * BN + row;
         }
-        b_ptr[q] = Bexp + wrow * eltK + c16 * 16;
+        b_ptr[q] = Bexp + packed_offset(wrow, c16 * 16, eltK);
     }
 
     f32x4 acc[TM][TN];
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void grouped_gemm_kernel(GemmArgs g)
                 if (a_on[q]) ra[q] = *reinterpret_cast<const u32x4*>(a_ptr[q] + off);
 #pragma unroll
             for (int q = 0; q < B_ITEMS; ++q)
-                if (b_on[q]) rb[q] = *reinterpret_cast<const u32x4*>(b_ptr[q] + off);
+                if (b_on[q]) rb[q] = *reinterpret_cast<const u32x4*>(b_ptr[q] + off * 16);  // packed
         }
         u32x4 af[TM][2], bf[TN][2];
         const int lrow = lane % 16, lk = (lane / 16) * 16;

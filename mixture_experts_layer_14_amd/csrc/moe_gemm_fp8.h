@@ -66,7 +66,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
+    const int wave = wave_index(tid);
     const int wm = wave / WN, wn = wave % WN;
 
     const TilePos tp = map_block(blockIdx.x, *g.num_tiles, g.n_tiles_n, g.tiles);
@@ -85,15 +85,13 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
     for (int q = 0; q < COPIES; ++q) {
         const int row = (wave * COPIES + q) * RPC + lane / SLOTS;
         const int chunk = lds_slot<ROWB>(row, lane % SLOTS);
-        const uint8_t* base;
         if (row < BM) {
             int64_t r = tl.row0 + row;
             if (r >= tl.row1) r = tl.row0;
-            base = g.A + a_source_row<MODE>(g, r) * K;
+            src[q] = g.A + a_source_row<MODE>(g, r) * K + chunk * 16;
         } else {
-            base = Bexp + b_weight_row<MODE, BN, 32>(g, n_tile, row - BM) * K;
+            src[q] = Bexp + packed_offset(b_weight_row<MODE, BN, 32>(g, n_tile, row - BM), chunk * 16, K);
         }
-        src[q] = base + chunk * 16;
     }
     // scale copied by this lane: an A-scale row (lanes < SROWS) or, in wave
     // 0, a weight-scale row (lanes SROWS .. SROWS+NBS-1).  The other lanes
@@ -123,7 +121,8 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
 #pragma unroll
         for (int q = q0; q < q1; ++q)
             __builtin_amdgcn_global_load_lds(
-                reinterpret_cast<const void*>(src[q] + off),
+                // packed B (the later copies) advances 16x faster along k
+                reinterpret_cast<const void*>(src[q] + ((wave * COPIES + q) * RPC >= BM ? off << 4 : off)),
                 (__attribute__((address_space(3))) void*)(st + (wave * COPIES + q) * 1024), 16, 0, 0);
         if (q1 == COPIES)
             __builtin_amdgcn_global_load_lds(

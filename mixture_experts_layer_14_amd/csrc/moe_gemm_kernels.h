@@ -25,8 +25,8 @@ enum { kModeW13 = 0, kModeW2 = 1 };
 struct GemmArgs {
     const uint8_t* A;           // hidden [T, H] (w13) or act [R, I] (w2)
     const int32_t* sorted_slots;
-    const uint8_t* B;           // expert weights [E, N, Kd]
-    const uint8_t* B_shared;    // shared expert weights [N, Kd] or null
+    const uint8_t* B;           // expert weights [E, N, Kd], each matrix packed
+    const uint8_t* B_shared;    // shared expert weights [N, Kd] packed, or null
     const Tile* tiles;
     const int32_t* num_tiles;
     const float* topk_weights;  // w2: routing weight of each slot
@@ -62,6 +62,15 @@ __device__ __forceinline__ int64_t a_source_row(const GemmArgs& g, int64_t r) {
     if (MODE == kModeW2) return r;
     int64_t src = r >= g.routed_rows ? r - g.routed_rows : g.sorted_slots[r] / g.topk;
     return src < 0 ? 0 : (src >= g.T ? g.T - 1 : src);
+}
+
+// Weights are stored packed: a matrix of `rows` rows of `row_bytes` bytes
+// is laid out as [rows/16][row_bytes/64][16][64], so 16 consecutive rows x
+// 64 bytes of k form one contiguous KiB.  That is exactly what one 16-row
+// copy instruction or one 16x16 MFMA k-step reads, turning 16 short
+// strided row pieces into one sequential burst.  Byte offset of (row, byte):
+__device__ __forceinline__ int64_t packed_offset(int64_t row, int64_t byte, int64_t row_bytes) {
+    return (row >> 4) * (row_bytes << 4) + (byte >> 6) * 1024 + (row & 15) * 64 + (byte & 63);
 }
 
 // Routing weight of permuted row r for the w2 epilogue (shared rows: 1).
@@ -209,7 +218,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
+    const int wave = wave_index(tid);
     const int wm = wave / WN, wn = wave % WN;
 
     // w2 may split K: the n index runs over (part, n-tile), n-tile fastest,
@@ -231,22 +240,23 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
     for (int q = 0; q < COPIES; ++q) {
         const int row = (wave * COPIES + q) * RPC + lane / SLOTS;
         const int chunk = lds_slot<ROWB>(row, lane % SLOTS);  // the swizzle is an involution
-        const uint8_t* base;
         if (row < BM) {
             int64_t r = tl.row0 + row;
             if (r >= tl.row1) r = tl.row0;  // ragged tail: copy a valid row, never stored
-            base = g.A + a_source_row<MODE>(g, r) * eltK;
+            src[q] = g.A + a_source_row<MODE>(g, r) * eltK + chunk * 16;
         } else {
-            base = Bexp + b_weight_row<MODE, BN, 32>(g, n_tile, row - BM) * eltK;
+            src[q] = Bexp + packed_offset(b_weight_row<MODE, BN, 32>(g, n_tile, row - BM), chunk * 16, eltK);
         }
-        src[q] = base + chunk * 16;
     }
     // this block's k-iterations: part kpart of the nk_all of a full row
     const int nk_all = static_cast<int>(eltK / ROWB);
     const int k_first = kpart * nk_all / nparts;
     const int nk = (kpart + 1) * nk_all / nparts - k_first;
+    // bytes per k-iteration along a source row: ROWB in the row-major A,
+    // ROWB/64 KiB-blocks in the packed B (whose copies are the later ones)
+    auto kstep_shift = [&](int q) { return (wave * COPIES + q) * RPC >= BM ? 4 : 0; };
 #pragma unroll
-    for (int q = 0; q < COPIES; ++q) src[q] += static_cast<int64_t>(k_first) * ROWB;
+    for (int q = 0; q < COPIES; ++q) src[q] += (static_cast<int64_t>(k_first) * ROWB) << kstep_shift(q);
 
     // copies of k-iteration `it` into its stage buffer; past the last
     // k-iteration the source is clamped to it (a redundant in-bounds copy
@@ -262,7 +272,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
 #pragma unroll
         for (int q = q0; q < q1; ++q)
             __builtin_amdgcn_global_load_lds(
-                reinterpret_cast<const void*>(src[q] + off),
+                reinterpret_cast<const void*>(src[q] + (off << kstep_shift(q))),
                 (__attribute__((address_space(3))) void*)(dst + q * 1024), 16, 0, 0);
     };
 
@@ -419,7 +429,7 @@ __global__ __launch_bounds__(WAVES * kWave) void stream_kernel(GemmArgs g) {
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
+    const int wave = wave_index(tid);
     const int m_tile = blockIdx.x % g.max_m_tiles;
     const int n_grp = blockIdx.x / g.max_m_tiles;
     if (m_tile >= *g.num_tiles) return;
@@ -440,7 +450,7 @@ __global__ __launch_bounds__(WAVES * kWave) void stream_kernel(GemmArgs g) {
     }
 #pragma unroll
     for (int j = 0; j < NPW; ++j)
-        b_ptr[j] = Bexp + b_weight_row<MODE, NPW * 16, 16>(g, n_grp, j * 16 + lrow) * eltK + lk;
+        b_ptr[j] = Bexp + packed_offset(b_weight_row<MODE, NPW * 16, 16>(g, n_grp, j * 16 + lrow), lk, eltK);
 
     f32x4 acc[TM][NPW];
 #pragma unroll
@@ -468,7 +478,7 @@ __global__ __launch_bounds__(WAVES * kWave) void stream_kernel(GemmArgs g) {
             if (s + u < s1) {
                 const int64_t off = static_cast<int64_t>(s + u) * 64;
 #pragma unroll
-                for (int j = 0; j < NPW; ++j) b[u][j] = *reinterpret_cast<const u32x4*>(b_ptr[j] + off);
+                for (int j = 0; j < NPW; ++j) b[u][j] = *reinterpret_cast<const u32x4*>(b_ptr[j] + off * 16);
 #pragma unroll
                 for (int i = 0; i < TM; ++i) a[u][i] = *reinterpret_cast<const u32x4*>(a_ptr[i] + off);
             }

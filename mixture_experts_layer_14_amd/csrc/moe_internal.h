@@ -42,6 +42,10 @@ size_t gemm_tile_workspace_bytes(const GroupedProblem& p);
 // Scratch bytes of the w2 GEMM's per-row outputs before the combine.
 size_t w2_rows_workspace_bytes(const GroupedProblem& p);
 
+// Packed weight layout (see moe_pack_weights): matrices x rows x row_bytes.
+hipError_t launch_pack_weights(const void* src, void* dst, int64_t matrices, int64_t rows,
+                               int64_t row_bytes, hipStream_t stream);
+
 hipError_t launch_w13(const GroupedProblem& p, const void* hidden, const float* hidden_scale,
                       const void* w13, const float* w13_scale, const void* shared_w13,
                       const float* shared_w13_scale, const int32_t* offsets,

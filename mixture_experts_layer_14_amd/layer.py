@@ -30,13 +30,19 @@ def params_for(cfg, T: int | None = None) -> B.MoeParams:
         out_dtype=_DT[cfg.act_dtype], num_shared_experts=cfg.shared)
 
 
+_PACKED = ("w13", "w2", "shared_w13", "shared_w2")
+
+
 class FusedMoE:
     """One layer: weights (w13, w2, optional scales and shared expert) plus a
-    workspace sized for the largest token count seen so far."""
+    workspace sized for the largest token count seen so far.  The weight
+    matrices are given row-major and kept in the library's packed layout
+    (moe_pack_weights, done once here); scales stay as given."""
 
     def __init__(self, params: B.MoeParams, weights: dict):
         self.params = params
-        self.w = weights
+        self.w = {k: (B.pack_weights(v) if k in _PACKED and v is not None else v)
+                  for k, v in weights.items()}
         self._ws = None
 
     def workspace(self, T: int) -> torch.Tensor:

@@ -104,3 +104,19 @@ def test_status_strings():
     for s in (0, -1, -2, -3, -4):
         assert B.status_string(s)
     assert B.status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, FAKE + (1 << 20), -1, 16, 64), B.MOE_ERR_INVALID),           # negative size
+    ((FAKE, FAKE + (1 << 20), 1, 8, 64), B.MOE_ERR_INVALID),             # rows % 16
+    ((FAKE, FAKE + (1 << 20), 1, 16, 48), B.MOE_ERR_INVALID),            # row_bytes % 64
+    ((None, FAKE, 1, 16, 64), B.MOE_ERR_INVALID),                        # NULL with data
+    ((FAKE, FAKE + 512, 1, 16, 64), B.MOE_ERR_INVALID),                  # overlap
+    ((FAKE + 8, FAKE + (1 << 20), 1, 16, 64), B.MOE_ERR_INVALID),        # misaligned
+    ((None, None, 0, 16, 64), B.MOE_OK),                                 # empty: nothing to do
+    ((None, None, 3, 0, 64), B.MOE_OK),
+])
+def test_pack_weights_validation(args, status):
+    L = B.load()
+    src, dst, m, r, rb = args
+    assert L.moe_pack_weights(src, dst, m, r, rb, None) == status
