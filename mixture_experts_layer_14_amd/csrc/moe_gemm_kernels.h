@@ -322,55 +322,71 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
         constexpr int n = (STAGES - 2) * COPIES;
         __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
     };
-    auto mfma_range = [&](int lo, int hi, const u32x4 (&fa)[TM], const u32x4 (&fb)[TN]) {
+    // A ragged last tile of an expert skips the MFMAs of 32-row blocks that
+    // lie wholly past its rows (copies, reads and barriers still run, so
+    // every wave keeps the block's pace).  act_tm: this wave's live row blocks,
+    // a scalar so the skip is a scalar branch (an MFMA ignores EXEC).
+    const int live_rows = static_cast<int>(tl.row1 - tl.row0) - wm * WTM;
+    const int act_tm = __builtin_amdgcn_readfirstlane(
+        live_rows <= 0 ? 0 : (live_rows >= WTM ? TM : (live_rows + 31) / 32));
+    auto main_loop = [&](auto partial_tag) {
+        constexpr bool PARTIAL = decltype(partial_tag)::value;
+        auto mfma_range = [&](int lo, int hi, const u32x4 (&fa)[TM], const u32x4 (&fb)[TN]) {
 #pragma unroll
-        for (int m = lo; m < hi; ++m)
-            acc[m / TN][m % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, fa[m / TN]), __builtin_bit_cast(bf16x8, fb[m % TN]),
-                acc[m / TN][m % TN], 0, 0, 0);
-    };
+            for (int m = lo; m < hi; ++m)
+                if (!PARTIAL || m / TN < act_tm)
+                    acc[m / TN][m % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, fa[m / TN]), __builtin_bit_cast(bf16x8, fb[m % TN]),
+                        acc[m / TN][m % TN], 0, 0, 0);
+        };
 #pragma unroll
-    for (int st = 0; st < STAGES - 1; ++st) issue_copies(st, 0, COPIES);
-    wait_later_stages();
-    __builtin_amdgcn_s_barrier();
-    u32x4 af[2][TM], bfr[2][TN];
-    read_step(smem, 0, af[0], bfr[0]);
-    // copies per k-step when a stage's copies are spread over the k-steps
-    // that precede the next barrier
-    constexpr int CPS = (COPIES + KSTEPS - 2) / (KSTEPS - 1);
-    for (int it = 0; it < nk; ++it) {
-        const uint8_t* sA = smem + (it % STAGES) * STAGE;
-        static_for<KSTEPS - 1>([&](auto sc) {
-            constexpr int s = decltype(sc)::value;
-            read_step(sA, s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
-            // stage it+STAGES-1 goes to the buffer of stage it-1, free since
-            // the previous barrier
-            constexpr int q0 = s * CPS < COPIES ? s * CPS : COPIES;
-            constexpr int q1 = (s + 1) * CPS < COPIES ? (s + 1) * CPS : COPIES;
-            issue_copies(it + STAGES - 1, q0, q1);
-            mfma_range(0, kMfma, af[s & 1], bfr[s & 1]);
-            mix_sched<kMfma, kReads, q1 - q0>();
-            __builtin_amdgcn_sched_barrier(0);
-        });
-        // the last k-step; in the last iteration the reads after the barrier
-        // fetch a buffer that is never used, so the loop body has no branch
-        constexpr int L = (KSTEPS - 1) & 1;
-        constexpr int H = kMfma / 2;
-        mfma_range(0, H, af[L], bfr[L]);
-        __builtin_amdgcn_sched_group_barrier(0x008, H, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        // this wave's reads of stage it have landed (the MFMAs above consumed
-        // the last of them); its copies of stage it+1 must land too, with
-        // those of stages it+2 .. it+STAGES-1 still in flight
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        for (int st = 0; st < STAGES - 1; ++st) issue_copies(st, 0, COPIES);
         wait_later_stages();
         __builtin_amdgcn_s_barrier();
-        // reads first: the compiler keeps LDS reads behind copies into LDS
-        read_step(smem + ((it + 1) % STAGES) * STAGE, 0, af[L ^ 1], bfr[L ^ 1]);
-        mfma_range(H, kMfma, af[L], bfr[L]);
-        mix_sched<kMfma - H, kReads, 0>();
-        __builtin_amdgcn_sched_barrier(0);
-    }
+        u32x4 af[2][TM], bfr[2][TN];
+        read_step(smem, 0, af[0], bfr[0]);
+        // copies per k-step when a stage's copies are spread over the k-steps
+        // that precede the next barrier
+        constexpr int CPS = (COPIES + KSTEPS - 2) / (KSTEPS - 1);
+        for (int it = 0; it < nk; ++it) {
+            const uint8_t* sA = smem + (it % STAGES) * STAGE;
+            static_for<KSTEPS - 1>([&](auto sc) {
+                constexpr int s = decltype(sc)::value;
+                read_step(sA, s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
+                // stage it+STAGES-1 goes to the buffer of stage it-1, free
+                // since the previous barrier
+                constexpr int q0 = s * CPS < COPIES ? s * CPS : COPIES;
+                constexpr int q1 = (s + 1) * CPS < COPIES ? (s + 1) * CPS : COPIES;
+                issue_copies(it + STAGES - 1, q0, q1);
+                mfma_range(0, kMfma, af[s & 1], bfr[s & 1]);
+                if constexpr (!PARTIAL) mix_sched<kMfma, kReads, q1 - q0>();
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            // the last k-step; in the last iteration the reads after the
+            // barrier fetch a buffer that is never used, so the loop body has
+            // no branch
+            constexpr int L = (KSTEPS - 1) & 1;
+            constexpr int H = kMfma / 2;
+            mfma_range(0, H, af[L], bfr[L]);
+            if constexpr (!PARTIAL) __builtin_amdgcn_sched_group_barrier(0x008, H, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            // this wave's reads of stage it have landed (the MFMAs above
+            // consumed the last of them); its copies of stage it+1 must land
+            // too, with those of stages it+2 .. it+STAGES-1 still in flight
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+            wait_later_stages();
+            __builtin_amdgcn_s_barrier();
+            // reads first: the compiler keeps LDS reads behind copies into LDS
+            read_step(smem + ((it + 1) % STAGES) * STAGE, 0, af[L ^ 1], bfr[L ^ 1]);
+            mfma_range(H, kMfma, af[L], bfr[L]);
+            if constexpr (!PARTIAL) mix_sched<kMfma - H, kReads, 0>();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    if (tl.row1 - tl.row0 == BM)
+        main_loop(std::false_type{});
+    else
+        main_loop(std::true_type{});
     // no copy may still write LDS when the block ends
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
