@@ -400,12 +400,22 @@ size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 // last wave of tiles would leave most of the 256 compute units idle, so the
 // reduction is cut into parts whose bf16 partial outputs the combine sums.
 // A function of the problem alone, so workspace sizing and launch agree.
+#ifndef MOE_W2_BIG
+#define MOE_W2_BIG 1
+#endif
+// The 256 x 256 tile (64-byte row slabs) for a GEMM with n output columns.
+static bool big_tile(const GroupedProblem& p, int mode, int64_t n) {
+    return (mode == kModeW13 || MOE_W2_BIG) && rows_per_active_expert(p) >= MOE_BIG_TILE_MIN_ROWS &&
+           n % 256 == 0;
+}
+
 static int w2_ksplit(const GroupedProblem& p) {
     if (p.dtype != MOE_DTYPE_BF16 || rows_per_active_expert(p) <= MOE_STREAM_MAX_ROWS) return 1;
     if (p.H % MOE_TILE_BN != 0) return 1;
     constexpr int64_t kCUs = 256;
-    const int64_t tiles = static_cast<int64_t>(max_m_tiles(p, MOE_TILE_BM)) * (p.H / MOE_TILE_BN);
-    const int64_t nk_all = static_cast<int64_t>(p.I) * 2 / MOE_TILE_ROWB;
+    const bool big = big_tile(p, kModeW2, p.H);
+    const int64_t tiles = static_cast<int64_t>(max_m_tiles(p, big ? 256 : MOE_TILE_BM)) * (p.H / (big ? 256 : MOE_TILE_BN));
+    const int64_t nk_all = static_cast<int64_t>(p.I) * 2 / (big ? 64 : MOE_TILE_ROWB);
     int ks = 1;
     while (ks < 4 && tiles * ks < 8 * kCUs && nk_all / (ks + 1) >= 32) ++ks;
     return ks;
@@ -488,7 +498,7 @@ static hipError_t bf16_gemm(const GroupedProblem& p, GemmArgs g, const int32_t* 
         return launch_stream<4, MODE>(p, g, offsets, ws, stream);
     }
     const int n = MODE == kModeW13 ? 2 * p.I : p.H;
-    if (MODE == kModeW13 && m >= MOE_BIG_TILE_MIN_ROWS && n % 256 == 0)
+    if (big_tile(p, MODE, n))
         return launch_tile<256, 256, 2, 4, MODE>(p, g, offsets, ws, stream);
     if (n % MOE_TILE_BN == 0)
         return launch_tile<MOE_TILE_BM, MOE_TILE_BN, MOE_TILE_WM, MOE_TILE_WN, MODE>(p, g, offsets, ws, stream);

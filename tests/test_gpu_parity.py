@@ -44,6 +44,9 @@ SMALL = {
     # few w2 tiles and a long reduction: the down projection splits K in two
     # parts whose partial outputs the combine sums
     "w2_split_k": MC("w2_split_k", E=4, K=2, H=256, I=4096, T=257, seed=19, weight_seed=19),
+    # experts of >= 768 rows: 256 x 256 tiles in both GEMMs, ragged last
+    # tiles, and a K-split w2
+    "big_tiles": MC("big_tiles", E=2, K=1, H=256, I=2048, T=1600, seed=20, weight_seed=20),
 }
 
 
