@@ -112,6 +112,83 @@ __global__ __launch_bounds__(64) void align_scatter_kernel(const int32_t* __rest
     }
 }
 
+// Whole permutation in one block for small slot counts (decode batches):
+// 16 waves each own a contiguous run of slots; per-wave expert counts in LDS,
+// one scan gives the offsets and every wave's starting row per expert, then
+// each wave scatters its run in slot order (the same stable result as the
+// three-kernel path, in one launch instead of three).
+constexpr int kAlignSmallWaves = 16;
+constexpr int64_t kAlignSmallMax = 4096;
+
+__global__ __launch_bounds__(kAlignSmallWaves * kWave) void align_small_kernel(
+    const int32_t* __restrict__ ids, int64_t n, int E, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_slots, int32_t* __restrict__ slot_to_row) {
+    __shared__ int32_t cnt[kAlignSmallWaves][kAlignMaxExperts];  // counts, then cursors
+    __shared__ int32_t tot[1024];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), w = wave_index(tid);
+    const int chunk = static_cast<int>((n + kAlignSmallWaves - 1) / kAlignSmallWaves);
+    const int begin = w * chunk;
+    const int end = begin + chunk < n ? begin + chunk : static_cast<int>(n);
+    for (int e = lane; e < E; e += kWave) cnt[w][e] = 0;
+    __syncthreads();
+    for (int i = begin + lane; i < end; i += kWave) {
+        const int e = ids[i];
+        if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&cnt[w][e], 1);
+    }
+    __syncthreads();
+    // expert `tid`: its per-wave counts become running starts within the
+    // expert; tot[tid] = its total, scanned across experts below
+    int32_t run = 0;
+    if (tid < E) {
+        for (int v = 0; v < kAlignSmallWaves; ++v) {
+            const int32_t c = cnt[v][tid];
+            cnt[v][tid] = run;
+            run += c;
+        }
+    }
+    tot[tid] = tid < E ? run : 0;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int32_t v = tid >= off ? tot[tid - off] : 0;
+        __syncthreads();
+        tot[tid] += v;
+        __syncthreads();
+    }
+    const int32_t base = tot[tid] - run;  // exclusive prefix of expert tid
+    if (tid < E) {
+        offsets[tid] = base;
+        for (int v = 0; v < kAlignSmallWaves; ++v) cnt[v][tid] += base;
+    }
+    if (tid == 1023) offsets[E] = tot[1023];
+    __syncthreads();
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
+    for (int b0 = begin; b0 < end; b0 += kWave) {
+        const int i = b0 + lane;
+        int e = i < end ? ids[i] : -1;
+        const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(E);
+        if (!valid) e = kAlignMaxExperts;  // matches only other invalid lanes
+        uint64_t same = __ballot(valid);
+        same = valid ? same : ~same;
+#pragma unroll
+        for (int bit = 0; bit < 10; ++bit) {
+            const bool on = (e >> bit) & 1;
+            const uint64_t bal = __ballot(on);
+            same &= on ? bal : ~bal;
+        }
+        const int before = __popcll(same & lt_mask);
+        const int total = __popcll(same);
+        int32_t row = 0;
+        if (valid) row = cnt[w][e] + before;
+        // this wave's cursor row is private: a wave's LDS accesses complete in
+        // order, so the read above precedes the update below
+        if (valid) {
+            sorted_slots[row] = i;
+            slot_to_row[i] = row;
+            if (before == total - 1) cnt[w][e] = row + 1;
+        }
+    }
+}
+
 int64_t align_chunk(int64_t n) {
     // one wave per chunk, at most 256 chunks (keeps the scan matrix small)
     int64_t chunk = 1024;
@@ -127,6 +204,11 @@ size_t align_workspace_bytes(int64_t n, int E) {
 
 hipError_t launch_align(const int32_t* ids, int64_t n, int E, int32_t* offsets,
                         int32_t* sorted_slots, int32_t* slot_to_row, void* ws, hipStream_t stream) {
+    if (n <= kAlignSmallMax && E <= kAlignMaxExperts) {
+        align_small_kernel<<<1, kAlignSmallWaves * kWave, 0, stream>>>(ids, n, E, offsets, sorted_slots,
+                                                                        slot_to_row);
+        return hipGetLastError();
+    }
     const int64_t chunk = align_chunk(n);
     const int nchunks = static_cast<int>((n + chunk - 1) / chunk);
     int32_t* counts = static_cast<int32_t*>(ws);
