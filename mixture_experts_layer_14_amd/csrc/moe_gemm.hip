@@ -362,10 +362,13 @@ size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 }  // namespace
 
 
-// Prefill tile configuration: block tile BM x BN on WM x WN waves, GM m-tiles
-// per L2 group, ROWB bytes of every row per pipeline stage.  Measured on
-// MI355X: 8 waves (two per SIMD) beat 4; 256 x 256 tiles pay off for the
-// gate/up GEMM once experts hold several hundred rows.
+// Prefill tile configuration: block tile BM x BN on WM x WN waves, at most GM
+// m-tiles of an expert per L2 group, ROWB bytes of every row per pipeline
+// stage.  Measured on MI355X: 8 waves (two per SIMD) beat 4; 256 x 256 tiles
+// pay off in both GEMMs once experts average 256 rows: each weight tile is
+// then copied through L2 into LDS once per 256 rows instead of per 128 (the
+// global->LDS copy stream, not the MFMAs, limits these kernels), and the
+// MFMAs of a ragged last tile's empty row blocks are skipped.
 #ifndef MOE_TILE_BM
 #define MOE_TILE_BM 128
 #endif
@@ -385,7 +388,7 @@ size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 #define MOE_TILE_ROWB 128
 #endif
 #ifndef MOE_BIG_TILE_MIN_ROWS
-#define MOE_BIG_TILE_MIN_ROWS 768
+#define MOE_BIG_TILE_MIN_ROWS 256
 #endif
 // k-steps each streaming wave keeps in flight, and the largest average rows
 // per expert that still uses the streaming kernel.
