@@ -387,6 +387,12 @@ size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 #ifndef MOE_TILE_ROWB
 #define MOE_TILE_ROWB 128
 #endif
+#ifndef MOE_BIG_TILE_WN
+#define MOE_BIG_TILE_WN 4
+#endif
+#ifndef MOE_BIG_TILE_ROWB
+#define MOE_BIG_TILE_ROWB 64
+#endif
 #ifndef MOE_BIG_TILE_MIN_ROWS
 #define MOE_BIG_TILE_MIN_ROWS 256
 #endif
@@ -412,15 +418,18 @@ static bool big_tile(const GroupedProblem& p, int mode, int64_t n) {
            n % 256 == 0;
 }
 
+#ifndef MOE_W2_KSPLIT_MAX
+#define MOE_W2_KSPLIT_MAX 4
+#endif
 static int w2_ksplit(const GroupedProblem& p) {
     if (p.dtype != MOE_DTYPE_BF16 || rows_per_active_expert(p) <= MOE_STREAM_MAX_ROWS) return 1;
     if (p.H % MOE_TILE_BN != 0) return 1;
     constexpr int64_t kCUs = 256;
     const bool big = big_tile(p, kModeW2, p.H);
     const int64_t tiles = static_cast<int64_t>(max_m_tiles(p, big ? 256 : MOE_TILE_BM)) * (p.H / (big ? 256 : MOE_TILE_BN));
-    const int64_t nk_all = static_cast<int64_t>(p.I) * 2 / (big ? 64 : MOE_TILE_ROWB);
+    const int64_t nk_all = static_cast<int64_t>(p.I) * 2 / (big ? MOE_BIG_TILE_ROWB : MOE_TILE_ROWB);
     int ks = 1;
-    while (ks < 4 && tiles * ks < 8 * kCUs && nk_all / (ks + 1) >= 32) ++ks;
+    while (ks < MOE_W2_KSPLIT_MAX && tiles * ks < 8 * kCUs && nk_all / (ks + 1) >= 32) ++ks;
     return ks;
 }
 
@@ -463,7 +472,7 @@ static hipError_t launch_tile(const GroupedProblem& p, GemmArgs g, const int32_t
     g.n_tiles_n = MODE == kModeW13 ? (2 * p.I) / BN : p.H / BN;
     const int64_t total = static_cast<int64_t>(g.max_m_tiles) * g.n_tiles_n * (MODE == kModeW2 ? g.ksplit : 1);
     const int64_t blocks = 8 * ((total + 7) / 8);
-    tile_kernel<BM, BN, WM, WN, (BM + BN >= 512 ? 64 : MOE_TILE_ROWB), MODE><<<static_cast<unsigned>(blocks), WM * WN * kWave, 0, stream>>>(g);
+    tile_kernel<BM, BN, WM, WN, (BM + BN >= 512 ? MOE_BIG_TILE_ROWB : MOE_TILE_ROWB), MODE><<<static_cast<unsigned>(blocks), WM * WN * kWave, 0, stream>>>(g);
     return hipGetLastError();
 }
 
@@ -502,7 +511,7 @@ static hipError_t bf16_gemm(const GroupedProblem& p, GemmArgs g, const int32_t* 
     }
     const int n = MODE == kModeW13 ? 2 * p.I : p.H;
     if (big_tile(p, MODE, n))
-        return launch_tile<256, 256, 2, 4, MODE>(p, g, offsets, ws, stream);
+        return launch_tile<256, 256, 2, MOE_BIG_TILE_WN, MODE>(p, g, offsets, ws, stream);
     if (n % MOE_TILE_BN == 0)
         return launch_tile<MOE_TILE_BM, MOE_TILE_BN, MOE_TILE_WM, MOE_TILE_WN, MODE>(p, g, offsets, ws, stream);
     if (n % 128 == 0) return launch_tile<128, 128, 2, 2, MODE>(p, g, offsets, ws, stream);  // 64 x 64 per wave
