@@ -306,9 +306,35 @@ static double or_weight(const void *data, const float *scale, int dtype,
     }
 }
 
-static double or_silu(double z) { return z / (1.0 + exp(-z)); }
+/* Router gate logits ([SGL-DSV2] MoEGate: weight [E, H]; forward returns
+ * F.linear(hidden.float(), weight) for an fp32 gate and a bf16 GEMM with fp32
+ * output for a bf16 gate).  Both are the sum over h of x[t,h] * W[e,h] of the
+ * exactly decoded values, evaluated here in double:
+ *   out[t*E + e] = sum_h x[t,h] W[e,h]. */
+void or_router_logits(int64_t T, int64_t E, int64_t H, const void *hidden,
+                      int x_dtype, const void *gate, int g_dtype, double *out)
+{
+    for (int64_t t = 0; t < T; t++)
+        for (int64_t e = 0; e < E; e++) {
+            double acc = 0.0;
+            for (int64_t h = 0; h < H; h++) {
+                double x = x_dtype == OR_F32
+                               ? (double)((const float *)hidden)[t * H + h]
+                               : or_bf16_to_f64(((const uint16_t *)hidden)[t * H + h]);
+                double w = g_dtype == OR_F32
+                               ? (double)((const float *)gate)[e * H + h]
+                               : or_bf16_to_f64(((const uint16_t *)gate)[e * H + h]);
+                acc += x * w;
+            }
+            out[t * E + e] = acc;
+        }
+}
 
-/* One expert's gated MLP ([vLLM-layer] FusedMoE w13 = [gate; up] along the
+/* SiLU with a slope inside the sigmoid ([SGL-layer] FusedMoE gemm1_alpha;
+ * reading: silu_a(z) = z * sigmoid(a * z), a = 1 being plain SiLU). */
+static double or_silu_a(double z, double a) { return z / (1.0 + exp(-a * z)); }
+
+/* One expert's MLP ([vLLM-layer] FusedMoE w13 = [gate; up] along the
  * output dimension per _load_w13, w2 = down; activation "silu" with
  * is_act_and_mul; [SGL-DSV2] DeepseekV2MLP gate_up_proj -> SiluAndMul ->
  * down_proj):
@@ -316,21 +342,39 @@ static double or_silu(double z) { return z / (1.0 + exp(-z)); }
  *   act = silu(gu[0:I]) * gu[I:2I]
  *   y   = W2 act           (H values)
  * fp8 layers quantise act per group of 128 in fp32 before W2 (the
- * DeepseekV2MLP fp8 path quantises the SiLU-and-mul output with group 128). */
+ * DeepseekV2MLP fp8 path quantises the SiLU-and-mul output with group 128).
+ * Variants ([vLLM-layer] is_act_and_mul; [SGL-layer] is_gated, gemm1_alpha,
+ * gemm1_clamp_limit; [SGL-DSV2] DeepseekV2MLP swiglu_limit with
+ * silu_and_mul_clamp / clipped SwiGLU), read plainly:
+ *   non-gated: W13 is [I, H] and act = silu_a(W13 x);
+ *   gated with limit L > 0: g = min(g, L), u = min(max(u, -L), L), then
+ *   act = silu_a(g) * u;  silu_a as above. */
 static void or_expert_mlp(const or_layer *L, const void *w13, const float *s13,
                           const void *w2, const float *s2, const double *x,
                           double *gu, double *act, float *a32, uint8_t *aq,
                           float *as, double *y)
 {
     int64_t H = L->H, I = L->I;
-    for (int64_t n = 0; n < 2 * I; n++) {
+    int64_t N1 = L->gated ? 2 * I : I;
+    double L_ = L->clamp_limit;
+    for (int64_t n = 0; n < N1; n++) {
         double acc = 0.0;
         for (int64_t h = 0; h < H; h++)
             acc += x[h] * or_weight(w13, s13, L->w_dtype, H, n, h);
         gu[n] = acc;
     }
-    for (int64_t i = 0; i < I; i++)
-        act[i] = or_silu(gu[i]) * gu[I + i];
+    for (int64_t i = 0; i < I; i++) {
+        if (!L->gated) {
+            act[i] = or_silu_a(gu[i], L->act_alpha);
+            continue;
+        }
+        double g = gu[i], u = gu[I + i];
+        if (L_ > 0.0) {
+            g = g < L_ ? g : L_;
+            u = u < -L_ ? -L_ : (u > L_ ? L_ : u);
+        }
+        act[i] = or_silu_a(g, L->act_alpha) * u;
+    }
     if (L->act_fp8) {
         for (int64_t i = 0; i < I; i++)
             a32[i] = (float)act[i];
@@ -348,7 +392,7 @@ static void or_expert_mlp(const or_layer *L, const void *w13, const float *s13,
 
 /* Scratch of one worker. */
 typedef struct {
-    double *x, *gu, *act, *y;
+    double *x, *xw, *gu, *act, *y;
     float *x32, *a32, *xs, *as;
     uint8_t *xq, *aq;
 } or_scratch;
@@ -357,6 +401,7 @@ static int or_scratch_alloc(const or_layer *L, or_scratch *s)
 {
     int64_t H = L->H, I = L->I;
     s->x = malloc(sizeof(double) * H);
+    s->xw = malloc(sizeof(double) * H);
     s->gu = malloc(sizeof(double) * 2 * I);
     s->act = malloc(sizeof(double) * I);
     s->y = malloc(sizeof(double) * H);
@@ -366,13 +411,13 @@ static int or_scratch_alloc(const or_layer *L, or_scratch *s)
     s->as = malloc(sizeof(float) * (I / 128 + 1));
     s->xq = malloc(H);
     s->aq = malloc(I);
-    return (s->x && s->gu && s->act && s->y && s->x32 && s->a32 && s->xs &&
+    return (s->x && s->xw && s->gu && s->act && s->y && s->x32 && s->a32 && s->xs &&
             s->as && s->xq && s->aq) ? 0 : -1;
 }
 
 static void or_scratch_free(or_scratch *s)
 {
-    free(s->x); free(s->gu); free(s->act); free(s->y); free(s->x32);
+    free(s->x); free(s->xw); free(s->gu); free(s->act); free(s->y); free(s->x32);
     free(s->a32); free(s->xs); free(s->as); free(s->xq); free(s->aq);
 }
 
@@ -382,7 +427,10 @@ static void or_scratch_free(or_scratch *s)
  * shared expert is added with weight 1, never scaled by rsf ([SGL-DSV2]
  * DeepseekV2MoE: shared output plus routed output times
  * routed_scaling_factor).  fp8 layers use the group-128 quantised x for both
- * the routed and the shared experts (quantise once). */
+ * the routed and the shared experts (quantise once).
+ * With weight_on_input ([vLLM-layer] and [SGL-layer] FusedMoE
+ * apply_router_weight_on_input) the weight scales the expert's input instead:
+ *   out = sum_k MLP_{id_k}(w_k x_t)  +  MLP_shared(x_t). */
 static int or_token(const or_layer *L, int64_t t, or_scratch *s, double *out)
 {
     int64_t H = L->H;
@@ -408,13 +456,19 @@ static int or_token(const or_layer *L, int64_t t, or_scratch *s, double *out)
         out[h] = 0.0;
     for (int k = 0; k < L->K; k++) {
         int e = ids[k];
+        const double *xin = s->x;
         if (!L->w13[e] || !L->w2[e])
             return -2; /* caller did not supply this expert's weights */
+        if (L->weight_on_input) {
+            for (int64_t h = 0; h < H; h++)
+                s->xw[h] = w[k] * s->x[h];
+            xin = s->xw;
+        }
         or_expert_mlp(L, L->w13[e], L->w13_scale ? L->w13_scale[e] : NULL,
-                      L->w2[e], L->w2_scale ? L->w2_scale[e] : NULL, s->x,
+                      L->w2[e], L->w2_scale ? L->w2_scale[e] : NULL, xin,
                       s->gu, s->act, s->a32, s->aq, s->as, s->y);
         for (int64_t h = 0; h < H; h++)
-            out[h] += w[k] * s->y[h];
+            out[h] += (L->weight_on_input ? 1.0 : w[k]) * s->y[h];
     }
     if (L->shared_w13) {
         or_expert_mlp(L, L->shared_w13, L->shared_w13_scale, L->shared_w2,
@@ -462,6 +516,11 @@ int or_moe_forward_tokens(const or_layer *L, int64_t ntok,
     if (L->E < 1 || L->E > OR_MAX_EXPERTS || L->K < 1 || L->K > L->E)
         return -1;
     if (L->act_fp8 && (L->H % 128 || L->I % 128))
+        return -1;
+    /* variants outside the pages' combinations: a clamp needs the gated
+     * form, and the fp8 paths quantise x itself, so they take no input
+     * weighting */
+    if ((!L->gated && L->clamp_limit > 0.0) || (L->act_fp8 && L->weight_on_input))
         return -1;
     if (nthreads < 1)
         nthreads = 1;

@@ -35,6 +35,12 @@ typedef struct {
     const float *shared_w13_scale;
     const void *shared_w2;        /* [H, I] or NULL */
     const float *shared_w2_scale;
+    /* activation variants (defaults: gated = 1, act_alpha = 1, clamp_limit =
+     * 0, weight_on_input = 0 give the plain SiLU-and-mul layer) */
+    int gated;                    /* 1: w13 is [2I, H] gate;up; 0: [I, H]     */
+    double act_alpha;             /* silu_a(z) = z * sigmoid(act_alpha * z)   */
+    double clamp_limit;           /* > 0: gate <= L and |up| <= L (gated)     */
+    int weight_on_input;          /* 1: sum_k MLP(w_k x) instead of w_k MLP(x) */
 } or_layer;
 
 double or_bf16_to_f64(uint16_t v);
@@ -47,6 +53,8 @@ int or_route(int64_t T, int E, int K, const float *logits, const float *bias,
              int32_t *ids, double *weights);
 int or_permute(int64_t N, int E, const int32_t *ids, int32_t *offsets,
                int32_t *sorted_slots, int32_t *slot_to_row);
+void or_router_logits(int64_t T, int64_t E, int64_t H, const void *hidden,
+                      int x_dtype, const void *gate, int g_dtype, double *out);
 int or_moe_forward_tokens(const or_layer *L, int64_t ntok,
                           const int64_t *tokens, double *out, int nthreads);
 

@@ -54,6 +54,8 @@ class _Layer(ctypes.Structure):
         ("w2", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p),
         ("shared_w13", ctypes.c_void_p), ("shared_w13_scale", ctypes.c_void_p),
         ("shared_w2", ctypes.c_void_p), ("shared_w2_scale", ctypes.c_void_p),
+        ("gated", ctypes.c_int), ("act_alpha", ctypes.c_double),
+        ("clamp_limit", ctypes.c_double), ("weight_on_input", ctypes.c_int),
     ]
 
 
@@ -74,6 +76,10 @@ def _bind(path):
                            ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p]
     L.or_permute.restype = ctypes.c_int
     L.or_permute.argtypes = [ctypes.c_int64, ctypes.c_int] + [ctypes.c_void_p] * 4
+    L.or_router_logits.restype = None
+    L.or_router_logits.argtypes = [ctypes.c_int64] * 3 + [ctypes.c_void_p, ctypes.c_int,
+                                                          ctypes.c_void_p, ctypes.c_int,
+                                                          ctypes.c_void_p]
     L.or_moe_forward_tokens.restype = ctypes.c_int
     L.or_moe_forward_tokens.argtypes = [ctypes.POINTER(_Layer), ctypes.c_int64,
                                         ctypes.c_void_p, ctypes.c_void_p,
@@ -160,6 +166,21 @@ def permute(ids: np.ndarray, E: int, lib_=None):
     return offsets, sorted_slots, slot_to_row
 
 
+def router_logits(hidden: np.ndarray, x_dtype: int, gate: np.ndarray, g_dtype: int,
+                  lib_=None) -> np.ndarray:
+    """Router gate logits x W_g^T in float64 ([T, E]); hidden [T, H] and gate
+    [E, H] as float32 arrays (F32) or bf16 bit patterns (BF16)."""
+    hidden = np.ascontiguousarray(hidden)
+    gate = np.ascontiguousarray(gate)
+    T, H = hidden.shape
+    E = gate.shape[0]
+    assert gate.shape[1] == H
+    out = np.empty((T, E), np.float64)
+    (lib_ or lib()).or_router_logits(T, E, H, _ptr(hidden), x_dtype, _ptr(gate), g_dtype,
+                                     _ptr(out))
+    return out
+
+
 def _expert_ptrs(per_expert, E):
     """Array of E pointers from either one [E, ...] array or a dict e -> array."""
     arr = (ctypes.c_void_p * E)()
@@ -183,8 +204,10 @@ def moe_forward_tokens(layer: dict, tokens, nthreads: int = 1, lib_=None) -> np.
     ``layer`` keys: T E K H I, scoring, renormalize, n_group, topk_group,
     routed_scaling_factor, x_dtype, w_dtype, act_fp8, hidden, logits, bias,
     w13, w13_scale, w2, w2_scale, shared_w13, shared_w13_scale, shared_w2,
-    shared_w2_scale.  Weight entries are [E, ...] arrays or dicts e -> array
-    (only the experts the listed tokens use need to be present).
+    shared_w2_scale, and the activation variants gated (True), act_alpha
+    (1.0), clamp_limit (0.0: none), weight_on_input (False).  Weight entries
+    are [E, ...] arrays or dicts e -> array (only the experts the listed
+    tokens use need to be present).
     """
     E = int(layer["E"])
     keep = []
@@ -208,6 +231,10 @@ def moe_forward_tokens(layer: dict, tokens, nthreads: int = 1, lib_=None) -> np.
     st.x_dtype = int(layer["x_dtype"])
     st.w_dtype = int(layer["w_dtype"])
     st.act_fp8 = int(bool(layer.get("act_fp8", False)))
+    st.gated = int(bool(layer.get("gated", True)))
+    st.act_alpha = float(layer.get("act_alpha", 1.0))
+    st.clamp_limit = float(layer.get("clamp_limit", 0.0))
+    st.weight_on_input = int(bool(layer.get("weight_on_input", False)))
     st.hidden = _ptr(arr("hidden"))
     st.logits = _ptr(arr("logits", np.float32))
     st.bias = _ptr(arr("bias", np.float32))

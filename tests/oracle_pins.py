@@ -16,7 +16,12 @@ a brute force, a closed form, an invariant, or a library routine):
 * the layer -> the dense SwiGLU MLP (one expert, top-1) written with torch
   library routines, identical-experts and linearity invariants, token-order
   invariance, a brute-force combine of per-expert dense MLPs, the shared-
-  expert difference, and an fp8 layer rebuilt from torch's e4m3 encoder.
+  expert difference, and an fp8 layer rebuilt from torch's e4m3 encoder;
+* router gate logits -> torch's float64 matmul and one-hot gate rows;
+* activation variants -> closed forms of the clipped SwiGLU on single
+  values, an inactive clamp (bitwise no-op), torch's dense MLP with the
+  alpha slope, the clamp or the non-gated form, and for the routing weight
+  on the input a brute force plus the w^2 law of the bilinear regime.
 
 Sources: vLLM docs page "vllm.model_executor.layers.fused_moe.layer"
 (FusedMoE.select_experts; w13 = [w1 (gate); w3 (up)] per _load_w13); SGLang
@@ -434,10 +439,130 @@ def check_layer_fp8(lib_=None):
     _close(out, _forward(Lf, lib_=lib_), 0.1, "fp8 layer near the unquantised layer")
 
 
+# ---------------------------------------------------------------------------
+# router gate logits and activation variants
+# ---------------------------------------------------------------------------
+
+
+def check_router_logits(lib_=None):
+    """x W_g^T against torch's float64 matmul of the decoded values, and a
+    gate of one-hot rows, which must copy hidden columns exactly."""
+    g = torch.Generator().manual_seed(11)
+    T, E, H = 9, 12, 96
+    x = torch.randn(T, H, generator=g)
+    w = torch.randn(E, H, generator=g) * 0.05
+    for x_dtype, g_dtype in [(O.BF16, O.BF16), (O.BF16, O.F32), (O.F32, O.F32)]:
+        xa = _bf16_bits(x) if x_dtype == O.BF16 else x.numpy().astype(np.float32)
+        wa = _bf16_bits(w) if g_dtype == O.BF16 else w.numpy().astype(np.float32)
+        x64 = _bits_to_f64(xa) if x_dtype == O.BF16 else torch.from_numpy(xa).double()
+        w64 = _bits_to_f64(wa) if g_dtype == O.BF16 else torch.from_numpy(wa).double()
+        out = O.router_logits(xa, x_dtype, wa, g_dtype, lib_=lib_)
+        _close(out, (x64 @ w64.T).numpy(), 1e-13, "router logits vs torch matmul")
+    cols = np.random.default_rng(3).permutation(H)[:E]
+    onehot = np.zeros((E, H), np.float32)
+    onehot[np.arange(E), cols] = 1.0
+    xa = x.numpy().astype(np.float32)
+    out = O.router_logits(xa, O.F32, onehot, O.F32, lib_=lib_)
+    assert np.array_equal(out, xa[:, cols].astype(np.float64)), "one-hot gate rows must copy columns"
+
+
+def _one_unit_layer(g, u_scale, limit=0.0, alpha=1.0):
+    """E=1, K=1, H=1, I=1: gate = 2*g, up = 2*u_scale, down = 1, so the
+    output is the activation of one (gate, up) pair."""
+    return dict(T=1, E=1, K=1, H=1, I=1, x_dtype=O.F32, w_dtype=O.F32,
+                hidden=np.array([[2.0]], np.float32), logits=np.zeros((1, 1), np.float32),
+                w13=np.array([[[g], [u_scale]]], np.float32), w2=np.array([[[1.0]]], np.float32),
+                clamp_limit=limit, act_alpha=alpha)
+
+
+def check_layer_clamp_closed_form(lib_=None):
+    """Clipped SwiGLU on single values: gate 10 -> 7, up -8 -> -7 (limit 7);
+    gate -10 stays (only capped above), up 9 -> 7; alpha in the sigmoid."""
+    import math
+    cases = [((5.0, -4.0, 7.0, 1.0), 7.0 / (1.0 + math.exp(-7.0)) * -7.0),
+             ((-5.0, 4.5, 7.0, 1.0), -10.0 / (1.0 + math.exp(10.0)) * 7.0),
+             ((1.5, 2.0, 7.0, 1.0), 3.0 / (1.0 + math.exp(-3.0)) * 4.0),
+             ((5.0, -4.0, 7.0, 1.702), 7.0 / (1.0 + math.exp(-1.702 * 7.0)) * -7.0),
+             ((1.5, 2.0, 0.0, 1.702), 3.0 / (1.0 + math.exp(-1.702 * 3.0)) * 4.0)]
+    for (gs, us, lim, a), exp in cases:
+        out = _forward(_one_unit_layer(gs, us, lim, a), lib_=lib_)[0, 0]
+        assert abs(out - exp) <= 1e-14 * abs(exp), "clipped SwiGLU %r: %r != %r" % ((gs, us, lim, a), out, exp)
+
+
+def check_layer_activation_variants(lib_=None):
+    """A limit above every |gate| and |up| changes nothing (bitwise); alpha
+    and the non-gated form against torch's dense MLP for one expert."""
+    L, ref = make_layer(4, 2, 48, 64, 7, seed=12)
+    base = _forward(L, lib_=lib_)
+    assert np.array_equal(_forward(dict(L, clamp_limit=1e6), lib_=lib_), base), "inactive clamp changed the output"
+    assert np.array_equal(_forward(dict(L, act_alpha=1.0), lib_=lib_), base), "alpha = 1 changed the output"
+    L, ref = make_layer(1, 1, 64, 96, 5, seed=13, w_dtype=O.BF16, x_dtype=O.BF16)
+    I = 96
+    x, w13, w2 = ref["x"], ref["w13"][0], ref["w2"][0]
+    gate, up = x @ w13[:I].T, x @ w13[I:].T
+    exp = ((gate * torch.sigmoid(1.702 * gate)) * up) @ w2.T
+    _close(_forward(dict(L, act_alpha=1.702), lib_=lib_), exp.numpy(), 1e-12, "silu alpha, dense")
+    gc, uc = gate.clamp(max=0.3), up.clamp(-0.3, 0.3)
+    exp = (F.silu(gc) * uc) @ w2.T
+    _close(_forward(dict(L, clamp_limit=0.3), lib_=lib_), exp.numpy(), 1e-12, "clipped SwiGLU, dense")
+    # non-gated: w13 holds I rows only
+    Ln = dict(L, gated=False, w13=L["w13"][:, :I])
+    exp = F.silu(x @ w13[:I].T) @ w2.T
+    _close(_forward(Ln, lib_=lib_), exp.numpy(), 1e-12, "non-gated SiLU MLP, dense")
+
+
+def check_layer_weight_on_input(lib_=None):
+    """Routing weight on the input: top-1 with renormalisation is unchanged;
+    otherwise a brute force over per-expert dense MLPs of w_k x; and with
+    every gate deep in SiLU's linear range the MLP is bilinear, so scaling
+    the input by w scales the output by w^2."""
+    L, _ = make_layer(6, 1, 32, 48, 5, seed=14)
+    assert np.array_equal(_forward(dict(L, weight_on_input=True), lib_=lib_), _forward(L, lib_=lib_)), \
+        "top-1 renormalised weight 1 must not change the output"
+    L, ref = make_layer(6, 2, 40, 56, 8, seed=15, scoring=O.SIGMOID, n_group=2, topk_group=1,
+                        bias=True, rsf=2.5, shared=True)
+    out = _forward(dict(L, weight_on_input=True), lib_=lib_)
+    exp = np.zeros_like(out)
+    for t in range(L["T"]):
+        ids, w = brute_route(L["logits"][t], 2, bias=L["bias"], scoring=O.SIGMOID, n_group=2,
+                             topk_group=1, rsf=2.5)
+        for e, wk in zip(ids, w):
+            exp[t] += dense_swiglu(wk * ref["x"][t:t + 1], ref["w13"][e], ref["w2"][e]).numpy()[0]
+        exp[t] += dense_swiglu(ref["x"][t:t + 1], ref["sw13"], ref["sw2"]).numpy()[0]
+    _close(out, exp, 1e-12, "weight on input, brute force")
+    # bilinear regime: positive x and gate rows make every gate >= ~1e3 * w
+    g = torch.Generator().manual_seed(16)
+    E, K, H, I, T = 4, 2, 16, 8, 5
+    x = torch.rand(T, H, generator=g) + 1.0
+    w13 = torch.randn(E, 2 * I, H, generator=g)
+    w13[:, :I] = torch.rand(E, I, H, generator=g) * 200.0 + 100.0
+    w2 = torch.randn(E, H, I, generator=g)
+    Lb = dict(T=T, E=E, K=K, H=H, I=I, x_dtype=O.F32, w_dtype=O.F32, renormalize=True,
+              hidden=x.numpy().astype(np.float32),
+              logits=torch.randn(T, E, generator=g).numpy().astype(np.float32),
+              w13=w13.numpy().astype(np.float32), w2=w2.numpy().astype(np.float32))
+    per_w = _forward(Lb, lib_=lib_)
+    on_in = _forward(dict(Lb, weight_on_input=True), lib_=lib_)
+    exp_def = np.zeros_like(per_w)
+    exp_sq = np.zeros_like(per_w)
+    for t in range(T):
+        ids, w = brute_route(Lb["logits"][t], K)
+        for e, wk in zip(ids, w):
+            y = O.moe_forward_tokens(dict(Lb, E=1, K=1, logits=np.zeros((T, 1), np.float32),
+                                          w13=Lb["w13"][e:e + 1], w2=Lb["w2"][e:e + 1]), [t],
+                                     lib_=lib_)[0]
+            exp_def[t] += wk * y
+            exp_sq[t] += wk * wk * y
+    _close(per_w, exp_def, 1e-12, "bilinear regime, weight on output")
+    _close(on_in, exp_sq, 1e-12, "bilinear regime, weight on input scales by w^2")
+
+
 ALL_CHECKS = [
     check_bf16_decode, check_e4m3_decode, check_e4m3_encode, check_quant_rule,
     check_route_softmax_bruteforce, check_route_softmax_weights, check_route_ties,
     check_route_grouped_bruteforce, check_route_grouped_reductions, check_permute,
     check_layer_dense, check_layer_identical_experts, check_layer_bruteforce_combine,
     check_layer_linearity, check_layer_token_permutation, check_layer_shared, check_layer_fp8,
+    check_router_logits, check_layer_clamp_closed_form, check_layer_activation_variants,
+    check_layer_weight_on_input,
 ]

@@ -15,9 +15,22 @@ from oracle import oracle as O
 from tests import oracle_pins as P
 
 MUTANTS = {
-    "swap_gate_up": ("act[i] = or_silu(gu[i]) * gu[I + i];",
-                     "act[i] = or_silu(gu[I + i]) * gu[i];"),
-    "silu_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
+    "swap_gate_up": ("double g = gu[i], u = gu[I + i];", "double g = gu[I + i], u = gu[i];"),
+    "silu_sign": ("return z / (1.0 + exp(-a * z));", "return z / (1.0 + exp(a * z));"),
+    "alpha_ignored": ("return z / (1.0 + exp(-a * z));", "return z / (1.0 + exp(-z));"),
+    "clamp_up_one_side": ("u = u < -L_ ? -L_ : (u > L_ ? L_ : u);", "u = u > L_ ? L_ : u;"),
+    "clamp_gate_both_sides": ("g = g < L_ ? g : L_;", "g = g < -L_ ? -L_ : (g > L_ ? L_ : g);"),
+    "clamp_swapped": ("g = g < L_ ? g : L_;\n            u = u < -L_ ? -L_ : (u > L_ ? L_ : u);",
+                      "u = u < L_ ? u : L_;\n            g = g < -L_ ? -L_ : (g > L_ ? L_ : g);"),
+    "nongated_times_self": ("act[i] = or_silu_a(gu[i], L->act_alpha);",
+                            "act[i] = or_silu_a(gu[i], L->act_alpha) * gu[i];"),
+    "weight_on_input_and_output": ("out[h] += (L->weight_on_input ? 1.0 : w[k]) * s->y[h];",
+                                   "out[h] += w[k] * s->y[h];"),
+    "weight_on_input_ignored": ("s->xw[h] = w[k] * s->x[h];", "s->xw[h] = s->x[h];"),
+    "router_gate_transposed": ("(double)((const float *)gate)[e * H + h]",
+                               "(double)((const float *)gate)[h * E + e]"),
+    "router_dropped_term": ("for (int64_t h = 0; h < H; h++) {\n                double x = x_dtype",
+                            "for (int64_t h = 1; h < H; h++) {\n                double x = x_dtype"),
     "sigmoid_sign": ("score[e] = 1.0 / (1.0 + exp(-(double)l[e]));",
                      "score[e] = 1.0 / (1.0 + exp((double)l[e]));"),
     "no_renormalize": ("w[k] /= denom;", "w[k] /= 1.0;"),
@@ -32,9 +45,10 @@ MUTANTS = {
                              "int64_t r = offsets[ids[i]] + offsets[ids[i] + 1] - 1 - cursor[ids[i]]++;"),
     "shared_scaled_by_rsf": ("            out[h] += s->y[h];",
                              "            out[h] += L->routed_scaling_factor * s->y[h];"),
-    "combine_wrong_weight": ("out[h] += w[k] * s->y[h];", "out[h] += w[0] * s->y[h];"),
+    "combine_wrong_weight": ("(L->weight_on_input ? 1.0 : w[k]) * s->y[h];",
+                             "(L->weight_on_input ? 1.0 : w[0]) * s->y[h];"),
     "w13_transposed": ("acc += x[h] * or_weight(w13, s13, L->w_dtype, H, n, h);",
-                       "acc += x[h] * or_weight(w13, s13, L->w_dtype, 2 * I, h, n);"),
+                       "acc += x[h] * or_weight(w13, s13, L->w_dtype, N1, h, n);"),
     "w2_transposed": ("acc += act[i] * or_weight(w2, s2, L->w_dtype, I, h, i);",
                       "acc += act[i] * or_weight(w2, s2, L->w_dtype, H, i, h);"),
     "e4m3_exponent_bias": ("mag = ldexp(1.0 + m / 8.0, e - 7);", "mag = ldexp(1.0 + m / 8.0, e - 8);"),
