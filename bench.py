@@ -119,6 +119,41 @@ def time_layer(cfg, T, steps, warmup):
             "forward_ms_per_step": fwd_ms}
 
 
+def time_router(cfg, T, gate_dtype, steps, warmup):
+    """moe_router_gemm (the router gate GEMM ahead of moe_topk) alone, HIP
+    events on its stream; algorithmic bytes = hidden + gate + logits, FLOPs =
+    2 T E H; its roofline is the larger of the two times at the MI355X peaks."""
+    import torch
+
+    from mixture_experts_layer_14_amd import binding, synth
+    from mixture_experts_layer_14_amd.layer import params_for
+
+    x = synth.make_hidden(cfg, T, device="cuda")
+    g = synth.make_gate(cfg, gate_dtype, device="cuda")
+    p = params_for(cfg, T)
+    ws = torch.empty(max(binding.moe_workspace_size(p), 256), dtype=torch.uint8, device="cuda")
+    out = torch.empty(T, cfg.E, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        binding.moe_router_gemm(p, x, g, out, ws)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        binding.moe_router_gemm(p, x, g, out, ws)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    x_b = 4 if cfg.act_dtype == "f32" else 2
+    byts = T * cfg.H * x_b + cfg.E * cfg.H * (4 if gate_dtype == "f32" else 2) + T * cfg.E * 4
+    flops = 2.0 * T * cfg.E * cfg.H
+    t_roof = max(byts / (PEAK_HBM_GBS * 1e9), flops / (PEAK_BF16_TFLOPS * 1e12))
+    del x, g, ws, out
+    return {"workload": "%s router T=%d E=%d H=%d gate %s" % (cfg.name, T, cfg.E, cfg.H, gate_dtype),
+            "us": ms * 1e3, "GBps": byts / (ms * 1e-3) / 1e9,
+            "tflops": flops / (ms * 1e-3) / 1e12, "roofline_frac": t_roof / (ms * 1e-3),
+            "bound": "hbm" if byts / (PEAK_HBM_GBS * 1e9) >= flops / (PEAK_BF16_TFLOPS * 1e12) else "mfma"}
+
+
 def source_digest():
     """sha256 over the HIP sources: identifies the kernels a stored counter
     measurement belongs to."""
@@ -275,6 +310,13 @@ def main():
                                       "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
                                       "traffic": stored_traffic("%s_w13" % dcfg.name),
                                       "avg_kernel_ms": d["w13_ms"], "algorithmic_bytes": wb}
+    # the router gate GEMM (a separate entry point, not part of the step)
+    dsv3 = synth.CONFIGS["dsv3"]
+    line["router"] = [time_router(cfg, T, "bf16", 20, 3),
+                      time_router(synth.CONFIGS[args.decode_config], synth.CONFIGS[args.decode_config].T,
+                                  "bf16", 50, 3),
+                      time_router(dsv3, dsv3.T, "f32", 20, 3),
+                      time_router(dsv3, 64, "f32", 50, 3)]
     if not args.no_cpu and args.cpu_sample > 0:
         line["cpu_baseline"] = cpu_baseline(cfg, T, args.cpu_sample)
     print(json.dumps(line), flush=True)

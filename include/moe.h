@@ -116,6 +116,25 @@ const char *moe_status_string(int status);
 int moe_pack_weights(const void *src, void *dst, int64_t matrices, int64_t rows,
                      int64_t row_bytes, void *stream);
 
+/* Router gate logits, the step ahead of moe_topk: logits = hidden W_g^T.
+ * Passage: MoEGate (SGLang deepseek_v2 page): weight [n_routed_experts,
+ * hidden_size] in the model dtype or fp32; forward is F.linear of the fp32
+ * hidden for an fp32 gate, a bf16 GEMM with fp32 output for a bf16 gate.
+ *   hidden        [T, H] act dtype (bf16 or fp32).
+ *   gate_w        [E, H] row-major (not packed), gate_dtype MOE_DTYPE_BF16 or
+ *                 MOE_DTYPE_F32.
+ *   router_logits [T, E] fp32 out.  Accumulation in fp32; a bf16 hidden with
+ *                 an fp32 gate is computed as hidden (hi + lo) with the gate
+ *                 split into two bf16 parts (relative error of a product
+ *                 <= 2^-16), so the result carries fp32-level accuracy.
+ *   workspace     >= moe_workspace_size(p) bytes (partial logits of a split
+ *                 over H when there are few tokens; unused otherwise).
+ * Errors: MOE_ERR_INVALID (NULL), MOE_ERR_UNSUPPORTED (gate or act dtype),
+ * MOE_ERR_WORKSPACE. */
+int moe_router_gemm(const moe_params *p, const void *hidden, const void *gate_w,
+                    int32_t gate_dtype, float *router_logits, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
 /* Router: top-k expert selection and routing weights per token.
  * Passage: FusedMoE.select_experts (vLLM page), grouped top-k and
  * e_score_correction_bias (vLLM page; DeepseekV2MoE TopK arguments and

@@ -24,7 +24,7 @@ F32, BF16, FP8_E4M3 = 0, 1, 2
 ENTRY_POINTS = (
     "moe_workspace_size", "moe_status_string", "moe_pack_weights", "moe_topk",
     "moe_align_permute", "moe_quant_act_fp8", "moe_grouped_gemm_w13_act",
-    "moe_grouped_gemm_w2_combine", "moe_forward",
+    "moe_grouped_gemm_w2_combine", "moe_forward", "moe_router_gemm",
 )
 
 
@@ -78,6 +78,11 @@ def load(path: str = LIB_PATH):
     L.moe_grouped_gemm_w13_act.argtypes = [_P] + [_VP] * 11 + [ctypes.c_size_t, _VP]
     L.moe_grouped_gemm_w2_combine.argtypes = [_P] + [_VP] * 12 + [ctypes.c_size_t, _VP]
     L.moe_forward.argtypes = [_P] + [_VP] * 15 + [ctypes.c_size_t, _VP]
+    L.moe_router_gemm.argtypes = [_P, _VP, _VP, ctypes.c_int32, _VP, _VP, ctypes.c_size_t, _VP]
+    # every entry point taking pointers must declare them (a bare Python int
+    # would be passed as a 32-bit C int)
+    for name in ENTRY_POINTS[2:]:
+        assert getattr(L, name).argtypes, name
     for name in ENTRY_POINTS[2:]:
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -182,6 +187,18 @@ def moe_grouped_gemm_w2_combine(p, act, act_scale, w2, w2_scale, shared_w2, shar
         _ptr(shared_w2_scale), _ptr(expert_offsets), _ptr(sorted_slots), _ptr(slot_to_row),
         _ptr(topk_weights), _ptr(out), _ptr(workspace), _nbytes(workspace), _stream(stream))
     return _check("moe_grouped_gemm_w2_combine", st, raise_on_error)
+
+
+def moe_router_gemm(p, hidden, gate_w, router_logits, workspace, gate_dtype=None, stream=None,
+                    raise_on_error=True):
+    """Router gate logits hidden W_g^T (fp32) into ``router_logits`` [T, E];
+    the gate dtype follows the tensor (bfloat16 or float32) unless given."""
+    if gate_dtype is None:
+        gate_dtype = F32 if gate_w is not None and gate_w.dtype == torch.float32 else BF16
+    st = load().moe_router_gemm(ctypes.byref(p), _ptr(hidden), _ptr(gate_w), int(gate_dtype),
+                                _ptr(router_logits), _ptr(workspace), _nbytes(workspace),
+                                _stream(stream))
+    return _check("moe_router_gemm", st, raise_on_error)
 
 
 def moe_forward(p, hidden, router_logits, e_score_correction_bias, w13, w13_scale, w2, w2_scale,

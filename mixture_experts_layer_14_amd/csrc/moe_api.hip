@@ -105,6 +105,10 @@ ForwardLayout forward_layout(const moe_params* p) {
     size_t s = align_scratch(p);
     if (w13_scratch(p) > s) s = w13_scratch(p);
     if (w2_scratch(p) > s) s = w2_scratch(p);
+    // covers moe_router_gemm's partial logits too (a call of its own)
+    const size_t r = moe::router_workspace_bytes(p->num_tokens, p->num_experts, p->hidden_size,
+                                                 p->act_dtype);
+    if (off + s < r) s = r - off;
     L.total = off + s;
     return L;
 }
@@ -236,6 +240,23 @@ int moe_grouped_gemm_w2_combine(const moe_params* p, const void* act, const floa
                                              shared_w2_scale, expert_offsets, sorted_slots,
                                              slot_to_row, topk_weights, out, workspace,
                                              as_stream(stream)));
+}
+
+int moe_router_gemm(const moe_params* p, const void* hidden, const void* gate_w,
+                    int32_t gate_dtype, float* router_logits, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    int st = check_params(p);
+    if (st != MOE_OK) return st;
+    if (gate_dtype != MOE_DTYPE_F32 && gate_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (p->num_tokens == 0) return MOE_OK;  // empty batch: nothing to do
+    if (!hidden || !gate_w || !router_logits) return MOE_ERR_INVALID;
+    if (p->act_dtype != MOE_DTYPE_F32 && p->act_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+    const size_t need = moe::router_workspace_bytes(p->num_tokens, p->num_experts,
+                                                    p->hidden_size, p->act_dtype);
+    if (need && (!workspace || workspace_bytes < need)) return MOE_ERR_WORKSPACE;
+    return hip_status(moe::launch_router(hidden, p->act_dtype, gate_w, gate_dtype, p->num_tokens,
+                                         p->num_experts, p->hidden_size, router_logits, workspace,
+                                         as_stream(stream)));
 }
 
 int moe_forward(const moe_params* p, const void* hidden, const float* router_logits,

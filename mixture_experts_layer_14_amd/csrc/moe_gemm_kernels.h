@@ -18,7 +18,6 @@
 
 namespace moe {
 
-typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 enum { kModeW13 = 0, kModeW2 = 1 };
 

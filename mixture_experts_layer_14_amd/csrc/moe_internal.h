@@ -59,6 +59,12 @@ hipError_t launch_w2_combine(const GroupedProblem& p, const void* act, const flo
                              const float* topk_weights, void* out, void* ws,
                              hipStream_t stream);
 
+// Router gate logits (moe_router.hip); dtypes are MOE_DTYPE_* values.
+int router_parts(int64_t T, int E, int H);
+size_t router_workspace_bytes(int64_t T, int E, int H, int act_dtype);
+hipError_t launch_router(const void* hidden, int act_dtype, const void* gate, int gate_dtype,
+                         int64_t T, int E, int H, float* logits, void* ws, hipStream_t stream);
+
 hipError_t launch_quant_fp8(const void* hidden, int64_t T, int H, uint8_t* q, float* scale,
                             hipStream_t stream);
 

@@ -1,0 +1,236 @@
+// moe_router.hip -- router gate logits, logits[T, E] = hidden[T, H] W_g[E, H]^T
+// in fp32 (SGLang page "srt/models/deepseek_v2.py", class MoEGate: the gate
+// weight is [n_routed_experts, hidden_size] in the model dtype or in fp32;
+// forward returns F.linear(hidden.float(), weight) for an fp32 gate and a
+// bf16 GEMM with fp32 output for a bf16 gate).
+//
+// bf16 hidden: MFMA 32x32x16 bf16 tiles of 64 tokens x 64 experts, fp32
+// accumulation.  An fp32 gate is split on the fly into bf16 hi + lo parts
+// (hi = bf16(w), lo = bf16(w - hi), |w - hi - lo| <= 2^-16 |w|), two MFMAs per
+// step; each bf16 x bf16 product is exact in fp32, so the result keeps fp32
+// accuracy at bf16 MFMA rate.  Few tiles (decode) split H into parts whose
+// fp32 partial logits a second kernel sums in a fixed order.
+// fp32 hidden: one thread per logit, fp32 FMAs in order over H.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kRBM = 64, kRBN = 64, kRK = 64;  // tile: tokens x experts x k per step
+constexpr int kRThreads = 256;                  // 4 waves, 2 x 2, each 32 x 32
+
+// 16-byte slot s of LDS row r (128-byte rows): XOR swizzle so the 32 rows one
+// MFMA operand read touches spread over all banks
+__device__ __forceinline__ int rslot(int r, int s) { return s ^ (r & 7); }
+
+template <bool GATE_F32>
+__global__ __launch_bounds__(kRThreads) void router_gemm_kernel(
+    const uint16_t* __restrict__ x, const void* __restrict__ gate, int64_t T, int E, int H,
+    int parts, float* __restrict__ out) {
+    constexpr int NB = GATE_F32 ? 2 : 1;  // gate planes in LDS: hi (and lo)
+    constexpr int STAGE = (kRBM + NB * kRBN) * kRK * 2;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = wave_index(tid);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRBM;
+    const int e0 = blockIdx.y * kRBN;
+    const int part = blockIdx.z;
+    const int nk_all = H / kRK;
+    const int k_first = part * nk_all / parts;
+    const int nk = (part + 1) * nk_all / parts - k_first;
+
+    // loads of one k-step into registers: A 2 x 16 B, gate 2 x 16 B (bf16)
+    // or 4 x 16 B (fp32) per thread; rows past T or E repeat the last row
+    u32x4 ra[2], rb[GATE_F32 ? 4 : 2];
+    auto load = [&](int kit) {
+        const int64_t k0 = static_cast<int64_t>(k_first + kit) * kRK;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int idx = tid + j * kRThreads;
+            const int r = idx >> 3, s = idx & 7;
+            const int64_t t = t0 + r < T ? t0 + r : T - 1;
+            ra[j] = *reinterpret_cast<const u32x4*>(x + t * H + k0 + s * 8);
+        }
+        if constexpr (!GATE_F32) {
+            const uint16_t* g = static_cast<const uint16_t*>(gate);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int idx = tid + j * kRThreads;
+                const int r = idx >> 3, s = idx & 7;
+                const int64_t e = e0 + r < E ? e0 + r : E - 1;
+                rb[j] = *reinterpret_cast<const u32x4*>(g + e * H + k0 + s * 8);
+            }
+        } else {
+            const float* g = static_cast<const float*>(gate);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int idx = tid + j * kRThreads;  // 4 floats each: 16 per row
+                const int r = idx >> 4, c = (idx & 15) * 4;
+                const int64_t e = e0 + r < E ? e0 + r : E - 1;
+                rb[j] = *reinterpret_cast<const u32x4*>(g + e * H + k0 + c);
+            }
+        }
+    };
+    auto store = [&](int buf) {
+        uint8_t* sA = smem + buf * STAGE;
+        uint8_t* sB = sA + kRBM * kRK * 2;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int idx = tid + j * kRThreads;
+            const int r = idx >> 3, s = idx & 7;
+            *reinterpret_cast<u32x4*>(sA + r * 128 + rslot(r, s) * 16) = ra[j];
+        }
+        if constexpr (!GATE_F32) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int idx = tid + j * kRThreads;
+                const int r = idx >> 3, s = idx & 7;
+                *reinterpret_cast<u32x4*>(sB + r * 128 + rslot(r, s) * 16) = rb[j];
+            }
+        } else {
+            uint8_t* sL = sB + kRBN * kRK * 2;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int idx = tid + j * kRThreads;
+                const int r = idx >> 4, c = (idx & 15) * 4;
+                uint32_t hi[2], lo[2];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const float w0 = __uint_as_float(rb[j][2 * q]), w1 = __uint_as_float(rb[j][2 * q + 1]);
+                    const uint16_t h0 = f32_to_bf16_bits(w0), h1 = f32_to_bf16_bits(w1);
+                    const uint16_t l0 = f32_to_bf16_bits(w0 - bf16_bits_to_f32(h0));
+                    const uint16_t l1 = f32_to_bf16_bits(w1 - bf16_bits_to_f32(h1));
+                    hi[q] = h0 | (static_cast<uint32_t>(h1) << 16);
+                    lo[q] = l0 | (static_cast<uint32_t>(l1) << 16);
+                }
+                // 4 values = 8 bytes: half of 16-byte slot c / 8
+                const int off = r * 128 + rslot(r, c >> 3) * 16 + (c & 7) * 2;
+                *reinterpret_cast<uint2*>(sB + off) = make_uint2(hi[0], hi[1]);
+                *reinterpret_cast<uint2*>(sL + off) = make_uint2(lo[0], lo[1]);
+            }
+        }
+    };
+
+    f32x16 acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+    const int ar = wm * 32 + (lane & 31), br = wn * 32 + (lane & 31), kh = lane >> 5;
+
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int kit = 0; kit < nk; ++kit) {
+        const int buf = kit & 1;
+        if (kit + 1 < nk) load(kit + 1);
+        const uint8_t* sA = smem + buf * STAGE;
+        const uint8_t* sB = sA + kRBM * kRK * 2;
+#pragma unroll
+        for (int ks = 0; ks < kRK / 16; ++ks) {
+            const int s = ks * 2 + kh;
+            const u32x4 a = *reinterpret_cast<const u32x4*>(sA + ar * 128 + rslot(ar, s) * 16);
+            const u32x4 b = *reinterpret_cast<const u32x4*>(sB + br * 128 + rslot(br, s) * 16);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                          __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+            if constexpr (GATE_F32) {
+                const uint8_t* sL = sB + kRBN * kRK * 2;
+                const u32x4 bl = *reinterpret_cast<const u32x4*>(sL + br * 128 + rslot(br, s) * 16);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                              __builtin_bit_cast(bf16x8, bl), acc, 0, 0, 0);
+            }
+        }
+        __syncthreads();  // every wave is done with `buf` and with the other buffer
+        if (kit + 1 < nk) {
+            store(buf ^ 1);
+            __syncthreads();
+        }
+    }
+
+    // acc[v] holds token row 8*(v/4) + 4*(lane/32) + v%4, expert column lane%32
+    float* o = out + static_cast<int64_t>(part) * T * E;
+    const int e = e0 + wn * 32 + (lane & 31);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int64_t t = t0 + wm * 32 + 8 * (v / 4) + 4 * (lane >> 5) + (v % 4);
+        if (t < T && e < E) o[t * E + e] = acc[v];
+    }
+}
+
+// logits = sum of the parts' partial logits, in part order
+__global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restrict__ partial,
+                                                            int64_t n, int parts,
+                                                            float* __restrict__ out) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    float s = partial[i];
+    for (int p = 1; p < parts; ++p) s += partial[p * n + i];
+    out[i] = s;
+}
+
+// fp32 hidden: one thread per (token, expert), fp32 FMAs in h order
+template <bool GATE_F32>
+__global__ __launch_bounds__(256) void router_f32_kernel(const float* __restrict__ x,
+                                                         const void* __restrict__ gate, int64_t T,
+                                                         int E, int H, float* __restrict__ out) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= T * E) return;
+    const int64_t t = i / E;
+    const int e = static_cast<int>(i - t * E);
+    float s = 0.0f;
+    for (int h = 0; h < H; ++h) {
+        const float w = GATE_F32 ? static_cast<const float*>(gate)[static_cast<int64_t>(e) * H + h]
+                                 : bf16_bits_to_f32(static_cast<const uint16_t*>(gate)[static_cast<int64_t>(e) * H + h]);
+        s = fmaf(x[t * H + h], w, s);
+    }
+    out[i] = s;
+}
+
+}  // namespace
+
+// Parts of H for the MFMA path: enough blocks to cover the chip when there
+// are few tiles, at least two k-steps per part.
+int router_parts(int64_t T, int E, int H) {
+    const int64_t tiles = ((T + kRBM - 1) / kRBM) * ((E + kRBN - 1) / kRBN);
+    const int nk_all = H / kRK;
+    int parts = 1;
+    while (parts < 32 && tiles * parts < 512 && nk_all / (parts * 2) >= 2) parts *= 2;
+    return parts;
+}
+
+size_t router_workspace_bytes(int64_t T, int E, int H, int act_dtype) {
+    if (act_dtype != 1 /* bf16 */ || T <= 0) return 0;
+    const int parts = router_parts(T, E, H);
+    return parts > 1 ? static_cast<size_t>(parts) * T * E * sizeof(float) : 0;
+}
+
+hipError_t launch_router(const void* hidden, int act_dtype, const void* gate, int gate_dtype,
+                         int64_t T, int E, int H, float* logits, void* ws, hipStream_t stream) {
+    const bool gf32 = gate_dtype == 0;
+    if (act_dtype != 1) {  // fp32 hidden
+        const unsigned blocks = static_cast<unsigned>((T * E + 255) / 256);
+        if (gf32)
+            router_f32_kernel<true><<<blocks, 256, 0, stream>>>(static_cast<const float*>(hidden), gate, T, E, H, logits);
+        else
+            router_f32_kernel<false><<<blocks, 256, 0, stream>>>(static_cast<const float*>(hidden), gate, T, E, H, logits);
+        return hipGetLastError();
+    }
+    const int parts = router_parts(T, E, H);
+    float* dst = parts > 1 ? static_cast<float*>(ws) : logits;
+    const dim3 grid(static_cast<unsigned>((T + kRBM - 1) / kRBM), static_cast<unsigned>((E + kRBN - 1) / kRBN),
+                    static_cast<unsigned>(parts));
+    const uint16_t* x = static_cast<const uint16_t*>(hidden);
+    if (gf32)
+        router_gemm_kernel<true><<<grid, kRThreads, 0, stream>>>(x, gate, T, E, H, parts, dst);
+    else
+        router_gemm_kernel<false><<<grid, kRThreads, 0, stream>>>(x, gate, T, E, H, parts, dst);
+    if (parts > 1) {
+        const int64_t n = T * E;
+        router_reduce_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, stream>>>(dst, n, parts, logits);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -15,7 +15,11 @@ MoE block of the SGLang page "srt/models/deepseek_v2.py"):
   (scale = amax / 448, codes = e4m3(w / scale));
 * router logits ~ N(0, 1) in fp32, plus a per-expert skew
   b_e = -1.2 * ln(e + 1) for the Zipf-skewed many-expert layer;
-* e_score_correction_bias ~ N(0, 0.01) in fp32 for the sigmoid layers.
+* e_score_correction_bias ~ N(0, 0.01) in fp32 for the sigmoid layers;
+* router gate weights W_g [E, H] ~ N(0, 1/H) (standard deviation H^-1/2, so
+  the logits of N(0, 1) hidden rows are again about N(0, 1)), drawn in fp32
+  and kept in fp32 or rounded to bf16 (MoEGate of the DeepSeek page holds the
+  gate in the model dtype or, with router_fp32, in fp32).
 
 No near-ties: a row of router logits whose routing decision is within
 ``delta`` of a tie (consecutive gaps among the K+1 best selection keys, and for
@@ -35,7 +39,7 @@ import numpy as np
 import torch
 
 # Stream ids of the tensors; each tensor draws from its own seeded stream.
-_LOGITS, _HIDDEN, _W13, _W2, _BIAS, _SW13, _SW2 = range(7)
+_LOGITS, _HIDDEN, _W13, _W2, _BIAS, _SW13, _SW2, _GATE = range(8)
 
 
 @dataclass(frozen=True)
@@ -238,6 +242,12 @@ def make_weights(cfg: MoEConfig, device="cpu") -> dict:
         out["shared_w13_scale"] = None if sa is None else sa[0]
         out["shared_w2_scale"] = None if sb is None else sb[0]
     return out
+
+
+def make_gate(cfg: MoEConfig, dtype: str = "bf16", device="cpu") -> torch.Tensor:
+    """Router gate weights [E, H] ~ N(0, 1/H) in fp32 ("f32") or bf16."""
+    w = _draw_matrix(cfg.weight_seed, _GATE, 0, (cfg.E, cfg.H), cfg.H ** -0.5, "cpu")
+    return w.to(torch.float32 if dtype == "f32" else torch.bfloat16).contiguous().to(device)
 
 
 def make_inputs(cfg: MoEConfig, T: int | None = None, device="cpu", weight_device=None) -> dict:

@@ -120,3 +120,22 @@ def test_pack_weights_validation(args, status):
     L = B.load()
     src, dst, m, r, rb = args
     assert L.moe_pack_weights(src, dst, m, r, rb, None) == status
+
+
+def test_router_gemm_validation():
+    L = B.load()
+    f = L.moe_router_gemm
+    # a decode-sized router splits H over parts and needs the workspace
+    p = _p(num_tokens=64, num_experts=256, top_k=8, hidden_size=7168, intermediate_size=2048)
+    need = B.moe_workspace_size(p)
+    assert need > 0
+    assert f(ctypes.byref(p), None, FAKE, B.BF16, FAKE, FAKE, need, None) == B.MOE_ERR_INVALID
+    assert f(ctypes.byref(p), FAKE, None, B.BF16, FAKE, FAKE, need, None) == B.MOE_ERR_INVALID
+    assert f(ctypes.byref(p), FAKE, FAKE, B.BF16, None, FAKE, need, None) == B.MOE_ERR_INVALID
+    assert f(ctypes.byref(p), FAKE, FAKE, B.FP8_E4M3, FAKE, FAKE, need, None) == B.MOE_ERR_UNSUPPORTED
+    assert f(ctypes.byref(p), FAKE, FAKE, 9, FAKE, FAKE, need, None) == B.MOE_ERR_UNSUPPORTED
+    assert f(ctypes.byref(p), FAKE, FAKE, B.F32, FAKE, None, 0, None) == B.MOE_ERR_WORKSPACE
+    p0 = _p(num_tokens=0)
+    assert f(ctypes.byref(p0), FAKE, FAKE, B.BF16, FAKE, None, 0, None) == B.MOE_OK
+    bad = _p(top_k=9)
+    assert f(ctypes.byref(bad), FAKE, FAKE, B.BF16, FAKE, FAKE, 1 << 30, None) == B.MOE_ERR_INVALID
