@@ -92,6 +92,20 @@ typedef struct moe_params {
     int32_t num_shared_experts;  /* 0, or 1: a shared expert (same format as  */
                                  /* the routed ones) of intermediate size I   */
                                  /* added to every token with weight 1        */
+    /* Activation variants; all zero gives the plain SiLU-and-mul layer.
+     * Passages: FusedMoE is_act_and_mul and apply_router_weight_on_input
+     * (vLLM page), is_gated, gemm1_alpha and gemm1_clamp_limit (SGLang layer
+     * page), DeepseekV2MLP swiglu_limit with the clipped SwiGLU (SGLang
+     * deepseek_v2 page).  With silu_a(z) = z * sigmoid(a * z):              */
+    int32_t non_gated;           /* 0: w13 is [E, 2I, H] (gate; up) and       */
+                                 /*    act = silu_a(min(g, L)) * clamp(u, -L, L) */
+                                 /* 1: w13 is [E, I, H] and act = silu_a(h)   */
+                                 /*    (bf16/fp32 layers)                     */
+    float swiglu_alpha;          /* a; 0 means 1 (plain SiLU); >= 0          */
+    float swiglu_limit;          /* L; 0 means no clamp; >= 0, gated only     */
+    int32_t router_weight_on_input; /* 1: the routing weight scales the      */
+                                 /* expert input, out_t = sum_k MLP(w_k x_t) */
+                                 /* (+ shared MLP(x_t)); bf16/fp32 layers     */
 } moe_params;
 
 /* Bytes of device workspace that moe_forward needs for `p` (the decomposed
@@ -192,22 +206,29 @@ int moe_quant_act_fp8(const moe_params *p, const void *hidden, uint8_t *q,
  *   hidden       [T, H]: act dtype; for fp8 weights the e4m3 codes from
  *                moe_quant_act_fp8 with hidden_scale [T, H/128].
  *   w13          [E, 2I, H] packed by moe_pack_weights (+ w13_scale
- *                [E, 2I/128, H/128] row-major for fp8).
- *   shared_w13   [2I, H] packed (+ scale) when num_shared_experts == 1,
- *                else NULL.
+ *                [E, 2I/128, H/128] row-major for fp8); [E, I, H] with
+ *                non_gated.
+ *   shared_w13   [2I, H] ([I, H] non-gated) packed (+ scale) when
+ *                num_shared_experts == 1, else NULL.
  *   expert_offsets, sorted_slots: from moe_align_permute.
+ *   topk_weights [T, K] fp32 from moe_topk when router_weight_on_input
+ *                (the w13 output of routed row r is scaled by its slot's
+ *                weight before the activation, which equals scaling the
+ *                input); else ignored and may be NULL.
  *   act          [T*K + T*S, I] out (S = num_shared_experts): row r holds
- *                silu(g) * u for the token of sorted_slots[r] (rows
- *                T*K + t: token t through the shared expert).  bf16 for
- *                bf16 layers, fp32 for fp32 layers, e4m3 codes for fp8
- *                layers with act_scale [T*K + T*S, I/128] fp32 out.
+ *                silu(g) * u (or its variant, see moe_params) for the token
+ *                of sorted_slots[r] (rows T*K + t: token t through the shared
+ *                expert).  bf16 for bf16 layers, fp32 for fp32 layers, e4m3
+ *                codes for fp8 layers with act_scale [T*K + T*S, I/128] fp32
+ *                out.
  * Errors: MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE. */
 int moe_grouped_gemm_w13_act(const moe_params *p, const void *hidden,
                              const float *hidden_scale, const void *w13,
                              const float *w13_scale, const void *shared_w13,
                              const float *shared_w13_scale,
                              const int32_t *expert_offsets,
-                             const int32_t *sorted_slots, void *act,
+                             const int32_t *sorted_slots,
+                             const float *topk_weights, void *act,
                              float *act_scale, void *workspace,
                              size_t workspace_bytes, void *stream);
 
@@ -222,7 +243,9 @@ int moe_grouped_gemm_w13_act(const moe_params *p, const void *hidden,
  *   shared_w2  [H, I] packed (+ scale) or NULL.
  *   topk_weights [T, K] fp32 from moe_topk; slot_to_row [T*K].
  *   out        [T, H] out_dtype:  out_t = sum_k w_{t,k} y_{row(t,k)}
- *              (+ y_{T*K+t} of the shared expert).  The sum over k runs in a
+ *              (+ y_{T*K+t} of the shared expert); with
+ *              router_weight_on_input the rows are added unweighted (the
+ *              weight went into the w13 call).  The sum over k runs in a
  *              fixed order in fp32, so results are bitwise reproducible.
  * Errors: MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE. */
 int moe_grouped_gemm_w2_combine(const moe_params *p, const void *act,

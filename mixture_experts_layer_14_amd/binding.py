@@ -45,6 +45,10 @@ class MoeParams(ctypes.Structure):
         ("weight_dtype", ctypes.c_int32),
         ("out_dtype", ctypes.c_int32),
         ("num_shared_experts", ctypes.c_int32),
+        ("non_gated", ctypes.c_int32),
+        ("swiglu_alpha", ctypes.c_float),
+        ("swiglu_limit", ctypes.c_float),
+        ("router_weight_on_input", ctypes.c_int32),
     ]
 
 
@@ -75,7 +79,7 @@ def load(path: str = LIB_PATH):
     L.moe_topk.argtypes = [_P, _VP, _VP, _VP, _VP, _VP]
     L.moe_align_permute.argtypes = [_P, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]
     L.moe_quant_act_fp8.argtypes = [_P, _VP, _VP, _VP, _VP]
-    L.moe_grouped_gemm_w13_act.argtypes = [_P] + [_VP] * 11 + [ctypes.c_size_t, _VP]
+    L.moe_grouped_gemm_w13_act.argtypes = [_P] + [_VP] * 12 + [ctypes.c_size_t, _VP]
     L.moe_grouped_gemm_w2_combine.argtypes = [_P] + [_VP] * 12 + [ctypes.c_size_t, _VP]
     L.moe_forward.argtypes = [_P] + [_VP] * 15 + [ctypes.c_size_t, _VP]
     L.moe_router_gemm.argtypes = [_P, _VP, _VP, ctypes.c_int32, _VP, _VP, ctypes.c_size_t, _VP]
@@ -96,11 +100,14 @@ def status_string(status: int) -> str:
 def make_params(*, num_tokens, num_experts, top_k, hidden_size, intermediate_size,
                 scoring_func=SOFTMAX, renormalize=True, num_expert_group=0, topk_group=0,
                 routed_scaling_factor=1.0, act_dtype=BF16, weight_dtype=BF16, out_dtype=BF16,
-                num_shared_experts=0) -> MoeParams:
+                num_shared_experts=0, non_gated=False, swiglu_alpha=0.0, swiglu_limit=0.0,
+                router_weight_on_input=False) -> MoeParams:
     return MoeParams(int(num_tokens), int(num_experts), int(top_k), int(hidden_size),
                      int(intermediate_size), int(scoring_func), int(bool(renormalize)),
                      int(num_expert_group), int(topk_group), float(routed_scaling_factor),
-                     int(act_dtype), int(weight_dtype), int(out_dtype), int(num_shared_experts))
+                     int(act_dtype), int(weight_dtype), int(out_dtype), int(num_shared_experts),
+                     int(bool(non_gated)), float(swiglu_alpha), float(swiglu_limit),
+                     int(bool(router_weight_on_input)))
 
 
 def _ptr(t):
@@ -170,12 +177,13 @@ def moe_quant_act_fp8(p, hidden, q, scale, stream=None, raise_on_error=True):
 
 
 def moe_grouped_gemm_w13_act(p, hidden, hidden_scale, w13, w13_scale, shared_w13,
-                             shared_w13_scale, expert_offsets, sorted_slots, act, act_scale,
-                             workspace, stream=None, raise_on_error=True):
+                             shared_w13_scale, expert_offsets, sorted_slots, topk_weights, act,
+                             act_scale, workspace, stream=None, raise_on_error=True):
     st = load().moe_grouped_gemm_w13_act(
         ctypes.byref(p), _ptr(hidden), _ptr(hidden_scale), _ptr(w13), _ptr(w13_scale),
         _ptr(shared_w13), _ptr(shared_w13_scale), _ptr(expert_offsets), _ptr(sorted_slots),
-        _ptr(act), _ptr(act_scale), _ptr(workspace), _nbytes(workspace), _stream(stream))
+        _ptr(topk_weights), _ptr(act), _ptr(act_scale), _ptr(workspace), _nbytes(workspace),
+        _stream(stream))
     return _check("moe_grouped_gemm_w13_act", st, raise_on_error)
 
 

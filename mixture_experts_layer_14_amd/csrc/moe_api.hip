@@ -53,6 +53,13 @@ int check_params(const moe_params* p) {
     if (!ok) return MOE_ERR_UNSUPPORTED;
     const int mult = fp8_layer(p) ? 128 : 64;
     if (p->hidden_size % mult || p->intermediate_size % mult) return MOE_ERR_INVALID;
+    // activation variants: a clamp needs the gated form; the fp8 paths run
+    // the gated SiLU family only and quantise x itself (no input weighting)
+    if (p->non_gated != 0 && p->non_gated != 1) return MOE_ERR_INVALID;
+    if (p->router_weight_on_input != 0 && p->router_weight_on_input != 1) return MOE_ERR_INVALID;
+    if (!(p->swiglu_alpha >= 0.0f) || !(p->swiglu_limit >= 0.0f)) return MOE_ERR_INVALID;  // NaN too
+    if (p->non_gated && p->swiglu_limit > 0.0f) return MOE_ERR_INVALID;
+    if (fp8_layer(p) && (p->non_gated || p->router_weight_on_input)) return MOE_ERR_UNSUPPORTED;
     // rows and element offsets held in int32 on the device
     if (all_rows(p) >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
@@ -67,6 +74,10 @@ moe::GroupedProblem problem(const moe_params* p) {
     g.shared = p->num_shared_experts;
     g.H = p->hidden_size;
     g.I = p->intermediate_size;
+    g.gated = p->non_gated ? 0 : 1;
+    g.alpha = p->swiglu_alpha > 0.0f ? p->swiglu_alpha : 1.0f;
+    g.limit = p->swiglu_limit;
+    g.weight_in = p->router_weight_on_input;
     return g;
 }
 
@@ -205,20 +216,23 @@ int moe_quant_act_fp8(const moe_params* p, const void* hidden, uint8_t* q, float
 int moe_grouped_gemm_w13_act(const moe_params* p, const void* hidden, const float* hidden_scale,
                              const void* w13, const float* w13_scale, const void* shared_w13,
                              const float* shared_w13_scale, const int32_t* expert_offsets,
-                             const int32_t* sorted_slots, void* act, float* act_scale,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+                             const int32_t* sorted_slots, const float* topk_weights, void* act,
+                             float* act_scale, void* workspace, size_t workspace_bytes,
+                             void* stream) {
     int st = check_params(p);
     if (st != MOE_OK) return st;
     if (p->num_tokens == 0) return MOE_OK;  // empty batch: nothing to do
     if (!hidden || !w13 || !expert_offsets || !sorted_slots || !act) return MOE_ERR_INVALID;
     if (p->num_shared_experts && !shared_w13) return MOE_ERR_INVALID;
+    if (p->router_weight_on_input && !topk_weights) return MOE_ERR_INVALID;
     if (fp8_layer(p) && (!hidden_scale || !w13_scale || !act_scale ||
                          (p->num_shared_experts && !shared_w13_scale)))
         return MOE_ERR_INVALID;
     if (!workspace || workspace_bytes < w13_scratch(p)) return MOE_ERR_WORKSPACE;
     return hip_status(moe::launch_w13(problem(p), hidden, hidden_scale, w13, w13_scale, shared_w13,
-                                      shared_w13_scale, expert_offsets, sorted_slots, act,
-                                      act_scale, workspace, as_stream(stream)));
+                                      shared_w13_scale, expert_offsets, sorted_slots,
+                                      topk_weights, act, act_scale, workspace,
+                                      as_stream(stream)));
 }
 
 int moe_grouped_gemm_w2_combine(const moe_params* p, const void* act, const float* act_scale,
@@ -302,7 +316,8 @@ int moe_forward(const moe_params* p, const void* hidden, const float* router_log
     void* act = ws + L.act;
     float* act_scale = fp8_layer(p) ? reinterpret_cast<float*>(ws + L.act_scale) : nullptr;
     st = moe_grouped_gemm_w13_act(p, a1, a1_scale, w13, w13_scale, shared_w13, shared_w13_scale,
-                                  offsets, sorted, act, act_scale, scratch, scratch_bytes, stream);
+                                  offsets, sorted, wts, act, act_scale, scratch, scratch_bytes,
+                                  stream);
     if (st != MOE_OK) return st;
     return moe_grouped_gemm_w2_combine(p, act, act_scale, w2, w2_scale, shared_w2, shared_w2_scale,
                                        offsets, sorted, inv, wts, out, scratch, scratch_bytes,

@@ -69,8 +69,5 @@ __device__ __forceinline__ uint8_t f32_to_e4m3(float x) {
     return static_cast<uint8_t>(__builtin_amdgcn_cvt_pk_fp8_f32(x, x, 0, false) & 0xFF);
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) {
-    return g / (1.0f + __expf(-g)) * u;
-}
 
 }  // namespace moe

@@ -172,15 +172,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void grouped_gemm_kernel(GemmArgs g)
         const int c = tid + q * NT;
         b_on[q] = c < BN * kChunks;
         const int row = c / kChunks, c16 = c % kChunks;
-        int64_t wrow;
-        if (MODE == kModeW13) {
-            const int blk = row / 16, pair = blk / 2, up = blk % 2;
-            const int64_t col = static_cast<int64_t>(n_tile) * (BN / 2) + pair * 16 + row % 16;
-            wrow = up ? g.I + col : col;
-        } else {
-            wrow = static_cast<int64_t>(n_tile) * BN + row;
-        }
-        b_ptr[q] = Bexp + packed_offset(wrow, c16 * 16, eltK);
+        b_ptr[q] = Bexp + packed_offset(b_weight_row<MODE, BN, 16>(g, n_tile, row), c16 * 16, eltK);
     }
 
     f32x4 acc[TM][TN];
@@ -246,13 +238,22 @@ __global__ __launch_bounds__(WM* WN* kWave) void grouped_gemm_kernel(GemmArgs g)
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int p = 0; p < TN / 2; ++p) {
-                const int64_t col = static_cast<int64_t>(n_tile) * (BN / 2) + (wn * (TN / 2) + p) * 16 + ccol;
+            for (int q = 0; q < 4; ++q) {
+                const int64_t r = tl.row0 + wm * WTM + i * 16 + crow + q;
+                if (r >= tl.row1) continue;
+                const float w = g.weight_in ? in_weight(g, r) : 1.0f;
+                if (g.gated) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int64_t r = tl.row0 + wm * WTM + i * 16 + crow + q;
-                    if (r < tl.row1)
-                        Pol::store(g.C, r * g.I + col, silu_mul(acc[i][2 * p][q], acc[i][2 * p + 1][q]));
+                    for (int p = 0; p < TN / 2; ++p) {
+                        const int64_t col = static_cast<int64_t>(n_tile) * (BN / 2) + (wn * (TN / 2) + p) * 16 + ccol;
+                        Pol::store(g.C, r * g.I + col, glu_act(g, acc[i][2 * p][q] * w, acc[i][2 * p + 1][q] * w));
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) {
+                        const int64_t col = static_cast<int64_t>(n_tile) * BN + wn * WTN + j * 16 + ccol;
+                        Pol::store(g.C, r * g.I + col, silu_a(acc[i][j][q] * w, g.act_alpha));
+                    }
                 }
             }
     } else {
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void grouped_gemm_kernel(GemmArgs g)
             for (int q = 0; q < 4; ++q) {
                 const int64_t r = tl.row0 + wm * WTM + i * 16 + crow + q;
                 if (r >= tl.row1) continue;
-                const float w = r < g.routed_rows ? g.topk_weights[g.sorted_slots[r]] : 1.0f;
+                const float w = row_weight(g, r);
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     const int64_t col = static_cast<int64_t>(n_tile) * BN + wn * WTN + j * 16 + ccol;
@@ -459,7 +460,7 @@ template <class Pol, int BM, int BN, int WM, int WN, int MODE>
 static hipError_t launch_grouped(const GroupedProblem& p, GemmArgs g, const int32_t* offsets,
                                  void* ws, hipStream_t stream) {
     build_tiles(p, offsets, BM, g, ws, stream);
-    g.n_tiles_n = MODE == kModeW13 ? (2 * p.I) / BN : p.H / BN;
+    g.n_tiles_n = g.N / BN;
     const int64_t blocks = static_cast<int64_t>(g.max_m_tiles) * g.n_tiles_n;
     grouped_gemm_kernel<Pol, BM, BN, WM, WN, MODE><<<static_cast<unsigned>(blocks), WM * WN * kWave, 0, stream>>>(g);
     return hipGetLastError();
@@ -469,7 +470,7 @@ template <int BM, int BN, int WM, int WN, int MODE>
 static hipError_t launch_tile(const GroupedProblem& p, GemmArgs g, const int32_t* offsets, void* ws,
                               hipStream_t stream) {
     build_tiles(p, offsets, BM, g, ws, stream);
-    g.n_tiles_n = MODE == kModeW13 ? (2 * p.I) / BN : p.H / BN;
+    g.n_tiles_n = g.N / BN;
     const int64_t total = static_cast<int64_t>(g.max_m_tiles) * g.n_tiles_n * (MODE == kModeW2 ? g.ksplit : 1);
     const int64_t blocks = 8 * ((total + 7) / 8);
     tile_kernel<BM, BN, WM, WN, (BM + BN >= 512 ? MOE_BIG_TILE_ROWB : MOE_TILE_ROWB), MODE><<<static_cast<unsigned>(blocks), WM * WN * kWave, 0, stream>>>(g);
@@ -493,7 +494,7 @@ static hipError_t launch_stream(const GroupedProblem& p, GemmArgs g, const int32
                                 hipStream_t stream) {
     constexpr int NPW = MODE == kModeW13 ? MOE_STREAM_NPW13 : MOE_STREAM_NPW2;
     build_tiles(p, offsets, TM * 16, g, ws, stream);
-    const int groups = MODE == kModeW13 ? p.I / (NPW / 2 * 16) : p.H / (NPW * 16);
+    const int groups = g.N / (NPW * 16);
     const int64_t blocks = static_cast<int64_t>(g.max_m_tiles) * groups;
     stream_kernel<TM, NPW, MOE_STREAM_WAVES, MODE, MOE_STREAM_U>
         <<<static_cast<unsigned>(blocks), MOE_STREAM_WAVES * kWave, 0, stream>>>(g);
@@ -509,7 +510,7 @@ static hipError_t bf16_gemm(const GroupedProblem& p, GemmArgs g, const int32_t* 
         if (m <= 32) return launch_stream<2, MODE>(p, g, offsets, ws, stream);
         return launch_stream<4, MODE>(p, g, offsets, ws, stream);
     }
-    const int n = MODE == kModeW13 ? 2 * p.I : p.H;
+    const int n = g.N;
     if (big_tile(p, MODE, n))
         return launch_tile<256, 256, 2, MOE_BIG_TILE_WN, MODE>(p, g, offsets, ws, stream);
     if (n % MOE_TILE_BN == 0)
@@ -522,7 +523,7 @@ template <int BM, int BN, int WM, int WN, int MODE>
 static hipError_t launch_tile_fp8(const GroupedProblem& p, GemmArgs g, const int32_t* offsets,
                                   void* ws, hipStream_t stream) {
     build_tiles(p, offsets, BM, g, ws, stream);
-    g.n_tiles_n = MODE == kModeW13 ? (2 * p.I) / BN : p.H / BN;
+    g.n_tiles_n = g.N / BN;
     const int64_t total = static_cast<int64_t>(g.max_m_tiles) * g.n_tiles_n;
     const int64_t blocks = 8 * ((total + 7) / 8);
     tile_kernel_fp8<BM, BN, WM, WN, MODE><<<static_cast<unsigned>(blocks), WM * WN * kWave, 0, stream>>>(g);
@@ -540,10 +541,20 @@ static hipError_t fp8_gemm(const GroupedProblem& p, GemmArgs g, const int32_t* o
     }
 }
 
+// Activation variants into the kernel arguments (limit 0: no clamp).
+static void set_variants(const GroupedProblem& p, GemmArgs& g) {
+    g.gated = p.gated;
+    g.weight_in = p.weight_in;
+    g.act_alpha = p.alpha;
+    g.act_limit = p.limit > 0.0f ? p.limit : __builtin_huge_valf();
+}
+
 template <class Pol>
 static hipError_t w13_for(const GroupedProblem& p, GemmArgs g, const int32_t* offsets, void* ws,
                           hipStream_t stream) {
-    if (rows_per_active_expert(p) <= 16 && (2 * p.I) % 128 == 0)
+    if (g.N % 128 != 0)  // non-gated, I an odd multiple of 64
+        return launch_grouped<Pol, 64, 64, 2, 2, kModeW13>(p, g, offsets, ws, stream);
+    if (rows_per_active_expert(p) <= 16)
         return launch_grouped<Pol, 16, 128, 1, 4, kModeW13>(p, g, offsets, ws, stream);
     return launch_grouped<Pol, 128, 128, 2, 2, kModeW13>(p, g, offsets, ws, stream);
 }
@@ -559,9 +570,11 @@ static hipError_t w2_for(const GroupedProblem& p, GemmArgs g, const int32_t* off
 hipError_t launch_w13(const GroupedProblem& p, const void* hidden, const float* hidden_scale,
                       const void* w13, const float* w13_scale, const void* shared_w13,
                       const float* shared_w13_scale, const int32_t* offsets,
-                      const int32_t* sorted_slots, void* act, float* act_scale, void* ws,
-                      hipStream_t stream) {
+                      const int32_t* sorted_slots, const float* topk_weights, void* act,
+                      float* act_scale, void* ws, hipStream_t stream) {
     GemmArgs g{};
+    set_variants(p, g);
+    g.topk_weights = topk_weights;
     g.A_scale = hidden_scale;
     g.B_scale = w13_scale;
     g.B_shared_scale = shared_w13_scale;
@@ -575,7 +588,7 @@ hipError_t launch_w13(const GroupedProblem& p, const void* hidden, const float* 
     g.routed_rows = p.T * p.K;
     g.topk = p.K;
     g.Kd = p.H;
-    g.N = 2 * p.I;
+    g.N = p.gated ? 2 * p.I : p.I;
     g.I = p.I;
     g.E = p.E;
     if (p.dtype == MOE_DTYPE_BF16) return bf16_gemm<kModeW13>(p, g, offsets, ws, stream);
@@ -593,6 +606,7 @@ hipError_t launch_w2_combine(const GroupedProblem& p, const void* act, const flo
     const size_t tile_bytes = gemm_tile_workspace_bytes(p);
     void* y = static_cast<uint8_t*>(ws) + tile_bytes;
     GemmArgs g{};
+    set_variants(p, g);
     g.A = static_cast<const uint8_t*>(act);
     g.sorted_slots = sorted_slots;
     g.B = static_cast<const uint8_t*>(w2);

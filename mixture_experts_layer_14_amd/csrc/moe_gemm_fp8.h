@@ -250,7 +250,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
             float m = 0.0f;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                act[i][v] = silu_mul(acc[i][0][v], acc[i][1][v]);
+                act[i][v] = glu_act(g, acc[i][0][v], acc[i][1][v]);
                 m = fmaxf(m, fabsf(act[i][v]));
             }
             m = fmaxf(m, __shfl_xor(m, 32, kWave));

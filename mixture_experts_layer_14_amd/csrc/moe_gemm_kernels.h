@@ -48,6 +48,16 @@ struct GemmArgs {
     // w2 split over K: ksplit parts, part p writing y + p * part_stride
     int32_t ksplit;
     int64_t part_stride;
+    // activation variants of the w13 epilogue: gated (silu_a(g) * u with g
+    // capped at act_limit and u clamped to +-act_limit; +inf: no clamp) or
+    // silu_a(h) of a single projection, silu_a(z) = z * sigmoid(act_alpha z);
+    // weight_in: the w13 output of a routed row is scaled by its routing
+    // weight (= the weight applied to the expert input, the MLP being linear
+    // up to the activation) and the w2 epilogue then adds rows unweighted
+    int32_t gated;
+    int32_t weight_in;
+    float act_alpha;
+    float act_limit;
 };
 
 constexpr int kRowBytes = 128;               // bytes of one row per k-iteration
@@ -72,9 +82,24 @@ __device__ __forceinline__ int64_t packed_offset(int64_t row, int64_t byte, int6
     return (row >> 4) * (row_bytes << 4) + (byte >> 6) * 1024 + (row & 15) * 64 + (byte & 63);
 }
 
-// Routing weight of permuted row r for the w2 epilogue (shared rows: 1).
+// Routing weight of permuted row r for the w2 epilogue (shared rows, and
+// every row when the weight went into the expert input: 1).
 __device__ __forceinline__ float row_weight(const GemmArgs& g, int64_t r) {
+    return (!g.weight_in && r < g.routed_rows) ? g.topk_weights[g.sorted_slots[r]] : 1.0f;
+}
+
+// Routing weight of permuted row r on the input side (w13 with weight_in).
+__device__ __forceinline__ float in_weight(const GemmArgs& g, int64_t r) {
     return r < g.routed_rows ? g.topk_weights[g.sorted_slots[r]] : 1.0f;
+}
+
+// The w13 activations.  With act_alpha = 1 and act_limit = +inf glu_act is
+// bitwise silu(g) * u.
+__device__ __forceinline__ float silu_a(float z, float a) { return z / (1.0f + __expf(-a * z)); }
+__device__ __forceinline__ float glu_act(const GemmArgs& g, float gate, float up) {
+    gate = fminf(gate, g.act_limit);
+    up = fminf(fmaxf(up, -g.act_limit), g.act_limit);
+    return silu_a(gate, g.act_alpha) * up;
 }
 
 // Weight row of local B-tile row `row` for an n-tile of width BN.  w13 tiles
@@ -82,7 +107,7 @@ __device__ __forceinline__ float row_weight(const GemmArgs& g, int64_t r) {
 // tile of gate column c and the one of up column c land in the same lanes.
 template <int MODE, int BN, int BLK>
 __device__ __forceinline__ int64_t b_weight_row(const GemmArgs& g, int n_tile, int row) {
-    if (MODE == kModeW2) return static_cast<int64_t>(n_tile) * BN + row;
+    if (MODE == kModeW2 || !g.gated) return static_cast<int64_t>(n_tile) * BN + row;
     const int b = row / BLK, pair = b / 2, up = b % 2;
     const int64_t col = static_cast<int64_t>(n_tile) * (BN / 2) + pair * BLK + row % BLK;
     return up ? g.I + col : col;
@@ -198,7 +223,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
     constexpr int COPIES = ROWS / RPC / NW;        // copy instructions per wave per stage
     constexpr int KSTEPS = ROWB / 32;              // 16-k MFMA steps per k-iteration
     constexpr int LDS_MAX = 160 * 1024;
-    constexpr int LDS_STAGES = LDS_MAX - (MODE == kModeW2 ? BM * 4 : 0);
+    constexpr int LDS_STAGES = LDS_MAX - BM * 4;
     constexpr int STAGES = 4 * STAGE <= LDS_STAGES ? 4 : (3 * STAGE <= LDS_STAGES ? 3 : 2);
     static_assert(ROWB == 64 || ROWB == 128, "row slab of 64 or 128 bytes");
     static_assert(ROWS % (RPC * NW) == 0, "stage rows split evenly over the waves");
@@ -207,11 +232,12 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
     static_assert(MODE != kModeW13 || TN % 2 == 0, "w13 wave tile holds gate/up pairs");
     static_assert(KSTEPS % 2 == 0, "a stage ends on fragment buffer 1");
     static_assert(COPIES * (STAGES - 2) <= 63, "vmcnt immediate range");
-    static_assert(MODE != kModeW2 || NW * kWave >= BM, "one thread per row weight");
-    // one LDS object: the stage buffers, then (w2) the tile's routing
-    // weights.  A second __shared__ array would make the compiler wait for
-    // every copy in flight before each LDS read of the main loop.
-    constexpr int ROW_W_BYTES = MODE == kModeW2 ? BM * 4 : 0;
+    static_assert(NW * kWave >= BM, "one thread per row weight");
+    // one LDS object: the stage buffers, then the tile's routing weights
+    // (w2, or w13 with the weight on the input).  A second __shared__ array
+    // would make the compiler wait for every copy in flight before each LDS
+    // read of the main loop.
+    constexpr int ROW_W_BYTES = BM * 4;
     static_assert(STAGES * STAGE + ROW_W_BYTES <= LDS_MAX, "LDS budget");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE + ROW_W_BYTES];
 
@@ -285,14 +311,16 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
 
     const int lrow = lane % 32, khalf = lane / 32;
 
-    // w2: the tile's routing weights, loaded into a register now so that
-    // their dependent loads (slot, then weight) overlap the main loop; they
-    // reach LDS only after it, where no copy is left in flight to wait for
+    // the tile's routing weights (w2, or w13 with the weight on the input),
+    // loaded into a register now so that their dependent loads (slot, then
+    // weight) overlap the main loop; they reach LDS only after it, where no
+    // copy is left in flight to wait for
     float* row_w = reinterpret_cast<float*>(smem + STAGES * STAGE);
+    const bool use_w = MODE == kModeW2 || g.weight_in;
     float my_w = 1.0f;
-    if (MODE == kModeW2 && tid < BM) {
+    if (use_w && tid < BM) {
         const int64_t r = tl.row0 + tid;
-        if (r < tl.row1) my_w = row_weight(g, r);
+        if (r < tl.row1) my_w = MODE == kModeW2 ? row_weight(g, r) : in_weight(g, r);
     }
     // Operand fragments are double-buffered across k-steps, and across
     // stages too: the first k-step of stage it+1 is read from LDS while the
@@ -389,7 +417,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
     // no copy may still write LDS when the block ends
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
-    if (MODE == kModeW2) {
+    if (use_w) {
         if (tid < BM) row_w[tid] = my_w;
         __syncthreads();
     }
@@ -397,18 +425,40 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
     const int crow = (lane / 32) * 4;
     if (MODE == kModeW13) {
         uint16_t* act = static_cast<uint16_t*>(g.C);
+        if (g.gated) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+            for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int p = 0; p < TN / 2; ++p) {
-                const int64_t col = static_cast<int64_t>(n_tile) * (BN / 2) + (wn * (TN / 2) + p) * 32 + ccol;
+                for (int p = 0; p < TN / 2; ++p) {
+                    const int64_t col = static_cast<int64_t>(n_tile) * (BN / 2) + (wn * (TN / 2) + p) * 32 + ccol;
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int64_t r = tl.row0 + wm * WTM + i * 32 + 8 * (v / 4) + crow + (v % 4);
-                    if (r < tl.row1)
-                        act[r * g.I + col] = f32_to_bf16_bits(silu_mul(acc[i][2 * p][v], acc[i][2 * p + 1][v]));
+                    for (int v = 0; v < 16; ++v) {
+                        const int lr = wm * WTM + i * 32 + 8 * (v / 4) + crow + (v % 4);
+                        const int64_t r = tl.row0 + lr;
+                        if (r < tl.row1) {
+                            const float w = use_w ? row_w[lr] : 1.0f;
+                            act[r * g.I + col] =
+                                f32_to_bf16_bits(glu_act(g, acc[i][2 * p][v] * w, acc[i][2 * p + 1][v] * w));
+                        }
+                    }
                 }
-            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int64_t col = static_cast<int64_t>(n_tile) * BN + wn * WTN + j * 32 + ccol;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int lr = wm * WTM + i * 32 + 8 * (v / 4) + crow + (v % 4);
+                        const int64_t r = tl.row0 + lr;
+                        if (r < tl.row1) {
+                            const float w = use_w ? row_w[lr] : 1.0f;
+                            act[r * g.I + col] = f32_to_bf16_bits(silu_a(acc[i][j][v] * w, g.act_alpha));
+                        }
+                    }
+                }
+        }
     } else {
         uint16_t* y = static_cast<uint16_t*>(g.C) + kpart * g.part_stride;
 #pragma unroll
@@ -473,15 +523,19 @@ __global__ __launch_bounds__(WAVES * kWave) void stream_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < NPW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // w2: routing weights of the 4 rows per m-subtile this lane stores,
-    // loaded up front so the dependent loads overlap the k-loop
+    // routing weights of the 4 rows per m-subtile this lane stores (w2, or
+    // w13 with the weight on the input), loaded up front so the dependent
+    // loads overlap the k-loop
     float rw[TM][4];
+    const bool use_w = MODE == kModeW2 || g.weight_in;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int64_t r = tl.row0 + i * 16 + (lane / 16) * 4 + q;
-            rw[i][q] = (MODE == kModeW2 && wave == 0 && r < tl.row1) ? row_weight(g, r) : 1.0f;
+            rw[i][q] = (use_w && wave == 0 && r < tl.row1)
+                           ? (MODE == kModeW2 ? row_weight(g, r) : in_weight(g, r))
+                           : 1.0f;
         }
 
     const int ks = static_cast<int>(eltK / 64);
@@ -534,17 +588,33 @@ __global__ __launch_bounds__(WAVES * kWave) void stream_kernel(GemmArgs g) {
     const int crow = (lane / 16) * 4;
     if constexpr (MODE == kModeW13) {
         uint16_t* act = static_cast<uint16_t*>(g.C);
+        if (g.gated) {
 #pragma unroll
-        for (int p = 0; p < NPW / 2; ++p) {
-            const int64_t col = static_cast<int64_t>(n_grp) * (NPW / 2) * 16 + p * 16 + ccol;
+            for (int p = 0; p < NPW / 2; ++p) {
+                const int64_t col = static_cast<int64_t>(n_grp) * (NPW / 2) * 16 + p * 16 + ccol;
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
+                for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int64_t r = tl.row0 + i * 16 + crow + q;
-                    if (r < tl.row1)
-                        act[r * g.I + col] = f32_to_bf16_bits(silu_mul(acc[i][2 * p][q], acc[i][2 * p + 1][q]));
-                }
+                    for (int q = 0; q < 4; ++q) {
+                        const int64_t r = tl.row0 + i * 16 + crow + q;
+                        if (r < tl.row1)
+                            act[r * g.I + col] = f32_to_bf16_bits(
+                                glu_act(g, acc[i][2 * p][q] * rw[i][q], acc[i][2 * p + 1][q] * rw[i][q]));
+                    }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NPW; ++j) {
+                const int64_t col = static_cast<int64_t>(n_grp) * NPW * 16 + j * 16 + ccol;
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int64_t r = tl.row0 + i * 16 + crow + q;
+                        if (r < tl.row1)
+                            act[r * g.I + col] = f32_to_bf16_bits(silu_a(acc[i][j][q] * rw[i][q], g.act_alpha));
+                    }
+            }
         }
     } else {
         uint16_t* y = static_cast<uint16_t*>(g.C);

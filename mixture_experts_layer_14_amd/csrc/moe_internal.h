@@ -35,6 +35,13 @@ struct GroupedProblem {
     int E;                 // routed experts
     int shared;            // 0/1 shared expert (rows T*K .. T*K+T-1)
     int H, I;              // hidden, intermediate
+    // activation variants (moe_params): gated SiLU-and-mul (1) or SiLU of
+    // one projection (0); SiLU slope; clamp limit (0: none); routing weight
+    // applied to the expert input instead of its output
+    int gated = 1;
+    float alpha = 1.0f;
+    float limit = 0.0f;
+    int weight_in = 0;
 };
 
 // Scratch bytes of one grouped GEMM launch (tile table).
@@ -49,8 +56,8 @@ hipError_t launch_pack_weights(const void* src, void* dst, int64_t matrices, int
 hipError_t launch_w13(const GroupedProblem& p, const void* hidden, const float* hidden_scale,
                       const void* w13, const float* w13_scale, const void* shared_w13,
                       const float* shared_w13_scale, const int32_t* offsets,
-                      const int32_t* sorted_slots, void* act, float* act_scale, void* ws,
-                      hipStream_t stream);
+                      const int32_t* sorted_slots, const float* topk_weights, void* act,
+                      float* act_scale, void* ws, hipStream_t stream);
 
 hipError_t launch_w2_combine(const GroupedProblem& p, const void* act, const float* act_scale,
                              const void* w2, const float* w2_scale, const void* shared_w2,

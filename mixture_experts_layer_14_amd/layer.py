@@ -27,7 +27,9 @@ def params_for(cfg, T: int | None = None) -> B.MoeParams:
         scoring_func=B.SIGMOID if cfg.scoring == "sigmoid" else B.SOFTMAX,
         renormalize=cfg.renormalize, num_expert_group=cfg.n_group, topk_group=cfg.topk_group,
         routed_scaling_factor=cfg.rsf, act_dtype=_DT[cfg.act_dtype], weight_dtype=_DT[cfg.w_dtype],
-        out_dtype=_DT[cfg.act_dtype], num_shared_experts=cfg.shared)
+        out_dtype=_DT[cfg.act_dtype], num_shared_experts=cfg.shared, non_gated=cfg.non_gated,
+        swiglu_alpha=cfg.swiglu_alpha, swiglu_limit=cfg.swiglu_limit,
+        router_weight_on_input=cfg.weight_on_input)
 
 
 _PACKED = ("w13", "w2", "shared_w13", "shared_w2")
@@ -118,7 +120,7 @@ class Stages:
         B.moe_grouped_gemm_w13_act(self.p, self.xq if fp8 else hidden, self.xs, w["w13"],
                                    w.get("w13_scale"), w.get("shared_w13"),
                                    w.get("shared_w13_scale"), self.offsets, self.sorted,
-                                   self.act, self.act_scale, self.ws)
+                                   self.weights, self.act, self.act_scale, self.ws)
 
     def w2(self):
         w = self.layer.w

@@ -65,6 +65,11 @@ class MoEConfig:
     delta: float = 1e-3
     w_std: float = 0.02
     T_gen: int = 0                 # rows drawn (decode = first T rows); 0 -> T
+    # activation variants (defaults: the plain SiLU-and-mul layer)
+    non_gated: bool = False        # w13 [E, I, H], act = silu_a(x W1^T)
+    swiglu_alpha: float = 0.0      # slope a of silu_a(z) = z sigmoid(a z); 0 -> 1
+    swiglu_limit: float = 0.0      # clamp of gate (above) and up (both sides); 0 -> none
+    weight_on_input: bool = False  # routing weight scales the expert input
 
     @property
     def fp8(self) -> bool:
@@ -233,10 +238,11 @@ def make_weights(cfg: MoEConfig, device="cpu") -> dict:
     w2 [E, H, I]; fp8 layers also get the 128x128 block scales and, with a
     shared expert, shared_w13 [2I, H] / shared_w2 [H, I] in the same format."""
     out = {}
-    out["w13"], out["w13_scale"] = _store_weights(cfg, cfg.E, _W13, (2 * cfg.I, cfg.H), device)
+    n13 = cfg.I if cfg.non_gated else 2 * cfg.I
+    out["w13"], out["w13_scale"] = _store_weights(cfg, cfg.E, _W13, (n13, cfg.H), device)
     out["w2"], out["w2_scale"] = _store_weights(cfg, cfg.E, _W2, (cfg.H, cfg.I), device)
     if cfg.shared:
-        a, sa = _store_weights(cfg, 1, _SW13, (2 * cfg.I, cfg.H), device)
+        a, sa = _store_weights(cfg, 1, _SW13, (n13, cfg.H), device)
         b, sb = _store_weights(cfg, 1, _SW2, (cfg.H, cfg.I), device)
         out["shared_w13"], out["shared_w2"] = a[0], b[0]
         out["shared_w13_scale"] = None if sa is None else sa[0]

@@ -44,7 +44,10 @@ def oracle_layer(cfg, inp: dict, T: int, experts=None) -> dict:
              logits=to_host_bits(inp["router_logits"]),
              bias=to_host_bits(inp.get("e_score_correction_bias")),
              w13=per_expert("w13"), w2=per_expert("w2"),
-             w13_scale=per_expert("w13_scale"), w2_scale=per_expert("w2_scale"))
+             w13_scale=per_expert("w13_scale"), w2_scale=per_expert("w2_scale"),
+             gated=not cfg.non_gated,
+             act_alpha=cfg.swiglu_alpha if cfg.swiglu_alpha > 0 else 1.0,
+             clamp_limit=cfg.swiglu_limit, weight_on_input=cfg.weight_on_input)
     if cfg.shared:
         L["shared_w13"] = to_host_bits(inp["shared_w13"])
         L["shared_w2"] = to_host_bits(inp["shared_w2"])

@@ -55,6 +55,15 @@ FAKE = 0x1000  # never dereferenced: every call below fails validation first
     (dict(weight_dtype=B.F32), B.MOE_ERR_UNSUPPORTED),
     (dict(num_shared_experts=2), B.MOE_ERR_UNSUPPORTED),
     (dict(scoring_func=7), B.MOE_ERR_INVALID),
+    # activation variants
+    (dict(swiglu_alpha=-1.0), B.MOE_ERR_INVALID),
+    (dict(swiglu_alpha=float("nan")), B.MOE_ERR_INVALID),
+    (dict(swiglu_limit=-1.0), B.MOE_ERR_INVALID),
+    (dict(non_gated=True, swiglu_limit=7.0), B.MOE_ERR_INVALID),          # clamp needs the gate
+    (dict(weight_dtype=B.FP8_E4M3, hidden_size=128, intermediate_size=256, non_gated=True),
+     B.MOE_ERR_UNSUPPORTED),
+    (dict(weight_dtype=B.FP8_E4M3, hidden_size=128, intermediate_size=256,
+          router_weight_on_input=True), B.MOE_ERR_UNSUPPORTED),
 ])
 def test_invalid_params_rejected_on_host(kw, status):
     L = B.load()
@@ -71,7 +80,13 @@ def test_null_pointers_and_bias_with_softmax():
     assert L.moe_forward(ctypes.byref(p), *([None] * 15), 0, None) == B.MOE_ERR_INVALID
     shared = _p(num_shared_experts=1)
     assert L.moe_grouped_gemm_w13_act(ctypes.byref(shared), FAKE, None, FAKE, None, None, None,
-                                      FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == B.MOE_ERR_INVALID
+                                      FAKE, FAKE, None, FAKE, None, FAKE, 1 << 30,
+                                      None) == B.MOE_ERR_INVALID
+    # the routing weight on the input needs the weights in the w13 call
+    won = _p(router_weight_on_input=True)
+    assert L.moe_grouped_gemm_w13_act(ctypes.byref(won), FAKE, None, FAKE, None, None, None,
+                                      FAKE, FAKE, None, FAKE, None, FAKE, 1 << 30,
+                                      None) == B.MOE_ERR_INVALID
 
 
 def test_workspace_checked_before_launch():
@@ -139,3 +154,12 @@ def test_router_gemm_validation():
     assert f(ctypes.byref(p0), FAKE, FAKE, B.BF16, FAKE, None, 0, None) == B.MOE_OK
     bad = _p(top_k=9)
     assert f(ctypes.byref(bad), FAKE, FAKE, B.BF16, FAKE, FAKE, 1 << 30, None) == B.MOE_ERR_INVALID
+
+
+def test_variant_flags_must_be_zero_or_one():
+    L = B.load()
+    for field in ("non_gated", "router_weight_on_input"):
+        p = _p()
+        setattr(p, field, 2)
+        assert L.moe_topk(ctypes.byref(p), FAKE, None, FAKE, FAKE, None) == B.MOE_ERR_INVALID
+        assert B.moe_workspace_size(p) == 0

@@ -31,6 +31,10 @@ FP8_SMALL = {
                       weight_seed=22),
     "fp8_many_tiles": MC("fp8_many_tiles", E=4, K=2, H=384, I=512, T=333, w_dtype="fp8",
                          shared=1, seed=23, weight_seed=23),
+    # clipped SwiGLU with a SiLU slope (gate/up std ~0.45 at H=512)
+    "fp8_clipped_swiglu": MC("fp8_clipped_swiglu", E=8, K=2, H=512, I=384, T=77, w_dtype="fp8",
+                             shared=1, seed=24, weight_seed=24, swiglu_alpha=1.702,
+                             swiglu_limit=0.5),
 }
 
 

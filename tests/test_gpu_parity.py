@@ -47,6 +47,32 @@ SMALL = {
     # experts of >= 768 rows: 256 x 256 tiles in both GEMMs, ragged last
     # tiles, and a K-split w2
     "big_tiles": MC("big_tiles", E=2, K=1, H=256, I=2048, T=1600, seed=20, weight_seed=20),
+    # activation variants (gate/up values have std ~0.45 at H=512, so a
+    # limit of 0.5 clamps a good share of them); each on the tile path, the
+    # weight-streaming path (few rows) and the fp32 path
+    "clipped_swiglu": MC("clipped_swiglu", E=8, K=2, H=512, I=448, T=300, seed=21, weight_seed=21,
+                         swiglu_alpha=1.702, swiglu_limit=0.5, shared=1),
+    "clipped_swiglu_decode": MC("clipped_swiglu_decode", E=8, K=2, H=512, I=256, T=5, seed=22,
+                                weight_seed=22, swiglu_alpha=1.702, swiglu_limit=0.5),
+    "clipped_swiglu_f32": MC("clipped_swiglu_f32", E=6, K=3, H=192, I=320, T=97, act_dtype="f32",
+                             w_dtype="f32", seed=23, weight_seed=23, swiglu_alpha=1.702,
+                             swiglu_limit=0.3),
+    "weight_on_input": MC("weight_on_input", E=16, K=4, H=192, I=320, T=70, scoring="sigmoid",
+                          renormalize=False, correction_bias=True, shared=1, seed=24,
+                          weight_seed=24, delta=1e-4, weight_on_input=True),
+    "weight_on_input_tiles": MC("weight_on_input_tiles", E=8, K=2, H=512, I=448, T=300, seed=25,
+                                weight_seed=25, weight_on_input=True),
+    "weight_on_input_f32": MC("weight_on_input_f32", E=6, K=3, H=192, I=320, T=97,
+                              act_dtype="f32", w_dtype="f32", seed=26, weight_seed=26,
+                              renormalize=False, weight_on_input=True),
+    "non_gated": MC("non_gated", E=8, K=2, H=512, I=448, T=300, seed=27, weight_seed=27,
+                    non_gated=True, shared=1),
+    "non_gated_decode": MC("non_gated_decode", E=8, K=2, H=512, I=448, T=5, seed=28,
+                           weight_seed=28, non_gated=True),
+    "non_gated_f32": MC("non_gated_f32", E=6, K=3, H=192, I=320, T=97, act_dtype="f32",
+                        w_dtype="f32", seed=29, weight_seed=29, non_gated=True, swiglu_alpha=1.702),
+    "non_gated_big_tiles": MC("non_gated_big_tiles", E=2, K=1, H=256, I=2048, T=1600, seed=30,
+                              weight_seed=30, non_gated=True, weight_on_input=True),
 }
 
 
