@@ -154,6 +154,74 @@ def time_router(cfg, T, gate_dtype, steps, warmup):
             "bound": "hbm" if byts / (PEAK_HBM_GBS * 1e9) >= flops / (PEAK_BF16_TFLOPS * 1e12) else "mfma"}
 
 
+def shared_streams(cfg_name, Ts, iters=50, warmup=5):
+    """The shared expert as a slot of the grouped GEMMs (moe_forward with
+    num_shared_experts = 1) against the pages' alternative: the routed layer
+    and the shared MLP (a one-expert layer whose only weight is 1) on two
+    streams of default priority, joined and added.  Times per forward with
+    HIP events; also the difference of the two outputs."""
+    import dataclasses
+
+    import torch
+
+    from mixture_experts_layer_14_amd import synth
+    from mixture_experts_layer_14_amd.layer import FusedMoE, params_for
+
+    base = synth.CONFIGS[cfg_name]
+    full = synth.make_inputs(base, max(Ts), device="cuda")
+    res = []
+    for T in Ts:
+        cfg = base.with_T(T)
+        inp = dict(full, hidden=full["hidden"][:T].contiguous(),
+                   router_logits=full["router_logits"][:T].contiguous())
+        fused = FusedMoE(params_for(cfg, T), inp)
+        rcfg = dataclasses.replace(cfg, shared=0)
+        routed = FusedMoE(params_for(rcfg, T), {k: v for k, v in inp.items()
+                                               if not k.startswith("shared")})
+        scfg = dataclasses.replace(cfg, E=1, K=1, shared=0, scoring="softmax", n_group=0,
+                                   topk_group=0, rsf=1.0, correction_bias=False)
+        sw = {"w13": inp["shared_w13"][None], "w2": inp["shared_w2"][None],
+              "w13_scale": None if inp.get("shared_w13_scale") is None else inp["shared_w13_scale"][None],
+              "w2_scale": None if inp.get("shared_w2_scale") is None else inp["shared_w2_scale"][None]}
+        shared = FusedMoE(params_for(scfg, T), sw)
+        zero_logits = torch.zeros(T, 1, dtype=torch.float32, device="cuda")
+        x, lg, b = inp["hidden"], inp["router_logits"], inp.get("e_score_correction_bias")
+        out_f = torch.empty(T, cfg.H, dtype=torch.bfloat16, device="cuda")
+        out_r = torch.empty_like(out_f)
+        out_s = torch.empty_like(out_f)
+        main = torch.cuda.current_stream()
+        side = torch.cuda.Stream()  # default priority
+
+        def two_streams():
+            side.wait_stream(main)
+            routed.forward(x, lg, b, out=out_r)
+            with torch.cuda.stream(side):
+                shared.forward(x, zero_logits, None, out=out_s)
+            main.wait_stream(side)
+            out_r.add_(out_s)
+
+        def timed(fn):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(main)
+            for _ in range(iters):
+                fn()
+            e.record(main)
+            torch.cuda.synchronize()
+            return a.elapsed_time(e) / iters * 1e3
+
+        t_f = timed(lambda: fused.forward(x, lg, b, out=out_f))
+        t_2 = timed(two_streams)
+        diff = (out_r.float() - out_f.float()).abs().max().item() / max(out_f.float().abs().max().item(), 1e-30)
+        res.append({"T": T, "fused_slot_us": t_f, "two_streams_us": t_2, "rel_diff": diff})
+        print(json.dumps(res[-1]), flush=True)
+        del fused, routed, shared, inp
+        torch.cuda.empty_cache()
+    print(json.dumps({"shared_expert": cfg_name, "results": res}), flush=True)
+
+
 def source_digest():
     """sha256 over the HIP sources: identifies the kernels a stored counter
     measurement belongs to."""
@@ -244,6 +312,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--shared-streams", action="store_true",
+                    help="only compare the shared expert as a GEMM slot with a second stream")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build runs the whole expert set on a single "
@@ -259,6 +329,9 @@ def main():
         sys.exit(1)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.shared_streams:
+        shared_streams("dsv3_fp8", [1, 16, 64, 256, 8192])
         return
     binding.load()
     cfg = synth.CONFIGS[args.config]
