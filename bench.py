@@ -222,6 +222,147 @@ def shared_streams(cfg_name, Ts, iters=50, warmup=5):
     print(json.dumps({"shared_expert": cfg_name, "results": res}), flush=True)
 
 
+def measured_peaks():
+    """What this GPU reaches: the library's bf16 MFMA loop and HBM read
+    stream (moe_peak_mfma_bf16 / moe_peak_read), best of 3 timed runs."""
+    import torch
+
+    from mixture_experts_layer_14_amd import binding
+
+    blocks, iters = 1024, 20000
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    binding.moe_peak_mfma_bf16(100, blocks, sink)
+    best = None
+    for _ in range(3):
+        a.record()
+        binding.moe_peak_mfma_bf16(iters, blocks, sink)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        best = ms if best is None else min(best, ms)
+    mfma = blocks * 4 * iters * 8 * 32768.0 / (best * 1e-3) / 1e12
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    rblocks = 16384
+    rsink = torch.empty(rblocks * 256, dtype=torch.int32, device="cuda")
+    binding.moe_peak_read(buf, rblocks, rsink)
+    best = None
+    for _ in range(3):
+        a.record()
+        binding.moe_peak_read(buf, rblocks, rsink)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        best = ms if best is None else min(best, ms)
+    read = buf.numel() / (best * 1e-3) / 1e9
+    del buf, sink, rsink
+    torch.cuda.empty_cache()
+    return {"bf16_mfma_tflops": mfma, "hbm_read_GBps": read,
+            "spec": {"bf16_mfma_tflops": PEAK_BF16_TFLOPS, "hbm_GBps": PEAK_HBM_GBS}}
+
+
+def cpu_sample(cfg, inp, tokens):
+    """The oracle as it stands on `tokens` of the workload (only the experts
+    they use are copied to the host), and its routing + permutation over all
+    T tokens; host threads (<= 16)."""
+    from mixture_experts_layer_14_amd import synth
+    from oracle import oracle as O
+
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    threads = max(1, min(threads, 16))
+    bits = synth.tensor_bits
+    logits = bits(inp["router_logits"])
+    bias = bits(inp.get("e_score_correction_bias"))
+    scoring = O.SIGMOID if cfg.scoring == "sigmoid" else O.SOFTMAX
+    t0 = time.perf_counter()
+    ids, _ = O.route(logits, cfg.K, bias=bias, scoring=scoring, renormalize=cfg.renormalize,
+                     n_group=cfg.n_group, topk_group=cfg.topk_group,
+                     routed_scaling_factor=cfg.rsf)
+    O.permute(ids, cfg.E)
+    t_route = time.perf_counter() - t0
+    tok = list(range(min(tokens, cfg.T)))
+    used = sorted(set(int(e) for e in ids[tok].reshape(-1)))
+
+    def per_expert(key):
+        t = inp.get(key)
+        return None if t is None else {e: bits(t[e]) for e in used}
+
+    L = dict(T=cfg.T, E=cfg.E, K=cfg.K, H=cfg.H, I=cfg.I, scoring=scoring,
+             renormalize=cfg.renormalize, n_group=cfg.n_group, topk_group=cfg.topk_group,
+             routed_scaling_factor=cfg.rsf, x_dtype=O.F32 if cfg.act_dtype == "f32" else O.BF16,
+             w_dtype={"f32": O.F32, "bf16": O.BF16, "fp8": O.E4M3}[cfg.w_dtype], act_fp8=cfg.fp8,
+             hidden=bits(inp["hidden"]), logits=logits, bias=bias,
+             w13=per_expert("w13"), w2=per_expert("w2"), w13_scale=per_expert("w13_scale"),
+             w2_scale=per_expert("w2_scale"))
+    if cfg.shared:
+        for k in ("shared_w13", "shared_w2", "shared_w13_scale", "shared_w2_scale"):
+            L[k] = bits(inp.get(k))
+    t0 = time.perf_counter()
+    O.moe_forward_tokens(L, tok, nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": len(tok) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d tokens, full layer in float64, %.2f s; routing + permutation of "
+                      "all %d tokens %.3f s" % (len(tok), cfg.T, dt, cfg.T, t_route)}
+
+
+# (config, CPU sample tokens): the five configurations at their sizes
+PER_CONFIG = [("tiny", 64), ("mixtral_decode", 8), ("mixtral", 8), ("qwen", 32),
+              ("dsv3_decode", 4), ("dsv3", 4), ("dsv3_fp8", 4)]
+
+
+def per_config(steps, warmup, peaks, with_cpu):
+    """Every configuration through moe_forward: tokens/s, TFLOP/s, GB/s of
+    algorithmic bytes, their fractions of the published and the measured
+    peaks, and the attainable-roofline fraction max(F/P, B/BW) / t."""
+    import torch
+
+    from mixture_experts_layer_14_amd import synth
+    from mixture_experts_layer_14_amd.layer import FusedMoE, Stages, params_for
+
+    rows = []
+    for name, sample in PER_CONFIG:
+        cfg = synth.CONFIGS[name]
+        T = cfg.T
+        inp = synth.make_inputs(cfg, T, device="cuda")
+        layer = FusedMoE(params_for(cfg, T), inp)
+        x, lg, b = inp["hidden"], inp["router_logits"], inp.get("e_score_correction_bias")
+        out = torch.empty(T, cfg.H, dtype=torch.float32 if cfg.act_dtype == "f32" else torch.bfloat16,
+                          device="cuda")
+        n = steps if T >= 1024 else max(steps, 50)
+        for _ in range(warmup):
+            layer.forward(x, lg, b, out=out)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            layer.forward(x, lg, b, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / n * 1e-3
+        st = Stages(layer, T)
+        st.topk(lg, b)
+        st.align()
+        active = int((st.offsets[1:] - st.offsets[:-1] > 0).sum().item())
+        flops = cfg.flops()
+        byts = algorithmic_bytes(cfg, T, active)
+        peak = {"bf16": PEAK_BF16_TFLOPS, "fp8": PEAK_FP8_TFLOPS, "f32": PEAK_F32_TFLOPS}[cfg.w_dtype]
+        t_f, t_b = flops / (peak * 1e12), byts / (PEAK_HBM_GBS * 1e9)
+        row = {"config": name, "T": T, "dtype": cfg.w_dtype, "ms": t * 1e3, "tokens_per_s": T / t,
+               "tflops": flops / t / 1e12, "GBps": byts / t / 1e9, "active_experts": active,
+               "mfma_frac": flops / t / 1e12 / peak, "hbm_frac": byts / t / 1e9 / PEAK_HBM_GBS,
+               "bound": "mfma" if t_f >= t_b else "hbm", "roofline_frac": max(t_f, t_b) / t}
+        if peaks and cfg.w_dtype == "bf16":
+            m_f = flops / (peaks["bf16_mfma_tflops"] * 1e12)
+            m_b = byts / (peaks["hbm_read_GBps"] * 1e9)
+            row["roofline_frac_measured_peaks"] = max(m_f, m_b) / t
+        if with_cpu:
+            row["cpu_baseline"] = cpu_sample(cfg, inp, sample)
+        rows.append(row)
+        print("config %s: %.3f ms" % (name, t * 1e3), file=sys.stderr, flush=True)
+        del layer, st, inp, out
+        torch.cuda.empty_cache()
+    return rows
+
+
 def source_digest():
     """sha256 over the HIP sources: identifies the kernels a stored counter
     measurement belongs to."""
@@ -312,6 +453,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration table and the measured peaks")
     ap.add_argument("--shared-streams", action="store_true",
                     help="only compare the shared expert as a GEMM slot with a second stream")
     args = ap.parse_args()
@@ -392,6 +535,10 @@ def main():
                       time_router(dsv3, 64, "f32", 50, 3)]
     if not args.no_cpu and args.cpu_sample > 0:
         line["cpu_baseline"] = cpu_baseline(cfg, T, args.cpu_sample)
+    if not args.no_configs:
+        peaks = measured_peaks()
+        line["measured_peaks"] = peaks
+        line["configs"] = per_config(10, 3, peaks, not args.no_cpu)
     print(json.dumps(line), flush=True)
 
 

@@ -278,6 +278,20 @@ int moe_forward(const moe_params *p, const void *hidden,
                 void *out, int32_t *topk_ids_out, float *topk_weights_out,
                 void *workspace, size_t workspace_bytes, void *stream);
 
+/* Measurement helpers (not steps of the method): what this GPU reaches, to
+ * print beside the published peaks.  The caller times the launch.
+ *   moe_peak_mfma_bf16: `blocks` blocks of 256 threads; every wave runs
+ *     `iters` rounds of 8 independent 32x32x16 bf16 MFMAs (32768 FLOP each),
+ *     i.e. blocks * 4 * iters * 8 * 32768 FLOP.  sink: blocks * 256 floats.
+ *   moe_peak_read: `blocks` blocks of 256 threads read `bytes` (multiple of
+ *     16, buffer 16-byte aligned) once with 16-byte loads, each block a
+ *     contiguous share.  sink: blocks * 256 uint32.
+ * Errors: MOE_ERR_INVALID for non-positive counts, NULL or misaligned
+ * buffers; MOE_ERR_HIP. */
+int moe_peak_mfma_bf16(int64_t iters, int32_t blocks, float *sink, void *stream);
+int moe_peak_read(const void *buf, int64_t bytes, int32_t blocks, uint32_t *sink,
+                  void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,6 +25,7 @@ ENTRY_POINTS = (
     "moe_workspace_size", "moe_status_string", "moe_pack_weights", "moe_topk",
     "moe_align_permute", "moe_quant_act_fp8", "moe_grouped_gemm_w13_act",
     "moe_grouped_gemm_w2_combine", "moe_forward", "moe_router_gemm",
+    "moe_peak_mfma_bf16", "moe_peak_read",
 )
 
 
@@ -83,6 +84,8 @@ def load(path: str = LIB_PATH):
     L.moe_grouped_gemm_w2_combine.argtypes = [_P] + [_VP] * 12 + [ctypes.c_size_t, _VP]
     L.moe_forward.argtypes = [_P] + [_VP] * 15 + [ctypes.c_size_t, _VP]
     L.moe_router_gemm.argtypes = [_P, _VP, _VP, ctypes.c_int32, _VP, _VP, ctypes.c_size_t, _VP]
+    L.moe_peak_mfma_bf16.argtypes = [ctypes.c_int64, ctypes.c_int32, _VP, _VP]
+    L.moe_peak_read.argtypes = [_VP, ctypes.c_int64, ctypes.c_int32, _VP, _VP]
     # every entry point taking pointers must declare them (a bare Python int
     # would be passed as a 32-bit C int)
     for name in ENTRY_POINTS[2:]:
@@ -219,6 +222,16 @@ def moe_forward(p, hidden, router_logits, e_score_correction_bias, w13, w13_scal
         _ptr(topk_ids_out), _ptr(topk_weights_out), _ptr(workspace), _nbytes(workspace),
         _stream(stream))
     return _check("moe_forward", st, raise_on_error)
+
+
+def moe_peak_mfma_bf16(iters, blocks, sink, stream=None, raise_on_error=True):
+    st = load().moe_peak_mfma_bf16(int(iters), int(blocks), _ptr(sink), _stream(stream))
+    return _check("moe_peak_mfma_bf16", st, raise_on_error)
+
+
+def moe_peak_read(buf, blocks, sink, stream=None, raise_on_error=True):
+    st = load().moe_peak_read(_ptr(buf), _nbytes(buf), int(blocks), _ptr(sink), _stream(stream))
+    return _check("moe_peak_read", st, raise_on_error)
 
 
 def _nbytes(t):

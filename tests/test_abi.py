@@ -163,3 +163,13 @@ def test_variant_flags_must_be_zero_or_one():
         setattr(p, field, 2)
         assert L.moe_topk(ctypes.byref(p), FAKE, None, FAKE, FAKE, None) == B.MOE_ERR_INVALID
         assert B.moe_workspace_size(p) == 0
+
+
+def test_peak_helpers_validate_on_host():
+    L = B.load()
+    assert L.moe_peak_mfma_bf16(0, 4, FAKE, None) == B.MOE_ERR_INVALID
+    assert L.moe_peak_mfma_bf16(10, 0, FAKE, None) == B.MOE_ERR_INVALID
+    assert L.moe_peak_mfma_bf16(10, 4, None, None) == B.MOE_ERR_INVALID
+    assert L.moe_peak_read(FAKE, 15, 4, FAKE, None) == B.MOE_ERR_INVALID   # not a multiple of 16
+    assert L.moe_peak_read(FAKE + 4, 64, 4, FAKE, None) == B.MOE_ERR_INVALID  # misaligned
+    assert L.moe_peak_read(None, 64, 4, FAKE, None) == B.MOE_ERR_INVALID
