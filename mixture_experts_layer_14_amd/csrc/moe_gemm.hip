@@ -36,9 +36,12 @@ namespace moe {
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets,
                                                            int E, int32_t shared_rows,
                                                            int32_t shared_base, int BM, int gm_max,
-                                                           Tile* __restrict__ tiles,
-                                                           int32_t* __restrict__ num_tiles) {
+                                                           int tail_rows, Tile* __restrict__ tiles,
+                                                           int32_t* __restrict__ num_tiles,
+                                                           GroupUnit* __restrict__ units,
+                                                           int32_t* __restrict__ num_units) {
     __shared__ int32_t scan[1024];
+    __shared__ int32_t uscan[1024];
     const int g = threadIdx.x;  // group: expert g, or the shared expert at g == E
     int32_t r0 = 0, r1 = 0;
     if (g < E) {
@@ -49,31 +52,50 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
         r0 = shared_base;
         r1 = shared_base + shared_rows;
     }
-    const int32_t nt = (r1 - r0 + BM - 1) / BM;
+    // main m-tiles of BM rows (the last one possibly ragged), unless a
+    // remainder of at most tail_rows rows goes to a tail tile
+    const int32_t rem = (r1 - r0) % BM;
+    const int32_t tail = rem > 0 && rem <= tail_rows ? 1 : 0;
+    const int32_t nmain = (r1 - r0) / BM + (rem > 0 && !tail ? 1 : 0);
+    const int32_t nt = nmain + tail;
     scan[g] = nt;
+    uscan[g] = 2 * nmain + tail;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
         const int32_t v = g >= off ? scan[g - off] : 0;
+        const int32_t u = g >= off ? uscan[g - off] : 0;
         __syncthreads();
         scan[g] += v;
+        uscan[g] += u;
         __syncthreads();
     }
     const int32_t start = scan[g] - nt;
+    const int32_t ustart = uscan[g] - (2 * nmain + tail);
     // an expert's m-tiles form groups of at most gm_max, balanced in size; a
-    // group's tiles sweep the n-tiles together so they share each weight tile
-    const int32_t ngroups = (nt + gm_max - 1) / gm_max;
-    int32_t c = 0;
-    for (int32_t j = 0; j < nt; ++j) {
-        while (j >= (c + 1) * nt / ngroups) ++c;
-        const int32_t first = c * nt / ngroups, last = (c + 1) * nt / ngroups;
-        Tile t;
-        t.expert = g;
-        t.row0 = r0 + j * BM;
-        t.row1 = r0 + (j + 1) * BM < r1 ? r0 + (j + 1) * BM : r1;
-        t.group = (start + first) * 256 + (last - first);
-        tiles[start + j] = t;
+    // group's tiles sweep the n-tiles together so they share each weight
+    // tile; the tail tile joins the expert's last group
+    const int32_t ngroups = nt == 0 ? 0 : (nmain == 0 ? 1 : (nmain + gm_max - 1) / gm_max);
+    for (int32_t c = 0; c < ngroups; ++c) {
+        const int32_t first = c * nmain / ngroups, last = (c + 1) * nmain / ngroups;
+        const int32_t has_tail = c == ngroups - 1 ? tail : 0;
+        const int32_t cnt = last - first;
+        for (int32_t j = first; j < last + has_tail; ++j) {
+            Tile t;
+            t.expert = g;
+            t.row0 = r0 + j * BM;
+            t.row1 = r0 + (j + 1) * BM < r1 ? r0 + (j + 1) * BM : r1;
+            t.group = (start + first) * 256 + cnt;
+            tiles[start + j] = t;
+        }
+        if (units) {
+            const GroupUnit d{start + first, cnt, has_tail, ustart + 2 * first};
+            for (int32_t u = 0; u < 2 * cnt + has_tail; ++u) units[ustart + 2 * first + u] = d;
+        }
     }
-    if (g == 1023) *num_tiles = scan[1023];
+    if (g == 1023) {
+        *num_tiles = scan[1023];
+        if (units) *num_units = uscan[1023];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -394,6 +416,11 @@ size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 #ifndef MOE_BIG_TILE_ROWB
 #define MOE_BIG_TILE_ROWB 64
 #endif
+// Remainders of at most this many rows (0: none) run as 128 x 512 tail
+// tiles in the 256 x 256 schedule.
+#ifndef MOE_TAIL_ROWS
+#define MOE_TAIL_ROWS 128
+#endif
 #ifndef MOE_BIG_TILE_MIN_ROWS
 #define MOE_BIG_TILE_MIN_ROWS 256
 #endif
@@ -434,8 +461,16 @@ static int w2_ksplit(const GroupedProblem& p) {
     return ks;
 }
 
+// Workspace of a grouped GEMM launch: the tile and unit counts, the tile
+// table (m-tiles of at least 16 rows) and the unit table of a schedule with
+// tail tiles (two units per 256-row m-tile at most).
+static size_t tile_table_bytes(const GroupedProblem& p) {
+    return align_up(sizeof(Tile) * static_cast<size_t>(max_m_tiles(p, 16)));
+}
+
 size_t gemm_tile_workspace_bytes(const GroupedProblem& p) {
-    return align_up(256) + align_up(sizeof(Tile) * static_cast<size_t>(max_m_tiles(p, 16)));
+    return align_up(256) + tile_table_bytes(p) +
+           align_up(sizeof(GroupUnit) * 2 * static_cast<size_t>(max_m_tiles(p, 256)));
 }
 
 size_t w2_rows_workspace_bytes(const GroupedProblem& p) {
@@ -443,15 +478,24 @@ size_t w2_rows_workspace_bytes(const GroupedProblem& p) {
     return align_up(static_cast<size_t>(w2_ksplit(p)) * total_rows(p) * p.H * elt);
 }
 
+// Tile table of BM-row m-tiles; with tail_rows > 0 (BM = 256 only) an
+// expert's remainder of at most tail_rows rows becomes a tail tile and the
+// unit table is written too.
 static void build_tiles(const GroupedProblem& p, const int32_t* offsets, int BM, GemmArgs& g,
-                        void* ws, hipStream_t stream) {
+                        void* ws, hipStream_t stream, int tail_rows = 0) {
     int32_t* num_tiles = static_cast<int32_t*>(ws);
+    int32_t* num_units = num_tiles + 1;
     Tile* tiles = reinterpret_cast<Tile*>(static_cast<uint8_t*>(ws) + 256);
+    GroupUnit* units = tail_rows > 0 ? reinterpret_cast<GroupUnit*>(static_cast<uint8_t*>(ws) + 256 +
+                                                                    tile_table_bytes(p))
+                                     : nullptr;
     build_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, p.E, p.shared ? static_cast<int32_t>(p.T) : 0,
-                                               static_cast<int32_t>(p.T * p.K), BM, MOE_TILE_GM, tiles,
-                                               num_tiles);
+                                               static_cast<int32_t>(p.T * p.K), BM, MOE_TILE_GM,
+                                               tail_rows, tiles, num_tiles, units, num_units);
     g.tiles = tiles;
     g.num_tiles = num_tiles;
+    g.units = units;
+    g.num_units = num_units;
     g.max_m_tiles = max_m_tiles(p, BM);
 }
 
@@ -474,6 +518,20 @@ static hipError_t launch_tile(const GroupedProblem& p, GemmArgs g, const int32_t
     const int64_t total = static_cast<int64_t>(g.max_m_tiles) * g.n_tiles_n * (MODE == kModeW2 ? g.ksplit : 1);
     const int64_t blocks = 8 * ((total + 7) / 8);
     tile_kernel<BM, BN, WM, WN, (BM + BN >= 512 ? MOE_BIG_TILE_ROWB : MOE_TILE_ROWB), MODE><<<static_cast<unsigned>(blocks), WM * WN * kWave, 0, stream>>>(g);
+    return hipGetLastError();
+}
+
+// 256 x 256 tiles with 128 x 512 tail tiles (n_tiles_n even: N % 512 == 0)
+template <int MODE>
+static hipError_t launch_tile_tail(const GroupedProblem& p, GemmArgs g, const int32_t* offsets, void* ws,
+                                   hipStream_t stream) {
+    build_tiles(p, offsets, 256, g, ws, stream, MOE_TAIL_ROWS);
+    g.n_tiles_n = g.N / 256;
+    const int nparts = MODE == kModeW2 ? g.ksplit : 1;
+    // units <= 2 per m-tile: every position of the schedule has a block
+    const int64_t total = 2 * static_cast<int64_t>(g.max_m_tiles) * (g.n_tiles_n * nparts / 2);
+    const int64_t blocks = 8 * ((total + 7) / 8);
+    tile_kernel_tail<MODE><<<static_cast<unsigned>(blocks), 8 * kWave, 0, stream>>>(g);
     return hipGetLastError();
 }
 
@@ -511,8 +569,11 @@ static hipError_t bf16_gemm(const GroupedProblem& p, GemmArgs g, const int32_t* 
         return launch_stream<4, MODE>(p, g, offsets, ws, stream);
     }
     const int n = g.N;
-    if (big_tile(p, MODE, n))
+    if (big_tile(p, MODE, n)) {
+        if (MOE_TAIL_ROWS > 0 && n % 512 == 0 && MOE_BIG_TILE_WN == 4 && MOE_BIG_TILE_ROWB == 64)
+            return launch_tile_tail<MODE>(p, g, offsets, ws, stream);
         return launch_tile<256, 256, 2, MOE_BIG_TILE_WN, MODE>(p, g, offsets, ws, stream);
+    }
     if (n % MOE_TILE_BN == 0)
         return launch_tile<MOE_TILE_BM, MOE_TILE_BN, MOE_TILE_WM, MOE_TILE_WN, MODE>(p, g, offsets, ws, stream);
     if (n % 128 == 0) return launch_tile<128, 128, 2, 2, MODE>(p, g, offsets, ws, stream);  // 64 x 64 per wave

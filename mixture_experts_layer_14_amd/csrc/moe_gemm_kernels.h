@@ -28,6 +28,8 @@ struct GemmArgs {
     const uint8_t* B_shared;    // shared expert weights [N, Kd] packed, or null
     const Tile* tiles;
     const int32_t* num_tiles;
+    const GroupUnit* units;     // tile_kernel_tail: group of each unit of positions
+    const int32_t* num_units;
     const float* topk_weights;  // w2: routing weight of each slot
     void* C;                    // act [R, I] (w13) or y [R, H] (w2)
     int64_t T;
@@ -211,20 +213,41 @@ __device__ __forceinline__ void mix_sched() {
     }
 }
 
-template <int BM, int BN, int WM, int WN, int ROWB, int MODE>
-__global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
+// LDS plan of a BM x BN tile with ROWB-byte row slabs: as many stages (4, 3
+// or 2) as fit in the 160 KiB beside the tile's BM routing weights.
+template <int BM, int BN, int ROWB>
+struct TileShape {
+    static constexpr int ROWS = BM + BN;        // rows staged per k-iteration
+    static constexpr int STAGE = ROWS * ROWB;   // bytes per stage
+    static constexpr int LDS_MAX = 160 * 1024;
+    static constexpr int LDS_STAGES = LDS_MAX - BM * 4;
+    static constexpr int STAGES = 4 * STAGE <= LDS_STAGES ? 4 : (3 * STAGE <= LDS_STAGES ? 3 : 2);
+    static constexpr int SMEM = STAGES * STAGE + BM * 4;
+};
+
+// Main loop of a tile: the guarded one (MFMAs of 32-row blocks past the
+// tile's rows skipped) only for tiles with fewer than BM rows, always, or
+// never (every MFMA runs; rows past the tile are computed and not stored).
+enum { kLoopAuto = 0, kLoopGuarded = 1, kLoopFull = 2 };
+
+// One BM x BN output tile (m-tile `tl`, n-tile `n_tile`, K part `kpart` of
+// `nparts`) on WM x WN waves; `smem` is the kernel's one LDS array, at least
+// TileShape::SMEM bytes.
+template <int BM, int BN, int WM, int WN, int ROWB, int MODE, int LOOP>
+__device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile tl, const int n_tile,
+                                          const int kpart, const int nparts, uint8_t* smem) {
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
-    constexpr int ROWS = BM + BN;                  // rows staged per k-iteration
-    constexpr int STAGE = ROWS * ROWB;             // bytes per stage
+    using Shape = TileShape<BM, BN, ROWB>;
+    constexpr int ROWS = Shape::ROWS;
+    constexpr int STAGE = Shape::STAGE;
     constexpr int SLOTS = ROWB / 16;               // 16-byte slots per row
     constexpr int RPC = kWave / SLOTS;             // rows per copy instruction
     constexpr int COPIES = ROWS / RPC / NW;        // copy instructions per wave per stage
     constexpr int KSTEPS = ROWB / 32;              // 16-k MFMA steps per k-iteration
-    constexpr int LDS_MAX = 160 * 1024;
-    constexpr int LDS_STAGES = LDS_MAX - BM * 4;
-    constexpr int STAGES = 4 * STAGE <= LDS_STAGES ? 4 : (3 * STAGE <= LDS_STAGES ? 3 : 2);
+    constexpr int LDS_MAX = Shape::LDS_MAX;
+    constexpr int STAGES = Shape::STAGES;
     static_assert(ROWB == 64 || ROWB == 128, "row slab of 64 or 128 bytes");
     static_assert(ROWS % (RPC * NW) == 0, "stage rows split evenly over the waves");
     static_assert(BM % RPC == 0, "copy instructions never straddle A and B");
@@ -239,21 +262,11 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
     // read of the main loop.
     constexpr int ROW_W_BYTES = BM * 4;
     static_assert(STAGES * STAGE + ROW_W_BYTES <= LDS_MAX, "LDS budget");
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE + ROW_W_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = wave_index(tid);
     const int wm = wave / WN, wn = wave % WN;
-
-    // w2 may split K: the n index runs over (part, n-tile), n-tile fastest,
-    // so blocks resident together share the part's A columns
-    const int nparts = MODE == kModeW2 ? g.ksplit : 1;
-    const TilePos tp = map_block(blockIdx.x, *g.num_tiles, g.n_tiles_n * nparts, g.tiles);
-    if (!tp.ok) return;
-    const Tile tl = g.tiles[tp.m];
-    const int kpart = tp.n / g.n_tiles_n;
-    const int n_tile = tp.n - kpart * g.n_tiles_n;
     const int64_t eltK = static_cast<int64_t>(g.Kd) * 2;
     const uint8_t* Bexp = tl.expert < g.E
                               ? g.B + static_cast<int64_t>(tl.expert) * g.N * eltK
@@ -329,19 +342,22 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
     // middle of stage it's last k-step; after it every wave has finished
     // reading stage it, whose buffer then takes the copies of stage
     // it+STAGES.
-    auto read_step = [&](const uint8_t* sA, int s, u32x4 (&fa)[TM], u32x4 (&fb)[TN]) {
-        const uint8_t* sB = sA + BM * ROWB;
-        const int chunk = s * 2 + khalf;
+    // LDS byte offsets of this lane's operand reads in k-step s of a stage:
+    // a 32-row block's swizzle depends on the lane alone, so block i (j) of
+    // the wave tile is i (j) * 32 rows further
+    auto a_lane = [&](int s) -> uint32_t {
+        const int r = wm * WTM + lrow;
+        return r * ROWB + lds_slot<ROWB>(r, s * 2 + khalf) * 16;
+    };
+    auto b_lane = [&](int s) -> uint32_t {
+        const int r = wn * WTN + lrow;
+        return BM * ROWB + r * ROWB + lds_slot<ROWB>(r, s * 2 + khalf) * 16;
+    };
+    auto read_at = [&](uint32_t pa, uint32_t pb, u32x4 (&fa)[TM], u32x4 (&fb)[TN]) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int r = wm * WTM + i * 32 + lrow;
-            fa[i] = *reinterpret_cast<const u32x4*>(sA + r * ROWB + lds_slot<ROWB>(r, chunk) * 16);
-        }
+        for (int i = 0; i < TM; ++i) fa[i] = *reinterpret_cast<const u32x4*>(smem + pa + i * 32 * ROWB);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int r = wn * WTN + j * 32 + lrow;
-            fb[j] = *reinterpret_cast<const u32x4*>(sB + r * ROWB + lds_slot<ROWB>(r, chunk) * 16);
-        }
+        for (int j = 0; j < TN; ++j) fb[j] = *reinterpret_cast<const u32x4*>(smem + pb + j * 32 * ROWB);
     };
     constexpr int kReads = TM + TN, kMfma = TM * TN;
     // this wave's copies of all but the STAGES-2 most recent stages landed
@@ -371,15 +387,15 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
         wait_later_stages();
         __builtin_amdgcn_s_barrier();
         u32x4 af[2][TM], bfr[2][TN];
-        read_step(smem, 0, af[0], bfr[0]);
+        read_at(a_lane(0), b_lane(0), af[0], bfr[0]);
         // copies per k-step when a stage's copies are spread over the k-steps
         // that precede the next barrier
         constexpr int CPS = (COPIES + KSTEPS - 2) / (KSTEPS - 1);
         for (int it = 0; it < nk; ++it) {
-            const uint8_t* sA = smem + (it % STAGES) * STAGE;
+            const uint32_t stage = (it % STAGES) * STAGE;
             static_for<KSTEPS - 1>([&](auto sc) {
                 constexpr int s = decltype(sc)::value;
-                read_step(sA, s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
+                read_at(stage + a_lane(s + 1), stage + b_lane(s + 1), af[(s + 1) & 1], bfr[(s + 1) & 1]);
                 // stage it+STAGES-1 goes to the buffer of stage it-1, free
                 // since the previous barrier
                 constexpr int q0 = s * CPS < COPIES ? s * CPS : COPIES;
@@ -397,23 +413,34 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
             mfma_range(0, H, af[L], bfr[L]);
             if constexpr (!PARTIAL) __builtin_amdgcn_sched_group_barrier(0x008, H, 0);
             __builtin_amdgcn_sched_barrier(0);
+            // the read offsets of stage it+1 are formed before the barrier,
+            // so its reads issue as soon as the barrier opens
+            uint32_t na = ((it + 1) % STAGES) * STAGE + a_lane(0);
+            uint32_t nb = ((it + 1) % STAGES) * STAGE + b_lane(0);
+            asm volatile("" : "+v"(na), "+v"(nb));
             // this wave's reads of stage it have landed (the MFMAs above
             // consumed the last of them); its copies of stage it+1 must land
             // too, with those of stages it+2 .. it+STAGES-1 still in flight
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
             wait_later_stages();
             __builtin_amdgcn_s_barrier();
+            // the MFMAs of the second half stay behind the barrier
+            __builtin_amdgcn_sched_barrier(0);
             // reads first: the compiler keeps LDS reads behind copies into LDS
-            read_step(smem + ((it + 1) % STAGES) * STAGE, 0, af[L ^ 1], bfr[L ^ 1]);
+            read_at(na, nb, af[L ^ 1], bfr[L ^ 1]);
             mfma_range(H, kMfma, af[L], bfr[L]);
             if constexpr (!PARTIAL) mix_sched<kMfma - H, kReads, 0>();
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    if (tl.row1 - tl.row0 == BM)
-        main_loop(std::false_type{});
-    else
-        main_loop(std::true_type{});
+    if constexpr (LOOP == kLoopAuto) {
+        if (tl.row1 - tl.row0 == BM)
+            main_loop(std::false_type{});
+        else
+            main_loop(std::true_type{});
+    } else {
+        main_loop(std::integral_constant<bool, LOOP == kLoopGuarded>{});
+    }
     // no copy may still write LDS when the block ends
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
@@ -475,6 +502,66 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
                     y[r * g.N + col] = f32_to_bf16_bits(acc[i][j][v] * w);
                 }
             }
+    }
+}
+
+template <int BM, int BN, int WM, int WN, int ROWB, int MODE>
+__global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[TileShape<BM, BN, ROWB>::SMEM];
+    // w2 may split K: the n index runs over (part, n-tile), n-tile fastest,
+    // so blocks resident together share the part's A columns
+    const int nparts = MODE == kModeW2 ? g.ksplit : 1;
+    const TilePos tp = map_block(blockIdx.x, *g.num_tiles, g.n_tiles_n * nparts, g.tiles);
+    if (!tp.ok) return;
+    const int kpart = tp.n / g.n_tiles_n;
+    tile_body<BM, BN, WM, WN, ROWB, MODE, kLoopAuto>(g, g.tiles[tp.m], tp.n - kpart * g.n_tiles_n, kpart,
+                                                nparts, smem);
+}
+
+// The tail tile runs every MFMA (its copies, not its MFMAs, set its time,
+// and the unguarded loop keeps the tuned instruction schedule; measured
+// faster than skipping the empty row blocks on the Mixtral-shape layer).
+#ifndef MOE_TAIL_LOOP
+#define MOE_TAIL_LOOP kLoopFull
+#endif
+
+// 256 x 256 tiles with 128 x 512 tail tiles.  The copies of a tile, not its
+// MFMAs, set its time, so the last m-tile of an expert with at most 128 rows
+// (a ragged remainder) is computed as a 128 x 512 tile: it stages 640 rows
+// per k-iteration for two n-tiles instead of 512 rows for each.  Tile order:
+// a group (m-tiles of one expert, as in map_block, plus the expert's tail
+// tile if it has one) sweeps pairs of n-tiles; per pair its main tiles take
+// both n-tiles (m fastest), then the tail tile takes the pair, so a weight
+// tile is still streamed once per group.  The positions of a group form
+// whole units of (n positions of a main m-tile) / 2, and units[u] describes
+// the group that owns unit u; each XCD takes a contiguous eighth of all
+// positions.
+template <int MODE>
+__global__ __launch_bounds__(8 * kWave) void tile_kernel_tail(GemmArgs g) {
+    constexpr int SM = TileShape<256, 256, 64>::SMEM, ST = TileShape<128, 512, 64>::SMEM;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[SM > ST ? SM : ST];
+    const int nparts = MODE == kModeW2 ? g.ksplit : 1;
+    const int half = g.n_tiles_n * nparts / 2;  // positions per unit (n_tiles_n is even)
+    const int total = *g.num_units * half;
+    const int per = (total + 7) / 8;
+    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+    if (local >= per) return;
+    const int t = xcd * per + local;
+    if (t >= total) return;
+    const GroupUnit d = g.units[t / half];
+    const int w = t - d.first_unit * half;
+    const int slot = 2 * d.cnt + d.tail;  // blocks per n-tile pair
+    const int pair = w / slot, r = w - pair * slot;
+    if (r < 2 * d.cnt) {
+        const int n = 2 * pair + r / d.cnt;
+        const int kpart = n / g.n_tiles_n;
+        tile_body<256, 256, 2, 4, 64, MODE, kLoopAuto>(g, g.tiles[d.first_tile + r % d.cnt],
+                                                       n - kpart * g.n_tiles_n, kpart, nparts, smem);
+    } else {
+        const int kpart = 2 * pair / g.n_tiles_n;
+        tile_body<128, 512, 2, 4, 64, MODE, MOE_TAIL_LOOP>(g, g.tiles[d.first_tile + d.cnt],
+                                                           (2 * pair - kpart * g.n_tiles_n) / 2, kpart,
+                                                           nparts, smem);
     }
 }
 

@@ -17,6 +17,16 @@ struct Tile {
     int32_t group;  // (index of the group's first m-tile) * 256 + m-tiles in the group
 };
 
+// A group of one expert's m-tiles in a schedule with tail tiles: cnt main
+// m-tiles from first_tile on, then (tail = 1) one tail m-tile; the group's
+// block positions start at unit first_unit.
+struct GroupUnit {
+    int32_t first_tile;
+    int32_t cnt;
+    int32_t tail;
+    int32_t first_unit;
+};
+
 hipError_t launch_topk(const float* logits, const float* bias, int64_t T, int E, int K,
                        int scoring, int renorm, int G, int TG, float rsf, int32_t* ids,
                        float* weights, hipStream_t stream);

@@ -73,6 +73,11 @@ SMALL = {
                         w_dtype="f32", seed=29, weight_seed=29, non_gated=True, swiglu_alpha=1.702),
     "non_gated_big_tiles": MC("non_gated_big_tiles", E=2, K=1, H=256, I=2048, T=1600, seed=30,
                               weight_seed=30, non_gated=True, weight_on_input=True),
+    # 256 x 256 tiles with 128 x 512 tail tiles in both GEMMs (N a multiple
+    # of 512): ~293 rows per expert leave remainders of a few dozen rows, the
+    # shared expert's 880 rows one of 112, and w2 splits K in two
+    "tail_tiles": MC("tail_tiles", E=3, K=1, H=512, I=2048, T=880, shared=1, seed=31,
+                     weight_seed=31),
 }
 
 
@@ -174,7 +179,12 @@ def test_full_size_layer(name):
     torch.cuda.synchronize()
     _check_permutation(cfg, st, ref_ids)
     rng = np.random.default_rng(cfg.seed)
-    sample = sorted(set([0, T - 1] + rng.choice(T, size=min(T, 10), replace=False).tolist()))
+    # random tokens, plus the token of the last row of the first 8 non-empty
+    # expert segments (rows of ragged or tail m-tiles)
+    off = st.offsets.cpu().numpy()
+    ends = [off[e + 1] - 1 for e in range(cfg.E) if off[e + 1] > off[e]][:8]
+    last_tokens = (st.sorted.cpu().numpy()[ends] // cfg.K).tolist()
+    sample = sorted(set([0, T - 1] + rng.choice(T, size=min(T, 10), replace=False).tolist() + last_tokens))
     experts = np.unique(ref_ids[sample])
     ref = O.moe_forward_tokens(U.oracle_layer(cfg, inp, T, experts=experts), sample, nthreads=16)
     got = U.out_to_f64(out[sample])
