@@ -95,12 +95,19 @@ __device__ __forceinline__ float in_weight(const GemmArgs& g, int64_t r) {
     return r < g.routed_rows ? g.topk_weights[g.sorted_slots[r]] : 1.0f;
 }
 
-// The w13 activations.  With act_alpha = 1 and act_limit = +inf glu_act is
-// bitwise silu(g) * u.
-__device__ __forceinline__ float silu_a(float z, float a) { return z / (1.0f + __expf(-a * z)); }
+// The w13 activations: silu_a(z) = z * sigmoid(a z), evaluated as
+// z * rcp(1 + 2^(-a log2(e) z)) with the hardware exp2 and reciprocal (each
+// within 1 ulp; the result is rounded to bf16 or kept as fp32 far inside the
+// tolerances).  For z -> -inf the reciprocal of inf is 0, for z -> +inf the
+// exponential is 0: no overflow path.  The clamp is one med3 per operand
+// (act_limit = +inf: no clamp).
+__device__ __forceinline__ float silu_a(float z, float a) {
+    const float e = __builtin_amdgcn_exp2f(-a * 1.44269504088896341f * z);
+    return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
 __device__ __forceinline__ float glu_act(const GemmArgs& g, float gate, float up) {
-    gate = fminf(gate, g.act_limit);
-    up = fminf(fmaxf(up, -g.act_limit), g.act_limit);
+    gate = __builtin_amdgcn_fmed3f(gate, -__builtin_huge_valf(), g.act_limit);
+    up = __builtin_amdgcn_fmed3f(up, -g.act_limit, g.act_limit);
     return silu_a(gate, g.act_alpha) * up;
 }
 
@@ -448,60 +455,90 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile tl, cons
         if (tid < BM) row_w[tid] = my_w;
         __syncthreads();
     }
+    // Accumulator value v of 32x32 block (i, j) holds row lr0 + i*32 +
+    // 8*(v/4) + v%4 (lr0 = this lane's first row) and column ccol of the
+    // block.  Stores address rows from this lane's first row, so the row
+    // offsets are compile-time multiples of the row pitch.  Tiles with all
+    // BM rows live skip the per-value row test.
     const int ccol = lane % 32;
-    const int crow = (lane / 32) * 4;
+    const int lr0 = wm * WTM + (lane / 32) * 4;
+    const bool full = tl.row1 - tl.row0 == BM;
+    auto row_ok = [&](auto full_tag, int dr) {
+        return decltype(full_tag)::value || tl.row0 + lr0 + dr < tl.row1;
+    };
     if (MODE == kModeW13) {
-        uint16_t* act = static_cast<uint16_t*>(g.C);
+        uint16_t* act = static_cast<uint16_t*>(g.C) + static_cast<int64_t>(tl.row0 + lr0) * g.I;
         if (g.gated) {
+            auto epi = [&](auto full_tag, auto w_tag) {
+                constexpr bool W = decltype(w_tag)::value;
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
+                for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int p = 0; p < TN / 2; ++p) {
-                    const int64_t col = static_cast<int64_t>(n_tile) * (BN / 2) + (wn * (TN / 2) + p) * 32 + ccol;
+                    for (int p = 0; p < TN / 2; ++p) {
+                        uint16_t* out = act + n_tile * (BN / 2) + (wn * (TN / 2) + p) * 32 + ccol;
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int lr = wm * WTM + i * 32 + 8 * (v / 4) + crow + (v % 4);
-                        const int64_t r = tl.row0 + lr;
-                        if (r < tl.row1) {
-                            const float w = use_w ? row_w[lr] : 1.0f;
-                            act[r * g.I + col] =
-                                f32_to_bf16_bits(glu_act(g, acc[i][2 * p][v] * w, acc[i][2 * p + 1][v] * w));
+                        for (int v = 0; v < 16; ++v) {
+                            const int dr = i * 32 + 8 * (v / 4) + v % 4;
+                            if (row_ok(full_tag, dr)) {
+                                float gt = acc[i][2 * p][v], up = acc[i][2 * p + 1][v];
+                                if constexpr (W) {
+                                    const float w = reinterpret_cast<const f32x4*>(row_w + lr0 + i * 32 + 8 * (v / 4))[0][v % 4];
+                                    gt *= w;
+                                    up *= w;
+                                }
+                                out[static_cast<int64_t>(dr) * g.I] = f32_to_bf16_bits(glu_act(g, gt, up));
+                            }
                         }
                     }
-                }
+            };
+            if (use_w)
+                epi(std::false_type{}, std::true_type{});
+            else if (full)
+                epi(std::true_type{}, std::false_type{});
+            else
+                epi(std::false_type{}, std::false_type{});
         } else {
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
-                    const int64_t col = static_cast<int64_t>(n_tile) * BN + wn * WTN + j * 32 + ccol;
+                    uint16_t* out = act + n_tile * BN + wn * WTN + j * 32 + ccol;
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
-                        const int lr = wm * WTM + i * 32 + 8 * (v / 4) + crow + (v % 4);
-                        const int64_t r = tl.row0 + lr;
-                        if (r < tl.row1) {
-                            const float w = use_w ? row_w[lr] : 1.0f;
-                            act[r * g.I + col] = f32_to_bf16_bits(silu_a(acc[i][j][v] * w, g.act_alpha));
+                        const int dr = i * 32 + 8 * (v / 4) + v % 4;
+                        if (row_ok(std::false_type{}, dr)) {
+                            const float w = use_w ? row_w[lr0 + dr] : 1.0f;
+                            out[static_cast<int64_t>(dr) * g.I] = f32_to_bf16_bits(silu_a(acc[i][j][v] * w, g.act_alpha));
                         }
                     }
                 }
         }
     } else {
-        uint16_t* y = static_cast<uint16_t*>(g.C) + kpart * g.part_stride;
+        uint16_t* y = static_cast<uint16_t*>(g.C) + kpart * g.part_stride +
+                      static_cast<int64_t>(tl.row0 + lr0) * g.N + n_tile * BN + wn * WTN + ccol;
+        auto epi = [&](auto full_tag) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+            for (int i = 0; i < TM; ++i) {
+                // the 16 rows' weights: rows 8q .. 8q+3 of the block are four
+                // consecutive (16-byte aligned) floats, one LDS read each
+                f32x4 wq[4];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int lr = wm * WTM + i * 32 + 8 * (v / 4) + crow + (v % 4);
-                const int64_t r = tl.row0 + lr;
-                if (r >= tl.row1) continue;
-                const float w = row_w[lr];
+                for (int q = 0; q < 4; ++q) wq[q] = *reinterpret_cast<const f32x4*>(row_w + lr0 + i * 32 + 8 * q);
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int64_t col = static_cast<int64_t>(n_tile) * BN + wn * WTN + j * 32 + ccol;
-                    y[r * g.N + col] = f32_to_bf16_bits(acc[i][j][v] * w);
+                for (int v = 0; v < 16; ++v) {
+                    const int dr = i * 32 + 8 * (v / 4) + v % 4;
+                    if (!row_ok(full_tag, dr)) continue;
+                    const float w = wq[v / 4][v % 4];
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        y[static_cast<int64_t>(dr) * g.N + j * 32] = f32_to_bf16_bits(acc[i][j][v] * w);
                 }
             }
+        };
+        if (full)
+            epi(std::true_type{});
+        else
+            epi(std::false_type{});
     }
 }
 
