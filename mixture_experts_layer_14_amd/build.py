@@ -17,6 +17,9 @@ HIPCC_FLAGS = [
     "-Wall", "-Wno-unused-result",
     # no packed-fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # loops start on a 64-byte boundary, so the GEMM main loops have one
+    # fixed layout (their speed depends on it; see the tile kernel's loop)
+    "-falign-loops=64",
     "-I", INCLUDE,
 ]
 

@@ -39,7 +39,8 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
                                                            int tail_rows, Tile* __restrict__ tiles,
                                                            int32_t* __restrict__ num_tiles,
                                                            GroupUnit* __restrict__ units,
-                                                           int32_t* __restrict__ num_units) {
+                                                           int32_t* __restrict__ num_units,
+                                                           int split_nn, int32_t* __restrict__ split) {
     __shared__ int32_t scan[1024];
     __shared__ int32_t uscan[1024];
     const int g = threadIdx.x;  // group: expert g, or the shared expert at g == E
@@ -95,6 +96,25 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
     if (g == 1023) {
         *num_tiles = scan[1023];
         if (units) *num_units = uscan[1023];
+    }
+    // Split of the K-split schedule (split_nn = n-tiles per m-tile): the
+    // m-tiles run whole-K in full rounds of 256 blocks, and only the trailing
+    // groups that cover the last, partial round are split along K.
+    // split[0] = split m-tiles (whole groups at the end of the table),
+    // split[1] = first row they own (rows below it have one K part).
+    if (split_nn > 0) {
+        __syncthreads();  // the tile table is written
+        if (g == 0) {
+            const int32_t nt = scan[1023];
+            const int32_t rem = static_cast<int32_t>((static_cast<int64_t>(nt) * split_nn) % 256);
+            int32_t first = nt;
+            if (rem > 0) {
+                first = nt - (rem + split_nn - 1) / split_nn;
+                first = tiles[first].group >> 8;  // back to the start of its group
+            }
+            split[0] = nt - first;
+            split[1] = first < nt ? tiles[first].row0 : 0x7fffffff;
+        }
     }
 }
 
@@ -303,20 +323,26 @@ template <class Pol>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y,
                                                       const int32_t* __restrict__ slot_to_row,
                                                       int64_t T, int K, int H, int shared,
-                                                      int64_t rows, int parts, void* __restrict__ out) {
+                                                      int64_t rows, int parts,
+                                                      const int32_t* __restrict__ split,
+                                                      void* __restrict__ out) {
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t t = idx / H;
     const int h = static_cast<int>(idx % H);
     if (t >= T) return;
     const int64_t part_stride = rows * H;
+    const int64_t split_row = split ? split[1] : 0;
     float s = 0.0f;
     for (int k = 0; k < K; ++k) {
         int64_t r = slot_to_row[t * K + k];
         r = r < 0 ? 0 : (r >= rows ? rows - 1 : r);
-        for (int q = 0; q < parts; ++q) s += Pol::load(y, q * part_stride + r * H + h);
+        const int np = r >= split_row ? parts : 1;
+        for (int q = 0; q < np; ++q) s += Pol::load(y, q * part_stride + r * H + h);
     }
-    if (shared)
-        for (int q = 0; q < parts; ++q) s += Pol::load(y, q * part_stride + (T * K + t) * H + h);
+    if (shared) {
+        const int np = T * K + t >= split_row ? parts : 1;
+        for (int q = 0; q < np; ++q) s += Pol::load(y, q * part_stride + (T * K + t) * H + h);
+    }
     Pol::store(out, t * H + h, s);
 }
 
@@ -327,6 +353,7 @@ __global__ __launch_bounds__(256) void combine_bf16x8_kernel(const uint16_t* __r
                                                              const int32_t* __restrict__ slot_to_row,
                                                              int64_t T, int K, int H, int shared,
                                                              int64_t rows, int parts,
+                                                             const int32_t* __restrict__ split,
                                                              uint16_t* __restrict__ out) {
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     const int hv = H / 8;
@@ -334,11 +361,13 @@ __global__ __launch_bounds__(256) void combine_bf16x8_kernel(const uint16_t* __r
     const int h = static_cast<int>(idx % hv) * 8;
     if (t >= T) return;
     const int64_t part_stride = rows * H;
+    const int64_t split_row = split ? split[1] : 0;
     float s[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) s[e] = 0.0f;
     auto add_row = [&](int64_t r) {
-        for (int q = 0; q < parts; ++q) {
+        const int np = r >= split_row ? parts : 1;
+        for (int q = 0; q < np; ++q) {
             const u32x4 v = *reinterpret_cast<const u32x4*>(y + q * part_stride + r * H + h);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -449,6 +478,11 @@ static bool big_tile(const GroupedProblem& p, int mode, int64_t n) {
 #ifndef MOE_W2_KSPLIT_MAX
 #define MOE_W2_KSPLIT_MAX 4
 #endif
+// Split only the m-tiles of the last, partial round of blocks (1), or every
+// m-tile (0).
+#ifndef MOE_W2_KSPLIT_TAIL_ONLY
+#define MOE_W2_KSPLIT_TAIL_ONLY 1
+#endif
 static int w2_ksplit(const GroupedProblem& p) {
     if (p.dtype != MOE_DTYPE_BF16 || rows_per_active_expert(p) <= MOE_STREAM_MAX_ROWS) return 1;
     if (p.H % MOE_TILE_BN != 0) return 1;
@@ -482,16 +516,19 @@ size_t w2_rows_workspace_bytes(const GroupedProblem& p) {
 // expert's remainder of at most tail_rows rows becomes a tail tile and the
 // unit table is written too.
 static void build_tiles(const GroupedProblem& p, const int32_t* offsets, int BM, GemmArgs& g,
-                        void* ws, hipStream_t stream, int tail_rows = 0) {
+                        void* ws, hipStream_t stream, int tail_rows = 0, int split_nn = 0) {
     int32_t* num_tiles = static_cast<int32_t*>(ws);
     int32_t* num_units = num_tiles + 1;
+    int32_t* split = num_tiles + 2;
     Tile* tiles = reinterpret_cast<Tile*>(static_cast<uint8_t*>(ws) + 256);
     GroupUnit* units = tail_rows > 0 ? reinterpret_cast<GroupUnit*>(static_cast<uint8_t*>(ws) + 256 +
                                                                     tile_table_bytes(p))
                                      : nullptr;
     build_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, p.E, p.shared ? static_cast<int32_t>(p.T) : 0,
                                                static_cast<int32_t>(p.T * p.K), BM, MOE_TILE_GM,
-                                               tail_rows, tiles, num_tiles, units, num_units);
+                                               tail_rows, tiles, num_tiles, units, num_units,
+                                               split_nn, split);
+    g.split = split_nn > 0 ? split : nullptr;
     g.tiles = tiles;
     g.num_tiles = num_tiles;
     g.units = units;
@@ -535,6 +572,21 @@ static hipError_t launch_tile_tail(const GroupedProblem& p, GemmArgs g, const in
     return hipGetLastError();
 }
 
+// w2 with a K split: 256 x 256 tiles whole-K in full rounds of 256 blocks,
+// the trailing groups split into g.ksplit K parts (tile_kernel_ksplit)
+template <int MODE>
+static hipError_t launch_tile_ksplit(const GroupedProblem& p, GemmArgs& g, const int32_t* offsets, void* ws,
+                                     hipStream_t stream) {
+    g.n_tiles_n = g.N / 256;
+    build_tiles(p, offsets, 256, g, ws, stream, 0, g.n_tiles_n);
+    // every position of either section has a block; surplus blocks exit
+    const int64_t whole = static_cast<int64_t>(g.max_m_tiles) * g.n_tiles_n;
+    const int64_t parts = whole * g.ksplit;
+    const int64_t blocks = 8 * ((whole + 7) / 8 + (parts + 7) / 8);
+    tile_kernel_ksplit<MODE><<<static_cast<unsigned>(blocks), 8 * kWave, 0, stream>>>(g);
+    return hipGetLastError();
+}
+
 // weight-streaming configuration: 16-column tiles per n-group for w13
 // (gate/up pairs) and w2, and waves splitting K inside a block
 #ifndef MOE_STREAM_NPW13
@@ -559,8 +611,10 @@ static hipError_t launch_stream(const GroupedProblem& p, GemmArgs g, const int32
     return hipGetLastError();
 }
 
+// g is updated with the schedule's split table when the K-split schedule
+// runs (the combine reads it)
 template <int MODE>
-static hipError_t bf16_gemm(const GroupedProblem& p, GemmArgs g, const int32_t* offsets, void* ws,
+static hipError_t bf16_gemm(const GroupedProblem& p, GemmArgs& g, const int32_t* offsets, void* ws,
                             hipStream_t stream) {
     const int64_t m = rows_per_active_expert(p);
     if (m <= MOE_STREAM_MAX_ROWS) {
@@ -570,6 +624,9 @@ static hipError_t bf16_gemm(const GroupedProblem& p, GemmArgs g, const int32_t* 
     }
     const int n = g.N;
     if (big_tile(p, MODE, n)) {
+        if (MODE == kModeW2 && g.ksplit > 1 && MOE_W2_KSPLIT_TAIL_ONLY && MOE_BIG_TILE_WN == 4 &&
+            MOE_BIG_TILE_ROWB == 64)
+            return launch_tile_ksplit<MODE>(p, g, offsets, ws, stream);
         if (MOE_TAIL_ROWS > 0 && n % 512 == 0 && MOE_BIG_TILE_WN == 4 && MOE_BIG_TILE_ROWB == 64)
             return launch_tile_tail<MODE>(p, g, offsets, ws, stream);
         return launch_tile<256, 256, 2, MOE_BIG_TILE_WN, MODE>(p, g, offsets, ws, stream);
@@ -700,14 +757,14 @@ hipError_t launch_w2_combine(const GroupedProblem& p, const void* act, const flo
     if (p.dtype != MOE_DTYPE_F32 && p.H % 8 == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
         const unsigned blocks = static_cast<unsigned>((n / 8 + 255) / 256);
         combine_bf16x8_kernel<<<blocks, 256, 0, stream>>>(static_cast<const uint16_t*>(y), slot_to_row, p.T, p.K,
-                                                         p.H, p.shared, total_rows(p), g.ksplit,
+                                                         p.H, p.shared, total_rows(p), g.ksplit, g.split,
                                                          static_cast<uint16_t*>(out));
     } else {
         const unsigned blocks = static_cast<unsigned>((n + 255) / 256);
         if (p.dtype != MOE_DTYPE_F32)
-            combine_kernel<PolBF16><<<blocks, 256, 0, stream>>>(y, slot_to_row, p.T, p.K, p.H, p.shared, total_rows(p), g.ksplit, out);
+            combine_kernel<PolBF16><<<blocks, 256, 0, stream>>>(y, slot_to_row, p.T, p.K, p.H, p.shared, total_rows(p), g.ksplit, g.split, out);
         else
-            combine_kernel<PolF32><<<blocks, 256, 0, stream>>>(y, slot_to_row, p.T, p.K, p.H, p.shared, total_rows(p), g.ksplit, out);
+            combine_kernel<PolF32><<<blocks, 256, 0, stream>>>(y, slot_to_row, p.T, p.K, p.H, p.shared, total_rows(p), g.ksplit, g.split, out);
     }
     return hipGetLastError();
 }
