@@ -33,25 +33,59 @@ __device__ __forceinline__ uint32_t ordered_bits(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+// Wave reductions on DPP (no LDS): lane shifts by 1, 2, 4 and 8 inside each
+// 16-lane row, then the row-15 and lane-31 broadcasts, leave op over all 64
+// lanes in lane 63 (an inclusive scan; lanes without a source take the
+// identity); readlane makes the result wave-uniform.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t identity, uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(identity), static_cast<int>(v),
+                                                             CTRL, ROW_MASK, 0xF, false));
+}
+
+// One step: every lane combines its value with the value DPP control CTRL
+// brings (32-bit words moved separately, so any trivially copyable T).
+template <int CTRL, int ROW_MASK, class T, class Op>
+__device__ __forceinline__ T dpp_step(T v, T identity, Op op) {
+    static_assert(sizeof(T) % 4 == 0, "32-bit words");
+    constexpr int W = sizeof(T) / 4;
+    struct Words { uint32_t w[W]; };
+    const Words a = __builtin_bit_cast(Words, v), id = __builtin_bit_cast(Words, identity);
+    Words b;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        uint64_t w = __shfl_xor(v, o, kWave);
-        v = v > w ? v : w;
-    }
+    for (int i = 0; i < W; ++i) b.w[i] = dpp_u32<CTRL, ROW_MASK>(id.w[i], a.w[i]);
+    return op(v, __builtin_bit_cast(T, b));
+}
+
+template <class T, class Op>
+__device__ __forceinline__ T wave_reduce_to_lane63(T v, T identity, Op op) {
+    v = dpp_step<0x111, 0xF>(v, identity, op);  // row_shr:1
+    v = dpp_step<0x112, 0xF>(v, identity, op);  // row_shr:2
+    v = dpp_step<0x114, 0xF>(v, identity, op);  // row_shr:4
+    v = dpp_step<0x118, 0xF>(v, identity, op);  // row_shr:8
+    v = dpp_step<0x142, 0xA>(v, identity, op);  // row_bcast:15 into rows 1 and 3
+    v = dpp_step<0x143, 0xC>(v, identity, op);  // row_bcast:31 into rows 2 and 3
     return v;
+}
+
+__device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int lane) {
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), lane));
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    v = wave_reduce_to_lane63(v, uint64_t{0}, [](uint64_t a, uint64_t b) { return a > b ? a : b; });
+    return (static_cast<uint64_t>(readlane_u32(static_cast<uint32_t>(v >> 32), 63)) << 32) |
+           readlane_u32(static_cast<uint32_t>(v), 63);
 }
 
 __device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-    return v;
+    v = wave_reduce_to_lane63(v, -__builtin_huge_valf(), [](float a, float b) { return fmaxf(a, b); });
+    return __uint_as_float(readlane_u32(__float_as_uint(v), 63));
 }
 
 __device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+    v = wave_reduce_to_lane63(v, 0.0f, [](float a, float b) { return a + b; });
+    return __uint_as_float(readlane_u32(__float_as_uint(v), 63));
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {

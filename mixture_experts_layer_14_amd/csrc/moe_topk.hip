@@ -67,24 +67,21 @@ __global__ __launch_bounds__(256) void topk_kernel(
         const int per = E / G;
         float my_gscore = -INFINITY;
         for (int g = 0; g < G; ++g) {
-            float b1 = -INFINITY, b2 = -INFINITY;
+            float2 top{-INFINITY, -INFINITY};  // the lane's two largest keys of group g
 #pragma unroll
             for (int v = 0; v < VPL; ++v) {
                 const int e = lane + kWave * v;
                 if (cand[v] && e / per == g) {
                     const float k = key[v];
-                    if (k > b1) { b2 = b1; b1 = k; } else if (k > b2) { b2 = k; }
+                    if (k > top.x) { top.y = top.x; top.x = k; } else if (k > top.y) { top.y = k; }
                 }
             }
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) {
-                const float o1 = __shfl_xor(b1, o, kWave);
-                const float o2 = __shfl_xor(b2, o, kWave);
-                const float n1 = fmaxf(b1, o1);
-                const float n2 = fmaxf(fminf(b1, o1), fmaxf(b2, o2));
-                b1 = n1;
-                b2 = n2;
-            }
+            // merge of two (largest, second largest) pairs, over the wave
+            top = wave_reduce_to_lane63(top, float2{-INFINITY, -INFINITY}, [](float2 a, float2 b) {
+                return float2{fmaxf(a.x, b.x), fmaxf(fminf(a.x, b.x), fmaxf(a.y, b.y))};
+            });
+            const float b1 = __uint_as_float(readlane_u32(__float_as_uint(top.x), 63));
+            const float b2 = __uint_as_float(readlane_u32(__float_as_uint(top.y), 63));
             const float gs = (bias != nullptr && per >= 2) ? b1 + b2 : b1;
             if (lane == g) my_gscore = gs;
         }
@@ -129,7 +126,7 @@ __global__ __launch_bounds__(256) void topk_kernel(
                 if (lane == owner) cand[v] = false;
             }
         }
-        const float s_sel = __shfl(s_mine, owner, kWave);
+        const float s_sel = __uint_as_float(readlane_u32(__float_as_uint(s_mine), owner));
         sel_sum += s_sel;
         if (lane == k) {
             my_id = e_sel;
