@@ -41,34 +41,42 @@ __global__ __launch_bounds__(64) void align_hist_kernel(const int32_t* __restric
 }
 
 // Exclusive scan over the E*nchunks counts in expert-major order, in place.
+// The matrix passes through LDS in segments of 16384 counts: loaded and
+// stored coalesced, each thread scans a contiguous run of 16 (LDS rows padded
+// by one word per 16, so the 64 lanes' runs fall in distinct banks), the
+// block scans the run sums, and a carry links the segments.
+constexpr int kScanSeg = 16384, kScanRun = 16;
+__device__ __forceinline__ int scan_slot(int i) { return i + i / kScanRun; }
+
 __global__ __launch_bounds__(1024) void align_scan_kernel(int32_t* __restrict__ counts, int E,
                                                           int nchunks,
                                                           int32_t* __restrict__ offsets) {
-    __shared__ int32_t partial[1024];
+    __shared__ int32_t buf[kScanSeg + kScanSeg / kScanRun];
+    __shared__ int32_t wave_sums[16];
     const int tid = threadIdx.x;
     const int64_t m = static_cast<int64_t>(E) * nchunks;
-    const int64_t per = (m + blockDim.x - 1) / blockDim.x;
-    const int64_t b = tid * per;
-    const int64_t e_ = b + per < m ? b + per : m;
-    int32_t s = 0;
-    for (int64_t i = b; i < e_; ++i) s += counts[i];
-    partial[tid] = s;
-    __syncthreads();
-    // Hillis-Steele inclusive scan of the per-thread sums
-    for (int off = 1; off < static_cast<int>(blockDim.x); off <<= 1) {
-        const int32_t v = tid >= off ? partial[tid - off] : 0;
+    int32_t carry = 0;
+    for (int64_t base = 0; base < m; base += kScanSeg) {
+        const int n = static_cast<int>(m - base < kScanSeg ? m - base : kScanSeg);
+        for (int i = tid; i < n; i += 1024) buf[scan_slot(i)] = counts[base + i];
         __syncthreads();
-        partial[tid] += v;
+        const int b = tid * kScanRun, e = b + kScanRun < n ? b + kScanRun : n;
+        int32_t s = 0;
+        for (int i = b; i < e; ++i) s += buf[scan_slot(i)];
+        int32_t seg_total;
+        int32_t run = carry + block_exclusive_sum_i32<1024>(s, wave_sums, &seg_total);
+        for (int i = b; i < e; ++i) {
+            const int32_t c = buf[scan_slot(i)];
+            buf[scan_slot(i)] = run;
+            if ((base + i) % nchunks == 0) offsets[(base + i) / nchunks] = run;
+            run += c;
+        }
+        __syncthreads();
+        for (int i = tid; i < n; i += 1024) counts[base + i] = buf[scan_slot(i)];
+        carry += seg_total;
         __syncthreads();
     }
-    int32_t run = tid > 0 ? partial[tid - 1] : 0;
-    for (int64_t i = b; i < e_; ++i) {
-        const int32_t c = counts[i];
-        counts[i] = run;
-        if (i % nchunks == 0) offsets[i / nchunks] = run;
-        run += c;
-    }
-    if (tid == static_cast<int>(blockDim.x) - 1) offsets[E] = partial[tid];
+    if (tid == 0) offsets[E] = carry;
 }
 
 __global__ __launch_bounds__(64) void align_scatter_kernel(const int32_t* __restrict__ ids,
@@ -124,7 +132,7 @@ __global__ __launch_bounds__(kAlignSmallWaves * kWave) void align_small_kernel(
     const int32_t* __restrict__ ids, int64_t n, int E, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_slots, int32_t* __restrict__ slot_to_row) {
     __shared__ int32_t cnt[kAlignSmallWaves][kAlignMaxExperts];  // counts, then cursors
-    __shared__ int32_t tot[1024];
+    __shared__ int32_t wave_sums[kAlignSmallWaves];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), w = wave_index(tid);
     const int chunk = static_cast<int>((n + kAlignSmallWaves - 1) / kAlignSmallWaves);
     const int begin = w * chunk;
@@ -146,20 +154,13 @@ __global__ __launch_bounds__(kAlignSmallWaves * kWave) void align_small_kernel(
             run += c;
         }
     }
-    tot[tid] = tid < E ? run : 0;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        const int32_t v = tid >= off ? tot[tid - off] : 0;
-        __syncthreads();
-        tot[tid] += v;
-        __syncthreads();
-    }
-    const int32_t base = tot[tid] - run;  // exclusive prefix of expert tid
+    int32_t total;
+    const int32_t base = block_exclusive_sum_i32<kAlignSmallWaves * kWave>(tid < E ? run : 0, wave_sums, &total);
     if (tid < E) {
         offsets[tid] = base;
         for (int v = 0; v < kAlignSmallWaves; ++v) cnt[v][tid] += base;
     }
-    if (tid == 1023) offsets[E] = tot[1023];
+    if (tid == 0) offsets[E] = total;
     __syncthreads();
     const uint64_t lt_mask = (1ull << lane) - 1ull;
     for (int b0 = begin; b0 < end; b0 += kWave) {

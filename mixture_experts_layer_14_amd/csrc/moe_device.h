@@ -88,6 +88,35 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
     return __uint_as_float(readlane_u32(__float_as_uint(v), 63));
 }
 
+// Inclusive prefix sum across the wave: the reduction steps above leave
+// lane i holding lanes 0..i (each step combines disjoint lane ranges).
+__device__ __forceinline__ int32_t wave_inclusive_sum_i32(int32_t v) {
+    return wave_reduce_to_lane63(v, int32_t{0}, [](int32_t a, int32_t b) { return a + b; });
+}
+
+// Exclusive prefix sum of v over the NT threads of a block (NT a multiple of
+// 64, at most 64 waves); `wave_sums` is LDS scratch of NT/64 ints.  Every
+// thread of the block must call it; *total receives the block sum.
+template <int NT>
+__device__ __forceinline__ int32_t block_exclusive_sum_i32(int32_t v, int32_t* wave_sums, int32_t* total) {
+    static_assert(NT % 64 == 0 && NT / 64 <= 64, "whole waves");
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63, w = wave_index(threadIdx.x);
+    const int32_t incl = wave_inclusive_sum_i32(v);
+    if (lane == 63) wave_sums[w] = incl;
+    __syncthreads();
+    int32_t before = 0, all = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const int32_t t = wave_sums[i];
+        before += i < w ? t : 0;
+        all += t;
+    }
+    __syncthreads();  // wave_sums may be reused after the call
+    *total = all;
+    return before + incl - v;
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }

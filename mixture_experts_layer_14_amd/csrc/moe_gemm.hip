@@ -41,8 +41,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
                                                            GroupUnit* __restrict__ units,
                                                            int32_t* __restrict__ num_units,
                                                            int split_nn, int32_t* __restrict__ split) {
-    __shared__ int32_t scan[1024];
-    __shared__ int32_t uscan[1024];
+    __shared__ int32_t wave_sums[16];
     const int g = threadIdx.x;  // group: expert g, or the shared expert at g == E
     int32_t r0 = 0, r1 = 0;
     if (g < E) {
@@ -59,19 +58,9 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
     const int32_t tail = rem > 0 && rem <= tail_rows ? 1 : 0;
     const int32_t nmain = (r1 - r0) / BM + (rem > 0 && !tail ? 1 : 0);
     const int32_t nt = nmain + tail;
-    scan[g] = nt;
-    uscan[g] = 2 * nmain + tail;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        const int32_t v = g >= off ? scan[g - off] : 0;
-        const int32_t u = g >= off ? uscan[g - off] : 0;
-        __syncthreads();
-        scan[g] += v;
-        uscan[g] += u;
-        __syncthreads();
-    }
-    const int32_t start = scan[g] - nt;
-    const int32_t ustart = uscan[g] - (2 * nmain + tail);
+    int32_t all_tiles, all_units;
+    const int32_t start = block_exclusive_sum_i32<1024>(nt, wave_sums, &all_tiles);
+    const int32_t ustart = block_exclusive_sum_i32<1024>(2 * nmain + tail, wave_sums, &all_units);
     // an expert's m-tiles form groups of at most gm_max, balanced in size; a
     // group's tiles sweep the n-tiles together so they share each weight
     // tile; the tail tile joins the expert's last group
@@ -93,9 +82,9 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
             for (int32_t u = 0; u < 2 * cnt + has_tail; ++u) units[ustart + 2 * first + u] = d;
         }
     }
-    if (g == 1023) {
-        *num_tiles = scan[1023];
-        if (units) *num_units = uscan[1023];
+    if (g == 0) {
+        *num_tiles = all_tiles;
+        if (units) *num_units = all_units;
     }
     // Split of the K-split schedule (split_nn = n-tiles per m-tile): the
     // m-tiles run whole-K in full rounds of 256 blocks, and only the trailing
@@ -105,7 +94,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
     if (split_nn > 0) {
         __syncthreads();  // the tile table is written
         if (g == 0) {
-            const int32_t nt = scan[1023];
+            const int32_t nt = all_tiles;
             const int32_t rem = static_cast<int32_t>((static_cast<int64_t>(nt) * split_nn) % 256);
             int32_t first = nt;
             if (rem > 0) {
