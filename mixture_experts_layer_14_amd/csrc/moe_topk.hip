@@ -65,13 +65,15 @@ __global__ __launch_bounds__(256) void topk_kernel(
 
     if (G > 1) {
         const int per = E / G;
+        int grp[VPL];  // group of each of the lane's experts (one division each)
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) grp[v] = (lane + kWave * v) / per;
         float my_gscore = -INFINITY;
         for (int g = 0; g < G; ++g) {
             float2 top{-INFINITY, -INFINITY};  // the lane's two largest keys of group g
 #pragma unroll
             for (int v = 0; v < VPL; ++v) {
-                const int e = lane + kWave * v;
-                if (cand[v] && e / per == g) {
+                if (cand[v] && grp[v] == g) {
                     const float k = key[v];
                     if (k > top.x) { top.y = top.x; top.x = k; } else if (k > top.y) { top.y = k; }
                 }
@@ -95,10 +97,7 @@ __global__ __launch_bounds__(256) void topk_kernel(
             keep |= 1ull << (~static_cast<uint32_t>(packed));
         }
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) {
-            const int e = lane + kWave * v;
-            cand[v] = cand[v] && ((keep >> (e / per)) & 1ull);
-        }
+        for (int v = 0; v < VPL; ++v) cand[v] = cand[v] && ((keep >> grp[v]) & 1ull);
     }
 
     int my_id = 0;
