@@ -587,6 +587,12 @@ static hipError_t launch_tile_ksplit(const GroupedProblem& p, GemmArgs& g, const
 #ifndef MOE_STREAM_WAVES
 #define MOE_STREAM_WAVES 4
 #endif
+// A reduction at least this long is split over 8 waves per block instead
+// (measured: Mixtral-shape w2, K = 14336, 188 -> 181 us; the shorter
+// reductions are slower with 8).
+#ifndef MOE_STREAM_LONG_K
+#define MOE_STREAM_LONG_K 8192
+#endif
 
 template <int TM, int MODE>
 static hipError_t launch_stream(const GroupedProblem& p, GemmArgs g, const int32_t* offsets, void* ws,
@@ -594,9 +600,12 @@ static hipError_t launch_stream(const GroupedProblem& p, GemmArgs g, const int32
     constexpr int NPW = MODE == kModeW13 ? MOE_STREAM_NPW13 : MOE_STREAM_NPW2;
     build_tiles(p, offsets, TM * 16, g, ws, stream);
     const int groups = g.N / (NPW * 16);
-    const int64_t blocks = static_cast<int64_t>(g.max_m_tiles) * groups;
-    stream_kernel<TM, NPW, MOE_STREAM_WAVES, MODE, MOE_STREAM_U>
-        <<<static_cast<unsigned>(blocks), MOE_STREAM_WAVES * kWave, 0, stream>>>(g);
+    const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(g.max_m_tiles) * groups);
+    if (g.Kd >= MOE_STREAM_LONG_K)
+        stream_kernel<TM, NPW, 8, MODE, MOE_STREAM_U><<<blocks, 8 * kWave, 0, stream>>>(g);
+    else
+        stream_kernel<TM, NPW, MOE_STREAM_WAVES, MODE, MOE_STREAM_U>
+            <<<blocks, MOE_STREAM_WAVES * kWave, 0, stream>>>(g);
     return hipGetLastError();
 }
 

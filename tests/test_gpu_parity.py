@@ -163,11 +163,17 @@ def test_all_tokens_to_one_expert_and_single_token():
 
 
 FULL = ["mixtral_decode", "mixtral", "qwen", "dsv3_decode", "dsv3"]
+# w2 with a K split where both sections of the schedule are populated: 4
+# experts of ~1100 rows (5 m-tiles each) x 16 n-tiles = 320 blocks, so the
+# last expert's group runs as 2 K parts and the rest whole-K; checked on
+# sampled rows (including each expert's last row)
+SAMPLED = {"w2_split_sections": MC("w2_split_sections", E=4, K=2, H=4096, I=2048, T=2200, seed=32,
+                                   weight_seed=32)}
 
 
-@pytest.mark.parametrize("name", FULL)
+@pytest.mark.parametrize("name", FULL + sorted(SAMPLED))
 def test_full_size_layer(name):
-    cfg = synth.CONFIGS[name]
+    cfg = SAMPLED[name] if name in SAMPLED else synth.CONFIGS[name]
     T = cfg.T
     print("case", name, "T", T, flush=True)
     inp = synth.make_inputs(cfg, T, device="cuda")
