@@ -36,8 +36,18 @@ __global__ __launch_bounds__(kRThreads) void router_gemm_kernel(
     const int lane = tid & (kWave - 1);
     const int wave = wave_index(tid);
     const int wm = wave >> 1, wn = wave & 1;
-    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRBM;
-    const int e0 = blockIdx.y * kRBN;
+    // block -> (token tile, expert tile): block b runs on XCD b % 8; each XCD
+    // takes a contiguous eighth of the tiles in token-major order, so the
+    // expert tiles of one token tile run together on one XCD and read its
+    // hidden rows from that XCD's L2 (token-tile-fastest order re-read every
+    // hidden row once per expert tile)
+    const int tiles_e = (E + kRBN - 1) / kRBN;
+    const int64_t tiles = ((T + kRBM - 1) / kRBM) * tiles_e;
+    const int64_t per = (tiles + 7) / 8;
+    const int64_t pos = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if ((blockIdx.x >> 3) >= per || pos >= tiles) return;
+    const int64_t t0 = pos / tiles_e * kRBM;
+    const int e0 = static_cast<int>(pos % tiles_e) * kRBN;
     const int part = blockIdx.z;
     const int nk_all = H / kRK;
     const int k_first = part * nk_all / parts;
@@ -219,8 +229,8 @@ hipError_t launch_router(const void* hidden, int act_dtype, const void* gate, in
     }
     const int parts = router_parts(T, E, H);
     float* dst = parts > 1 ? static_cast<float*>(ws) : logits;
-    const dim3 grid(static_cast<unsigned>((T + kRBM - 1) / kRBM), static_cast<unsigned>((E + kRBN - 1) / kRBN),
-                    static_cast<unsigned>(parts));
+    const int64_t tiles = ((T + kRBM - 1) / kRBM) * ((E + kRBN - 1) / kRBN);
+    const dim3 grid(static_cast<unsigned>(8 * ((tiles + 7) / 8)), 1, static_cast<unsigned>(parts));
     const uint16_t* x = static_cast<const uint16_t*>(hidden);
     if (gf32)
         router_gemm_kernel<true><<<grid, kRThreads, 0, stream>>>(x, gate, T, E, H, parts, dst);
