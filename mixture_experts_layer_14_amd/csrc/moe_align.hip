@@ -120,13 +120,20 @@ __global__ __launch_bounds__(64) void align_scatter_kernel(const int32_t* __rest
     }
 }
 
-// Whole permutation in one block for small slot counts (decode batches):
+// Whole permutation in one block for small slot counts (decode and
+// Mixtral-size prefill batches):
 // 16 waves each own a contiguous run of slots; per-wave expert counts in LDS,
 // one scan gives the offsets and every wave's starting row per expert, then
 // each wave scatters its run in slot order (the same stable result as the
 // three-kernel path, in one launch instead of three).
 constexpr int kAlignSmallWaves = 16;
-constexpr int64_t kAlignSmallMax = 4096;
+// Slot counts up to this run as the single block (measured: 8192 slots,
+// Mixtral-shape prefill, one launch instead of three saves ~8 us; at 65536
+// slots one block is slower than the three-kernel path)
+#ifndef MOE_ALIGN_SMALL_MAX
+#define MOE_ALIGN_SMALL_MAX 16384
+#endif
+constexpr int64_t kAlignSmallMax = MOE_ALIGN_SMALL_MAX;
 
 __global__ __launch_bounds__(kAlignSmallWaves * kWave) void align_small_kernel(
     const int32_t* __restrict__ ids, int64_t n, int E, int32_t* __restrict__ offsets,

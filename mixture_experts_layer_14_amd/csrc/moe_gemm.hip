@@ -13,13 +13,15 @@
 //
 // Both GEMMs are "NT": A rows and B rows are contiguous along the reduction
 // dimension, which is what the MFMA operand layout wants (each lane holds a
-// 16-byte run of one row).  A block computes a BM x BN tile with WM x WN
-// waves; every k-iteration stages 128 bytes of each A row and each B row in
-// LDS (rows padded to 144 bytes), double-buffered through registers so the
-// next iteration's global loads are in flight during the MFMAs.  The w13
-// tile loads gate rows and up rows in interleaved 16-row blocks, so the
-// MFMA tile holding gate columns and the one holding the matching up
-// columns sit in the same lanes and SiLU-and-mul happens in registers.
+// 16-byte run of one row).  The w13 tiles load gate rows and up rows in
+// interleaved blocks, so the MFMA tile holding gate columns and the one
+// holding the matching up columns sit in the same lanes and SiLU-and-mul
+// happens in registers.  Kernels: tile_kernel / tile_kernel_tail /
+// tile_kernel_ksplit (bf16 prefill, moe_gemm_kernels.h), stream_kernel
+// (bf16 decode, same file), tile_kernel_fp8 (moe_gemm_fp8.h) and, below,
+// grouped_gemm_kernel for fp32 layers: BM x BN tiles of 16x16 MFMAs with
+// 128 bytes of each A and B row per k-iteration in LDS (rows padded to 144
+// bytes), double-buffered through registers.
 #include "moe_device.h"
 #include "moe_gemm_kernels.h"
 #include "moe_gemm_fp8.h"

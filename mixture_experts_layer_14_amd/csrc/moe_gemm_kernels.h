@@ -304,10 +304,6 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile tl, cons
 #pragma unroll
     for (int q = 0; q < COPIES; ++q) src[q] += (static_cast<int64_t>(k_first) * ROWB) << kstep_shift(q);
 
-    // copies of k-iteration `it` into its stage buffer; past the last
-    // k-iteration the source is clamped to it (a redundant in-bounds copy
-    // into a buffer nobody reads again keeps the copy count per k-iteration
-    // fixed and the loop free of branches)
     // copies q0 .. q1-1 of this wave's share of k-iteration `kit`; past the
     // last k-iteration the source is clamped to it (a redundant in-bounds
     // copy into a buffer nobody reads again keeps the copy count per

@@ -1,5 +1,5 @@
 """moe_align_permute on the GPU against the oracle's stable counting sort,
-bit-exact, on both sides of the single-block path's size limit (4096 slots)
+bit-exact, on both sides of the single-block path's size limit (16384 slots)
 and for uniform, skewed, single-expert and out-of-range-free id patterns."""
 import numpy as np
 import pytest
@@ -21,7 +21,7 @@ def _ids(n, E, kind, rng):
 
 
 @pytest.mark.parametrize("n,E", [(1, 8), (63, 8), (64, 8), (65, 257), (1000, 512), (4096, 64),
-                                 (4097, 64), (20000, 128)])
+                                 (8192, 8), (16384, 512), (16385, 64), (20000, 128)])
 @pytest.mark.parametrize("kind", ["uniform", "skewed", "one"])
 def test_permutation_bit_exact(n, E, kind):
     rng = np.random.default_rng(n * 31 + E)
