@@ -644,7 +644,15 @@ static hipError_t launch_tile_fp8(const GroupedProblem& p, GemmArgs g, const int
     g.n_tiles_n = g.N / BN;
     const int64_t total = static_cast<int64_t>(g.max_m_tiles) * g.n_tiles_n;
     const int64_t blocks = 8 * ((total + 7) / 8);
-    tile_kernel_fp8<BM, BN, WM, WN, MODE><<<static_cast<unsigned>(blocks), WM * WN * kWave, 0, stream>>>(g);
+    // scale loads of 4 k-blocks when the row's 128-value blocks come in
+    // whole groups of 4 and the scale arrays start 16-byte aligned (every
+    // group in bounds and aligned)
+    const uintptr_t sc = reinterpret_cast<uintptr_t>(g.A_scale) | reinterpret_cast<uintptr_t>(g.B_scale) |
+                         reinterpret_cast<uintptr_t>(g.B_shared_scale);
+    if ((g.Kd / 128) % 4 == 0 && sc % 16 == 0)
+        tile_kernel_fp8<BM, BN, WM, WN, MODE, 4><<<static_cast<unsigned>(blocks), WM * WN * kWave, 0, stream>>>(g);
+    else
+        tile_kernel_fp8<BM, BN, WM, WN, MODE, 1><<<static_cast<unsigned>(blocks), WM * WN * kWave, 0, stream>>>(g);
     return hipGetLastError();
 }
 

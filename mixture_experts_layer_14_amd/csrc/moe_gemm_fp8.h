@@ -16,16 +16,23 @@
 // lane and MFMA tile, and the promotion costs one FMA per element (with
 // tokens as the first operand every element would need its own scale
 // product, which makes the vector ALU, not the matrix core, the limit).
-// Staging, swizzle, tile order and the pipeline follow tile_kernel; each
-// stage also carries the k-block's per-token A scales and the weight block
-// scales, copied by 4-byte gathered global_load_lds.
+// Staging, swizzle, tile order and the pipeline follow tile_kernel.  The
+// per-token A scales and the weight block scales are copied by gathered
+// global_load_lds too.  A copy instruction costs the CU's copy path the same
+// time whether it moves 4 or 16 bytes a lane, so when the k-blocks of a row
+// come in whole groups of SG = 4, each wave copies the scales of a group
+// (16 bytes a lane) once per group into a two-slot ring beside the stages;
+// otherwise (SG = 1) each stage carries its k-block's scales (4 bytes a
+// lane).
 #pragma once
+
+#include <type_traits>
 
 #include "moe_gemm_kernels.h"
 
 namespace moe {
 
-template <int BM, int BN, int WM, int WN, int MODE>
+template <int BM, int BN, int WM, int WN, int MODE, int SG>
 __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
     constexpr int ROWB = 128;                     // one 128-wide k block per stage
     constexpr int NW = WM * WN;
@@ -40,29 +47,43 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
     // 32-row blocks (one 128-row scale block of each), w2 tiles hold BN/128
     // consecutive scale blocks
     constexpr int NBS = MODE == kModeW13 ? 2 : BN / 128;
-    // stage: A rows, B rows, then one 256-byte scale slot per wave (lane l of
-    // wave w at byte 4l: A scale of token w*SROWS+l for l < SROWS; wave 0
-    // also holds the weight block scales at lanes SROWS .. SROWS+NBS-1)
-    constexpr int SCALES = NW * 256;
+    constexpr bool GROUPED = SG > 1;
+    // SG = 1: a stage is the A rows, the B rows, then one 256-byte scale slot
+    // per wave (lane l of wave w at byte 4l: the A scale of token w*SROWS+l
+    // for l < SROWS; wave 0 also holds the weight block scales at lanes
+    // SROWS .. SROWS+NBS-1).
+    // SG = 4: a ring slot holds one group's scales by position p, 16 bytes
+    // each (the group's 4 scales): A token p for p < BM, weight block scale
+    // p-BM for BM <= p < BM+NBS, a copy of token 0's past that.  The copy of
+    // wave w covers positions w*SROWS .. w*SROWS+63, so neighbouring waves
+    // write some positions twice, always with the same values.
+    constexpr int SCALES = GROUPED ? 0 : NW * 256;
     constexpr int STAGE = ROWS * ROWB + SCALES;
-    constexpr int PER_STAGE = COPIES + 1;          // copy instructions per wave per stage
+    constexpr int SPOS = (NW - 1) * SROWS + kWave;       // positions of a ring slot
+    constexpr int RING_SLOT = GROUPED ? (SPOS * 16 + 255) / 256 * 256 : 0;
+    constexpr int RING = 2 * RING_SLOT;
+    constexpr int PER_STAGE = GROUPED ? COPIES : COPIES + 1;  // copy instructions per wave per stage
     constexpr int LDS_MAX = 160 * 1024;
     constexpr int ROW_W_BYTES = MODE == kModeW2 ? BM * 4 : 0;
-    constexpr int STAGES = 4 * STAGE + ROW_W_BYTES <= LDS_MAX ? 4 : 3;
+    constexpr int STAGES = 4 * STAGE + RING + ROW_W_BYTES <= LDS_MAX ? 4 : 3;
     constexpr int KSTEPS = 2;                      // 64-value MFMA steps per k block
     static_assert(ROWS % (RPC * NW) == 0 && BM % RPC == 0 && BM % NW == 0, "copy split");
     static_assert(SROWS + NBS <= kWave, "scale slots of wave 0");
+    static_assert(SG == 1 || SG == 4, "scales per k-block or per group of 4");
+    static_assert(!GROUPED || BM + NBS <= SPOS, "ring positions");
+    static_assert(!GROUPED || SG >= STAGES - 2, "a group's scale copy lands within the group");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
     static_assert(MODE != kModeW2 || NW * kWave >= BM, "one thread per row weight");
     static_assert(MODE != kModeW13 || (TN == 2 && BN == 256 && WN == 4),
                   "w13 fp8: each wave holds one 32-feature gate/up pair, a block one 128-feature group");
-    static_assert(PER_STAGE * (STAGES - 2) <= 63, "vmcnt immediate range");
+    static_assert(PER_STAGE * (STAGES - 2) + 1 <= 63, "vmcnt immediate range");
     static_assert(MODE != kModeW13 || BM * WN * 4 <= STAGE, "w13 amax exchange fits one stage");
     // one LDS object: the stage buffers, then (w2) the tile's routing
     // weights.  A second __shared__ array would make the compiler wait for
     // every copy in flight before each LDS read of the main loop.
-    static_assert(STAGES * STAGE + ROW_W_BYTES <= LDS_MAX, "LDS budget");
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE + ROW_W_BYTES];
+    static_assert(STAGES * STAGE + RING + ROW_W_BYTES <= LDS_MAX, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE + RING + ROW_W_BYTES];
+    uint8_t* const ring = smem + STAGES * STAGE;
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -97,26 +118,37 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
     // 0, a weight-scale row (lanes SROWS .. SROWS+NBS-1).  The other lanes
     // copy the wave's first A-scale row into slots nobody reads, so the copy
     // needs no exec mask (a branch would split the loop's scheduling region)
+    // (SG = 4: the scales of ring position wave*SROWS + lane)
     const float* ssrc;
     {
-        const int l = lane < SROWS ? lane : 0;
-        int64_t r = tl.row0 + wave * SROWS + l;
+        const int p = GROUPED ? wave * SROWS + lane : (lane < SROWS ? wave * SROWS + lane : 0);
+        int64_t r = tl.row0 + (p < BM ? p : 0);
         if (r >= tl.row1) r = tl.row0;
         ssrc = g.A_scale + a_source_row<MODE>(g, r) * nkb;
-        if (wave == 0 && lane >= SROWS && lane < SROWS + NBS) {
-            const int slot = lane - SROWS;
+        const int slot = GROUPED ? p - BM : (wave == 0 ? lane - SROWS : -1);
+        if (slot >= 0 && slot < NBS) {
             const int rep = MODE == kModeW13 ? slot * 32 : slot * 128;  // a local row of the block
             const int b = static_cast<int>(b_weight_row<MODE, BN, 32>(g, n_tile, rep) / 128);
             ssrc = Bsc + static_cast<int64_t>(b) * nkb;
         }
     }
+    // SG = 4: the scales of group grp into ring slot grp % 2
+    auto issue_scales = [&](int grp) {
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const void*>(ssrc + grp * SG),
+            (__attribute__((address_space(3))) void*)(ring + (grp & 1) * RING_SLOT + wave * SROWS * 16), 16, 0, 0);
+    };
 
     // copies q0 .. q1-1 (and, with q1 == COPIES, the scales) of this wave's
     // share of k-block `kit`; past the last k-block the source is clamped to
     // it, keeping the copy count per k-block fixed and the loop branch-free
     auto issue_copies = [&](int kit, int q0, int q1) {
-        uint8_t* st = smem + (kit % STAGES) * STAGE;
-        const int kc = kit < nkb ? kit : nkb - 1;
+        int kc = kit < nkb ? kit : nkb - 1;
+        int sb = (kit % STAGES) * STAGE;
+        // opaque per call: with SG = 4 the compiler would otherwise form the
+        // sources of all four iterations of a group up front and keep them live
+        asm volatile("" : "+s"(kc), "+s"(sb));
+        uint8_t* st = smem + sb;
         const int64_t off = static_cast<int64_t>(kc) * ROWB;
 #pragma unroll
         for (int q = q0; q < q1; ++q)
@@ -124,14 +156,19 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
                 // packed B (the later copies) advances 16x faster along k
                 reinterpret_cast<const void*>(src[q] + ((wave * COPIES + q) * RPC >= BM ? off << 4 : off)),
                 (__attribute__((address_space(3))) void*)(st + (wave * COPIES + q) * 1024), 16, 0, 0);
-        if (q1 == COPIES)
+        if (!GROUPED && q1 == COPIES)
             __builtin_amdgcn_global_load_lds(
                 reinterpret_cast<const void*>(ssrc + kc),
                 (__attribute__((address_space(3))) void*)(st + ROWS * ROWB + wave * 256), 4, 0, 0);
     };
-    // this wave's copies of all but the STAGES-2 most recent stages landed
-    auto wait_later_stages = [&]() {
-        constexpr int n = (STAGES - 2) * PER_STAGE;
+    // this wave's copies of all but the STAGES-2 most recent stages landed.
+    // Loads complete in order; with SG = 4 a group's scale copy, issued
+    // before the stage copies of its first iteration, is one more operation
+    // that may stay in flight while that iteration is among the STAGES-2
+    // most recent (sub, the iteration's place in its group, < STAGES-2).
+    auto wait_later_stages = [&](auto sub_tag) {
+        constexpr int sub = decltype(sub_tag)::value;
+        constexpr int n = (STAGES - 2) * PER_STAGE + (GROUPED && sub < STAGES - 2 ? 1 : 0);
         __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
     };
 
@@ -147,7 +184,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
 
     // w2: the tile's routing weights, loaded into a register before the main
     // loop and moved to LDS after it (no copy left in flight to wait for)
-    float* row_w = reinterpret_cast<float*>(smem + STAGES * STAGE);
+    float* row_w = reinterpret_cast<float*>(smem + STAGES * STAGE + RING);
     float my_w = 1.0f;
     if (MODE == kModeW2 && tid < BM) {
         const int64_t r = tl.row0 + tid;
@@ -181,35 +218,66 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
         }
     };
 
+    if constexpr (GROUPED) issue_scales(0);
 #pragma unroll
     for (int st = 0; st < STAGES - 1; ++st) issue_copies(st, 0, COPIES);
-    wait_later_stages();
+    {
+        constexpr int n = (STAGES - 2) * PER_STAGE;
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
+    }
     __builtin_amdgcn_s_barrier();
     i32x8 af[2][TM], bfr[2][TN];
     read_step(smem, 0, af[0], bfr[0]);
-    for (int it = 0; it < nkb; ++it) {
-        const uint8_t* sA = smem + (it % STAGES) * STAGE;
-        const float* sS = reinterpret_cast<const float*>(sA + ROWS * ROWB);
+    const int ngroups = nkb / SG;
+    for (int it0 = 0; it0 < nkb; it0 += SG) static_for<SG>([&](auto sub_tag) {
+        constexpr int sub = decltype(sub_tag)::value;
+        const int it = it0 + sub;
+        // each iteration reads its own scales: without this the compiler
+        // merges a group's four scale reads and keeps them live across it
+        asm volatile("" ::: "memory");
+        int sb = (it % STAGES) * STAGE, nb = ((it + 1) % STAGES) * STAGE;
+        asm volatile("" : "+s"(sb), "+s"(nb));  // per iteration, as in issue_copies
+        const uint8_t* sA = smem + sb;
         // this k-block's scales: the A scale of each of the lane's tokens, the
         // weight scale of each of its 32-feature blocks (read before the
         // barrier below releases the buffer)
         float sa[TM], sw[TN];
+        if constexpr (GROUPED) {
+            const float* rs = reinterpret_cast<const float*>(ring + ((it0 / SG) & 1) * RING_SLOT);
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int t = wm * WTM + i * 32 + lrow;
-            sa[i] = sS[(t / SROWS) * 64 + t % SROWS];
-        }
+            for (int i = 0; i < TM; ++i) sa[i] = rs[(wm * WTM + i * 32 + lrow) * 4 + sub];
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int lr = wn * WTN + j * 32;
-            sw[j] = sS[SROWS + (MODE == kModeW13 ? (lr / 32) % 2 : lr / 128)];
+            for (int j = 0; j < TN; ++j) {
+                const int lr = wn * WTN + j * 32;
+                sw[j] = rs[(BM + (MODE == kModeW13 ? (lr / 32) % 2 : lr / 128)) * 4 + sub];
+            }
+        } else {
+            const float* sS = reinterpret_cast<const float*>(sA + ROWS * ROWB);
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int t = wm * WTM + i * 32 + lrow;
+                sa[i] = sS[(t / SROWS) * 64 + t % SROWS];
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int lr = wn * WTN + j * 32;
+                sw[j] = sS[SROWS + (MODE == kModeW13 ? (lr / 32) % 2 : lr / 128)];
+            }
         }
-        // step 0: step-1 reads, then this wave's copies of k-block
-        // it+STAGES-1 (buffer of k-block it-1, free since the last barrier)
+        // step 0: step-1 reads, then (first iteration of a group, SG = 4) the
+        // next group's scales into the other ring slot, last read in the
+        // previous group, and this wave's copies of k-block it+STAGES-1
+        // (buffer of k-block it-1, free since the last barrier); the last
+        // group copies itself again (same values), keeping the count fixed
         read_step(sA, 1, af[1], bfr[1]);
+        constexpr bool SCALE_COPY = GROUPED && sub == 0;
+        if constexpr (SCALE_COPY) {
+            const int nxt = it0 / SG + 1;
+            issue_scales(nxt < ngroups ? nxt : ngroups - 1);
+        }
         issue_copies(it + STAGES - 1, 0, COPIES);
         mfma_range(0, kMfma, af[0], bfr[0], true);
-        mix_sched<kMfma, kReads, PER_STAGE>();
+        mix_sched<kMfma, kReads, PER_STAGE + (SCALE_COPY ? 1 : 0)>();
         __builtin_amdgcn_sched_barrier(0);
         // step 1, split around the barrier that publishes k-block it+1
         constexpr int H = kMfma / 2;
@@ -217,9 +285,9 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
         __builtin_amdgcn_sched_group_barrier(0x008, H, 0);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage it landed
-        wait_later_stages();
+        wait_later_stages(sub_tag);
         __builtin_amdgcn_s_barrier();
-        read_step(smem + ((it + 1) % STAGES) * STAGE, 0, af[0], bfr[0]);
+        read_step(smem + nb, 0, af[0], bfr[0]);
         mfma_range(H, kMfma, af[1], bfr[1], false);
         mix_sched<kMfma - H, kReads, 0>();
         __builtin_amdgcn_sched_barrier(0);
@@ -232,7 +300,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = fmaf(blk[i][j][v], sc, acc[i][j][v]);
             }
-    }
+    });
     // no copy may still write LDS when the block ends or LDS is reused
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
