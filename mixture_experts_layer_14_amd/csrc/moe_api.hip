@@ -65,8 +65,9 @@ int check_params(const moe_params* p) {
     return MOE_OK;
 }
 
-moe::GroupedProblem problem(const moe_params* p) {
+moe::GroupedProblem problem(const moe_params* p, moe::TileTableKey* built = nullptr) {
     moe::GroupedProblem g;
+    g.built = built;
     g.dtype = p->weight_dtype;
     g.T = p->num_tokens;
     g.K = p->top_k;
@@ -213,12 +214,17 @@ int moe_quant_act_fp8(const moe_params* p, const void* hidden, uint8_t* q, float
                                             as_stream(stream)));
 }
 
-int moe_grouped_gemm_w13_act(const moe_params* p, const void* hidden, const float* hidden_scale,
-                             const void* w13, const float* w13_scale, const void* shared_w13,
-                             const float* shared_w13_scale, const int32_t* expert_offsets,
-                             const int32_t* sorted_slots, const float* topk_weights, void* act,
-                             float* act_scale, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The two GEMM entry points; `built` (moe_forward only) records the tile
+// table in the workspace across them.
+int w13_act(const moe_params* p, const void* hidden, const float* hidden_scale, const void* w13,
+            const float* w13_scale, const void* shared_w13, const float* shared_w13_scale,
+            const int32_t* expert_offsets, const int32_t* sorted_slots, const float* topk_weights,
+            void* act, float* act_scale, void* workspace, size_t workspace_bytes, void* stream,
+            moe::TileTableKey* built) {
     int st = check_params(p);
     if (st != MOE_OK) return st;
     if (p->num_tokens == 0) return MOE_OK;  // empty batch: nothing to do
@@ -229,18 +235,17 @@ int moe_grouped_gemm_w13_act(const moe_params* p, const void* hidden, const floa
                          (p->num_shared_experts && !shared_w13_scale)))
         return MOE_ERR_INVALID;
     if (!workspace || workspace_bytes < w13_scratch(p)) return MOE_ERR_WORKSPACE;
-    return hip_status(moe::launch_w13(problem(p), hidden, hidden_scale, w13, w13_scale, shared_w13,
+    return hip_status(moe::launch_w13(problem(p, built), hidden, hidden_scale, w13, w13_scale, shared_w13,
                                       shared_w13_scale, expert_offsets, sorted_slots,
                                       topk_weights, act, act_scale, workspace,
                                       as_stream(stream)));
 }
 
-int moe_grouped_gemm_w2_combine(const moe_params* p, const void* act, const float* act_scale,
-                                const void* w2, const float* w2_scale, const void* shared_w2,
-                                const float* shared_w2_scale, const int32_t* expert_offsets,
-                                const int32_t* sorted_slots, const int32_t* slot_to_row,
-                                const float* topk_weights, void* out, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+int w2_combine(const moe_params* p, const void* act, const float* act_scale, const void* w2,
+               const float* w2_scale, const void* shared_w2, const float* shared_w2_scale,
+               const int32_t* expert_offsets, const int32_t* sorted_slots,
+               const int32_t* slot_to_row, const float* topk_weights, void* out, void* workspace,
+               size_t workspace_bytes, void* stream, moe::TileTableKey* built) {
     int st = check_params(p);
     if (st != MOE_OK) return st;
     if (p->num_tokens == 0) return MOE_OK;  // empty batch: nothing to do
@@ -250,10 +255,36 @@ int moe_grouped_gemm_w2_combine(const moe_params* p, const void* act, const floa
     if (fp8_layer(p) && (!act_scale || !w2_scale || (p->num_shared_experts && !shared_w2_scale)))
         return MOE_ERR_INVALID;
     if (!workspace || workspace_bytes < w2_scratch(p)) return MOE_ERR_WORKSPACE;
-    return hip_status(moe::launch_w2_combine(problem(p), act, act_scale, w2, w2_scale, shared_w2,
+    return hip_status(moe::launch_w2_combine(problem(p, built), act, act_scale, w2, w2_scale, shared_w2,
                                              shared_w2_scale, expert_offsets, sorted_slots,
                                              slot_to_row, topk_weights, out, workspace,
                                              as_stream(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_grouped_gemm_w13_act(const moe_params* p, const void* hidden, const float* hidden_scale,
+                             const void* w13, const float* w13_scale, const void* shared_w13,
+                             const float* shared_w13_scale, const int32_t* expert_offsets,
+                             const int32_t* sorted_slots, const float* topk_weights, void* act,
+                             float* act_scale, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    return w13_act(p, hidden, hidden_scale, w13, w13_scale, shared_w13, shared_w13_scale,
+                   expert_offsets, sorted_slots, topk_weights, act, act_scale, workspace,
+                   workspace_bytes, stream, nullptr);
+}
+
+int moe_grouped_gemm_w2_combine(const moe_params* p, const void* act, const float* act_scale,
+                                const void* w2, const float* w2_scale, const void* shared_w2,
+                                const float* shared_w2_scale, const int32_t* expert_offsets,
+                                const int32_t* sorted_slots, const int32_t* slot_to_row,
+                                const float* topk_weights, void* out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    return w2_combine(p, act, act_scale, w2, w2_scale, shared_w2, shared_w2_scale, expert_offsets,
+                      sorted_slots, slot_to_row, topk_weights, out, workspace, workspace_bytes,
+                      stream, nullptr);
 }
 
 int moe_router_gemm(const moe_params* p, const void* hidden, const void* gate_w,
@@ -315,13 +346,14 @@ int moe_forward(const moe_params* p, const void* hidden, const float* router_log
     }
     void* act = ws + L.act;
     float* act_scale = fp8_layer(p) ? reinterpret_cast<float*>(ws + L.act_scale) : nullptr;
-    st = moe_grouped_gemm_w13_act(p, a1, a1_scale, w13, w13_scale, shared_w13, shared_w13_scale,
-                                  offsets, sorted, wts, act, act_scale, scratch, scratch_bytes,
-                                  stream);
+    // both GEMMs use the same scratch region, so w2 reuses w13's tile table
+    // when it would build the same one
+    moe::TileTableKey built;
+    st = w13_act(p, a1, a1_scale, w13, w13_scale, shared_w13, shared_w13_scale, offsets, sorted,
+                 wts, act, act_scale, scratch, scratch_bytes, stream, &built);
     if (st != MOE_OK) return st;
-    return moe_grouped_gemm_w2_combine(p, act, act_scale, w2, w2_scale, shared_w2, shared_w2_scale,
-                                       offsets, sorted, inv, wts, out, scratch, scratch_bytes,
-                                       stream);
+    return w2_combine(p, act, act_scale, w2, w2_scale, shared_w2, shared_w2_scale, offsets,
+                      sorted, inv, wts, out, scratch, scratch_bytes, stream, &built);
 }
 
 }  // extern "C"

@@ -515,10 +515,16 @@ static void build_tiles(const GroupedProblem& p, const int32_t* offsets, int BM,
     GroupUnit* units = tail_rows > 0 ? reinterpret_cast<GroupUnit*>(static_cast<uint8_t*>(ws) + 256 +
                                                                     tile_table_bytes(p))
                                      : nullptr;
-    build_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, p.E, p.shared ? static_cast<int32_t>(p.T) : 0,
-                                               static_cast<int32_t>(p.T * p.K), BM, MOE_TILE_GM,
-                                               tail_rows, tiles, num_tiles, units, num_units,
-                                               split_nn, split);
+    const TileTableKey key{ws, offsets, BM, tail_rows, split_nn};
+    const TileTableKey* b = p.built;
+    if (!b || b->ws != key.ws || b->offsets != key.offsets || b->bm != key.bm ||
+        b->tail_rows != key.tail_rows || b->split_nn != key.split_nn) {
+        build_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, p.E, p.shared ? static_cast<int32_t>(p.T) : 0,
+                                                   static_cast<int32_t>(p.T * p.K), BM, MOE_TILE_GM,
+                                                   tail_rows, tiles, num_tiles, units, num_units,
+                                                   split_nn, split);
+        if (p.built) *p.built = key;
+    }
     g.split = split_nn > 0 ? split : nullptr;
     g.tiles = tiles;
     g.num_tiles = num_tiles;

@@ -38,6 +38,15 @@ hipError_t launch_align(const int32_t* ids, int64_t n, int E, int32_t* offsets,
                         hipStream_t stream);
 
 // Grouped GEMM problem shared by the two expert GEMMs.
+// What the tile table at the start of a GEMM workspace was last built for.
+// moe_forward hands one record to both of its GEMM calls, so the second skips
+// a build identical to the first (same workspace, offsets and tile plan).
+struct TileTableKey {
+    const void* ws = nullptr;
+    const int32_t* offsets = nullptr;
+    int bm = 0, tail_rows = 0, split_nn = 0;
+};
+
 struct GroupedProblem {
     int dtype;             // MOE_DTYPE_* of A and B (F32, BF16, FP8_E4M3)
     int64_t T;             // tokens
@@ -52,6 +61,8 @@ struct GroupedProblem {
     float alpha = 1.0f;
     float limit = 0.0f;
     int weight_in = 0;
+    // record of the table in the workspace (null: always build)
+    TileTableKey* built = nullptr;
 };
 
 // Scratch bytes of one grouped GEMM launch (tile table).
