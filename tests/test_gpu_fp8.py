@@ -128,3 +128,39 @@ def test_full_size_dsv3_fp8():
     assert err <= U.TOL["fp8"]
     del layer, inp
     torch.cuda.empty_cache()
+
+
+def _offset_view(t: torch.Tensor) -> torch.Tensor:
+    """A tensor like `t` whose storage starts 4 bytes past a 16-byte boundary."""
+    buf = torch.empty(t.numel() + 4, dtype=t.dtype, device=t.device)
+    base = (16 - buf.data_ptr() % 16) % 16 // 4  # elements to the next 16-byte boundary
+    v = buf[base + 1:base + 1 + t.numel()].view(t.shape)
+    assert v.data_ptr() % 16 == 4
+    return v
+
+
+def test_unaligned_scale_arrays():
+    """The fp8 GEMMs copy the block scales once per group of four k-blocks
+    only when the scale arrays are 16-byte aligned; input and activation
+    scales handed over at a 4-byte offset take the per-k-block copies.  The
+    arithmetic is the same, so the layer output is bitwise the same."""
+    cfg = MC("fp8_aligned", E=8, K=2, H=512, I=512, T=77, w_dtype="fp8", shared=1, seed=25,
+             weight_seed=25)  # H and I: four k-blocks, so both GEMMs take the grouped copies
+    T = cfg.T
+    print("case", cfg.name, "T", T, flush=True)
+    inp = synth.make_inputs(cfg, T, device="cuda")
+    layer = FusedMoE(params_for(cfg, T), inp)
+    st = Stages(layer, T)
+    bias = inp.get("e_score_correction_bias")
+    out_a = st.run(inp["hidden"], inp["router_logits"], bias).clone()
+    act_a = st.act.clone()
+    st.xs = _offset_view(st.xs)
+    st.act_scale = _offset_view(st.act_scale)
+    out_b = st.run(inp["hidden"], inp["router_logits"], bias).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(st.act, act_a), "act codes differ between the two scale paths"
+    assert torch.equal(out_a, out_b), "layer output differs between the two scale paths"
+    ref = O.moe_forward_tokens(U.oracle_layer(cfg, inp, T), range(T), nthreads=8)
+    err = U.rel_err(U.out_to_f64(out_b), ref)
+    print("  max|err|/max|ref| = %.3e" % err, flush=True)
+    assert err <= U.TOL["fp8"]
