@@ -122,10 +122,13 @@ __global__ __launch_bounds__(64) void align_scatter_kernel(const int32_t* __rest
 
 // Whole permutation in one block for small slot counts (decode and
 // Mixtral-size prefill batches):
-// 16 waves each own a contiguous run of slots; per-wave expert counts in LDS,
-// one scan gives the offsets and every wave's starting row per expert, then
-// each wave scatters its run in slot order (the same stable result as the
-// three-kernel path, in one launch instead of three).
+// 16 waves each own a contiguous run of slots, loaded once into registers;
+// per-wave expert counts in LDS, one scan gives the offsets and every wave's
+// starting row per expert, then each wave scatters its run in slot order
+// (the same stable result as the three-kernel path, in one launch instead of
+// three).  Within each 64 slots, the lanes holding one expert find each
+// other by ballots over the id bits; the last of them adds their number to
+// the wave's count (no atomics) and, in the scatter, advances the cursor.
 constexpr int kAlignSmallWaves = 16;
 // Slot counts up to this run as the single block (measured: 8192 slots,
 // Mixtral-shape prefill, one launch instead of three saves ~8 us; at 65536
@@ -134,6 +137,9 @@ constexpr int kAlignSmallWaves = 16;
 #define MOE_ALIGN_SMALL_MAX 16384
 #endif
 constexpr int64_t kAlignSmallMax = MOE_ALIGN_SMALL_MAX;
+// ids per lane when a wave's run is held in registers
+constexpr int kAlignSmallPerLane =
+    static_cast<int>((kAlignSmallMax + kAlignSmallWaves * kWave - 1) / (kAlignSmallWaves * kWave));
 
 __global__ __launch_bounds__(kAlignSmallWaves * kWave) void align_small_kernel(
     const int32_t* __restrict__ ids, int64_t n, int E, int32_t* __restrict__ offsets,
@@ -144,11 +150,38 @@ __global__ __launch_bounds__(kAlignSmallWaves * kWave) void align_small_kernel(
     const int chunk = static_cast<int>((n + kAlignSmallWaves - 1) / kAlignSmallWaves);
     const int begin = w * chunk;
     const int end = begin + chunk < n ? begin + chunk : static_cast<int>(n);
+    // the wave's ids, slot begin + 64 j + lane in my[j] (-1 past the run)
+    int32_t my[kAlignSmallPerLane];
+#pragma unroll
+    for (int j = 0; j < kAlignSmallPerLane; ++j) {
+        const int i = begin + j * kWave + lane;
+        my[j] = i < end ? ids[i] : -1;
+    }
+    // lanes of the same 64 holding the same expert (or, for lanes whose id
+    // is out of range, the other such lanes); bits above E-1 are all zero
+    const int nbits = E > 1 ? 32 - __builtin_clz(static_cast<unsigned>(E - 1)) : 0;
+    auto same_expert = [&](int e, bool valid) {
+        uint64_t same = __ballot(valid);
+        same = valid ? same : ~same;
+        for (int bit = 0; bit < nbits; ++bit) {
+            const bool on = (e >> bit) & 1;
+            const uint64_t bal = __ballot(on);
+            same &= on ? bal : ~bal;
+        }
+        return same;
+    };
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
     for (int e = lane; e < E; e += kWave) cnt[w][e] = 0;
     __syncthreads();
-    for (int i = begin + lane; i < end; i += kWave) {
-        const int e = ids[i];
-        if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&cnt[w][e], 1);
+#pragma unroll
+    for (int j = 0; j < kAlignSmallPerLane; ++j) {
+        if (begin + j * kWave >= end) break;  // wave-uniform
+        const int e = my[j];
+        const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(E);
+        const uint64_t same = same_expert(e, valid);
+        // the last lane of each expert's group adds the group's size; a
+        // wave's LDS accesses complete in order
+        if (valid && __popcll(same & ~lt_mask) == 1) cnt[w][e] += __popcll(same);
     }
     __syncthreads();
     // expert `tid`: its per-wave counts become running starts within the
@@ -169,20 +202,13 @@ __global__ __launch_bounds__(kAlignSmallWaves * kWave) void align_small_kernel(
     }
     if (tid == 0) offsets[E] = total;
     __syncthreads();
-    const uint64_t lt_mask = (1ull << lane) - 1ull;
-    for (int b0 = begin; b0 < end; b0 += kWave) {
-        const int i = b0 + lane;
-        int e = i < end ? ids[i] : -1;
-        const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(E);
-        if (!valid) e = kAlignMaxExperts;  // matches only other invalid lanes
-        uint64_t same = __ballot(valid);
-        same = valid ? same : ~same;
 #pragma unroll
-        for (int bit = 0; bit < 10; ++bit) {
-            const bool on = (e >> bit) & 1;
-            const uint64_t bal = __ballot(on);
-            same &= on ? bal : ~bal;
-        }
+    for (int j = 0; j < kAlignSmallPerLane; ++j) {
+        if (begin + j * kWave >= end) break;  // wave-uniform
+        const int i = begin + j * kWave + lane;
+        const int e = my[j];
+        const bool valid = static_cast<unsigned>(e) < static_cast<unsigned>(E);
+        const uint64_t same = same_expert(e, valid);
         const int before = __popcll(same & lt_mask);
         const int total = __popcll(same);
         int32_t row = 0;
