@@ -27,9 +27,12 @@ __device__ __forceinline__ int wave_index(int tid) {
 }
 
 // Order-preserving map of an fp32 value onto uint32 (larger float -> larger
-// integer; -inf maps above 0, so 0 is below every real key).
+// integer; -inf maps above 0, so 0 is below every real key).  -0 and +0 are
+// equal values and get one key, so they tie like any other equal keys (and
+// a selection then takes the lower index).
 __device__ __forceinline__ uint32_t ordered_bits(float f) {
     uint32_t u = __float_as_uint(f);
+    u = u == 0x80000000u ? 0u : u;
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 

@@ -264,6 +264,20 @@ def check_route_ties(lib_=None):
     ids, _ = O.route(logits, 2, scoring=O.SIGMOID, n_group=4, topk_group=1,
                      bias=np.zeros(8, np.float32), lib_=lib_)
     assert ids[0].tolist() == [2, 3], ids
+    # -0 and +0 are the same value (IEEE 754 equality), so they tie and the
+    # lower index wins whichever sign it carries
+    logits = np.array([[-1.0, -0.0, 0.0, -2.0, -0.0, 0.0]], np.float32)
+    assert np.signbit(logits[0, 1]) and not np.signbit(logits[0, 2])
+    ids, w = O.route(logits, 4, lib_=lib_)
+    assert ids[0].tolist() == [1, 2, 4, 5], ids
+    assert np.all(w[0] == 0.25), w  # four equal probabilities, renormalised
+    ids, _ = O.route(logits, 1, renormalize=False, lib_=lib_)
+    assert ids[0].tolist() == [1], ids
+    # groups scored by their largest key (no bias): group 0's best is -0,
+    # group 1's +0; the tie keeps the lower group
+    logits = np.array([[-0.0, -3.0, 0.0, -1.0, -5.0, -4.0]], np.float32)
+    ids, _ = O.route(logits, 2, n_group=3, topk_group=1, lib_=lib_)
+    assert ids[0].tolist() == [0, 1], ids
 
 
 def check_route_grouped_bruteforce(lib_=None):

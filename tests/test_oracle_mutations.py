@@ -40,7 +40,17 @@ MUTANTS = {
                              "gscore[j] = best1;"),
     "tie_to_higher": ("if (eligible[e] && !taken[e] && (be < 0 || key[e] > key[be]))",
                       "if (eligible[e] && !taken[e] && (be < 0 || key[e] >= key[be]))"),
-    "strided_groups": ("eligible[e] = gkeep[e / per];", "eligible[e] = gkeep[e % G];"),
+    # a total order that ranks -0 below +0 (as an integer key of the raw
+    # bits would), for experts and for groups
+    "neg_zero_below_pos_zero": (
+        "if (eligible[e] && !taken[e] && (be < 0 || key[e] > key[be]))",
+        "if (eligible[e] && !taken[e] && (be < 0 || key[e] > key[be] ||"
+        " (key[e] == key[be] && signbit(key[be]) && !signbit(key[e]))))"),
+    "neg_zero_group_below_pos_zero": (
+        "if (!gkeep[j] && (bj < 0 || gscore[j] > gscore[bj]))",
+        "if (!gkeep[j] && (bj < 0 || gscore[j] > gscore[bj] ||"
+        " (gscore[j] == gscore[bj] && signbit(gscore[bj]) && !signbit(gscore[j]))))"),
+    "strided_groups":("eligible[e] = gkeep[e / per];", "eligible[e] = gkeep[e % G];"),
     "unstable_permutation": ("int64_t r = cursor[ids[i]]++;",
                              "int64_t r = offsets[ids[i]] + offsets[ids[i] + 1] - 1 - cursor[ids[i]]++;"),
     "shared_scaled_by_rsf": ("            out[h] += s->y[h];",
