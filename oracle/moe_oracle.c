@@ -338,6 +338,8 @@ static double or_silu_a(double z, double a) { return z / (1.0 + exp(-a * z)); }
  * output dimension per _load_w13, w2 = down; activation "silu" with
  * is_act_and_mul; [SGL-DSV2] DeepseekV2MLP gate_up_proj -> SiluAndMul ->
  * down_proj):
+ * I is this expert's intermediate size (the routed experts' I, or the
+ * shared expert's Is):
  *   gu  = W13 x            (2I values; rows [0, I) gate, [I, 2I) up)
  *   act = silu(gu[0:I]) * gu[I:2I]
  *   y   = W2 act           (H values)
@@ -349,12 +351,12 @@ static double or_silu_a(double z, double a) { return z / (1.0 + exp(-a * z)); }
  *   non-gated: W13 is [I, H] and act = silu_a(W13 x);
  *   gated with limit L > 0: g = min(g, L), u = min(max(u, -L), L), then
  *   act = silu_a(g) * u;  silu_a as above. */
-static void or_expert_mlp(const or_layer *L, const void *w13, const float *s13,
-                          const void *w2, const float *s2, const double *x,
-                          double *gu, double *act, float *a32, uint8_t *aq,
-                          float *as, double *y)
+static void or_expert_mlp(const or_layer *L, int64_t I, const void *w13,
+                          const float *s13, const void *w2, const float *s2,
+                          const double *x, double *gu, double *act, float *a32,
+                          uint8_t *aq, float *as, double *y)
 {
-    int64_t H = L->H, I = L->I;
+    int64_t H = L->H;
     int64_t N1 = L->gated ? 2 * I : I;
     double L_ = L->clamp_limit;
     for (int64_t n = 0; n < N1; n++) {
@@ -397,9 +399,16 @@ typedef struct {
     uint8_t *xq, *aq;
 } or_scratch;
 
+/* Intermediate size of the shared expert ([SGL-DSV2] DeepseekV2MoE builds
+ * it as a DeepseekV2MLP of moe_intermediate_size * n_shared_experts). */
+static int64_t or_shared_I(const or_layer *L)
+{
+    return L->shared_I > 0 ? L->shared_I : L->I;
+}
+
 static int or_scratch_alloc(const or_layer *L, or_scratch *s)
 {
-    int64_t H = L->H, I = L->I;
+    int64_t H = L->H, I = L->I > or_shared_I(L) ? L->I : or_shared_I(L);
     s->x = malloc(sizeof(double) * H);
     s->xw = malloc(sizeof(double) * H);
     s->gu = malloc(sizeof(double) * 2 * I);
@@ -423,6 +432,7 @@ static void or_scratch_free(or_scratch *s)
 
 /* The layer output of one token t into out[0:H]:
  *   out = sum_k w_k * MLP_{id_k}(x_t)  +  MLP_shared(x_t)
+ * (MLP_shared of intermediate size Is)
  * where routing gives (id_k, w_k) with rsf already folded into w_k, and the
  * shared expert is added with weight 1, never scaled by rsf ([SGL-DSV2]
  * DeepseekV2MoE: shared output plus routed output times
@@ -464,16 +474,16 @@ static int or_token(const or_layer *L, int64_t t, or_scratch *s, double *out)
                 s->xw[h] = w[k] * s->x[h];
             xin = s->xw;
         }
-        or_expert_mlp(L, L->w13[e], L->w13_scale ? L->w13_scale[e] : NULL,
+        or_expert_mlp(L, L->I, L->w13[e], L->w13_scale ? L->w13_scale[e] : NULL,
                       L->w2[e], L->w2_scale ? L->w2_scale[e] : NULL, xin,
                       s->gu, s->act, s->a32, s->aq, s->as, s->y);
         for (int64_t h = 0; h < H; h++)
             out[h] += (L->weight_on_input ? 1.0 : w[k]) * s->y[h];
     }
     if (L->shared_w13) {
-        or_expert_mlp(L, L->shared_w13, L->shared_w13_scale, L->shared_w2,
-                      L->shared_w2_scale, s->x, s->gu, s->act, s->a32, s->aq,
-                      s->as, s->y);
+        or_expert_mlp(L, or_shared_I(L), L->shared_w13, L->shared_w13_scale,
+                      L->shared_w2, L->shared_w2_scale, s->x, s->gu, s->act,
+                      s->a32, s->aq, s->as, s->y);
         for (int64_t h = 0; h < H; h++)
             out[h] += s->y[h];
     }
@@ -515,7 +525,9 @@ int or_moe_forward_tokens(const or_layer *L, int64_t ntok,
     int status = 0;
     if (L->E < 1 || L->E > OR_MAX_EXPERTS || L->K < 1 || L->K > L->E)
         return -1;
-    if (L->act_fp8 && (L->H % 128 || L->I % 128))
+    if (L->act_fp8 && (L->H % 128 || L->I % 128 || or_shared_I(L) % 128))
+        return -1;
+    if (L->shared_I < 0)
         return -1;
     /* variants outside the pages' combinations: a clamp needs the gated
      * form, and the fp8 paths quantise x itself, so they take no input

@@ -31,9 +31,9 @@ typedef struct {
     const float *const *w13_scale;/* E pointers to [2I/128, H/128] or NULL */
     const void *const *w2;        /* E pointers to [H, I] */
     const float *const *w2_scale; /* E pointers to [H/128, I/128] or NULL */
-    const void *shared_w13;       /* [2I, H] or NULL */
+    const void *shared_w13;       /* [2Is, H] or NULL */
     const float *shared_w13_scale;
-    const void *shared_w2;        /* [H, I] or NULL */
+    const void *shared_w2;        /* [H, Is] or NULL */
     const float *shared_w2_scale;
     /* activation variants (defaults: gated = 1, act_alpha = 1, clamp_limit =
      * 0, weight_on_input = 0 give the plain SiLU-and-mul layer) */
@@ -41,6 +41,8 @@ typedef struct {
     double act_alpha;             /* silu_a(z) = z * sigmoid(act_alpha * z)   */
     double clamp_limit;           /* > 0: gate <= L and |up| <= L (gated)     */
     int weight_on_input;          /* 1: sum_k MLP(w_k x) instead of w_k MLP(x) */
+    int64_t shared_I;             /* Is, intermediate size of the shared      */
+                                  /* expert; 0 means I                        */
 } or_layer;
 
 double or_bf16_to_f64(uint16_t v);

@@ -56,6 +56,7 @@ class _Layer(ctypes.Structure):
         ("shared_w2", ctypes.c_void_p), ("shared_w2_scale", ctypes.c_void_p),
         ("gated", ctypes.c_int), ("act_alpha", ctypes.c_double),
         ("clamp_limit", ctypes.c_double), ("weight_on_input", ctypes.c_int),
+        ("shared_I", ctypes.c_int64),
     ]
 
 
@@ -204,7 +205,8 @@ def moe_forward_tokens(layer: dict, tokens, nthreads: int = 1, lib_=None) -> np.
     ``layer`` keys: T E K H I, scoring, renormalize, n_group, topk_group,
     routed_scaling_factor, x_dtype, w_dtype, act_fp8, hidden, logits, bias,
     w13, w13_scale, w2, w2_scale, shared_w13, shared_w13_scale, shared_w2,
-    shared_w2_scale, and the activation variants gated (True), act_alpha
+    shared_w2_scale, shared_I (the shared expert's intermediate size; 0 or
+    absent: I), and the activation variants gated (True), act_alpha
     (1.0), clamp_limit (0.0: none), weight_on_input (False).  Weight entries
     are [E, ...] arrays or dicts e -> array (only the experts the listed
     tokens use need to be present).
@@ -235,6 +237,7 @@ def moe_forward_tokens(layer: dict, tokens, nthreads: int = 1, lib_=None) -> np.
     st.act_alpha = float(layer.get("act_alpha", 1.0))
     st.clamp_limit = float(layer.get("clamp_limit", 0.0))
     st.weight_on_input = int(bool(layer.get("weight_on_input", False)))
+    st.shared_I = int(layer.get("shared_I", 0))
     st.hidden = _ptr(arr("hidden"))
     st.logits = _ptr(arr("logits", np.float32))
     st.bias = _ptr(arr("bias", np.float32))

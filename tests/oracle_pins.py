@@ -97,8 +97,9 @@ def brute_route(row, K, *, bias=None, scoring=O.SOFTMAX, renormalize=True,
 
 def make_layer(E, K, H, I, T, *, w_dtype=O.F32, x_dtype=O.F32, seed=0, scoring=O.SOFTMAX,
                renormalize=True, n_group=0, topk_group=0, rsf=1.0, bias=False,
-               shared=False, identical=False, act_fp8=False, w_std=0.05):
-    """A small random layer as oracle arrays plus torch float64 copies of what it encodes."""
+               shared=False, identical=False, act_fp8=False, w_std=0.05, shared_I=0):
+    """A small random layer as oracle arrays plus torch float64 copies of what
+    it encodes; the shared expert has intermediate size shared_I (0: I)."""
     g = torch.Generator().manual_seed(seed)
     x = torch.randn(T, H, generator=g)
     logits = torch.randn(T, E, generator=g).numpy().astype(np.float32)
@@ -107,12 +108,14 @@ def make_layer(E, K, H, I, T, *, w_dtype=O.F32, x_dtype=O.F32, seed=0, scoring=O
     if identical:
         w13[:] = w13[0]
         w2[:] = w2[0]
-    sw13 = torch.randn(2 * I, H, generator=g) * w_std
-    sw2 = torch.randn(H, I, generator=g) * w_std
+    Is = shared_I or I
+    sw13 = torch.randn(2 * Is, H, generator=g) * w_std
+    sw2 = torch.randn(H, Is, generator=g) * w_std
     b = (torch.randn(E, generator=g) * 0.01).numpy().astype(np.float32) if bias else None
     L = dict(T=T, E=E, K=K, H=H, I=I, scoring=scoring, renormalize=renormalize,
              n_group=n_group, topk_group=topk_group, routed_scaling_factor=rsf,
-             x_dtype=x_dtype, w_dtype=w_dtype, act_fp8=act_fp8, logits=logits, bias=b)
+             x_dtype=x_dtype, w_dtype=w_dtype, act_fp8=act_fp8, logits=logits, bias=b,
+             shared_I=shared_I)
     ref = {}
     if x_dtype == O.F32:
         L["hidden"] = x.numpy().astype(np.float32)
@@ -403,20 +406,24 @@ def check_layer_token_permutation(lib_=None):
 
 
 def check_layer_shared(lib_=None):
-    L, ref = make_layer(8, 2, 128, 128, 5, seed=7, shared=True, scoring=O.SIGMOID,
-                        n_group=4, topk_group=2, bias=True, rsf=2.5)
-    with_shared = _forward(L, lib_=lib_)
-    L2 = {k: v for k, v in L.items() if not k.startswith("shared")}
-    without = _forward(L2, lib_=lib_)
-    _close(with_shared - without, dense_swiglu(ref["x"], ref["sw13"], ref["sw2"]).numpy(), 1e-11,
-           "shared expert adds its dense MLP with weight 1 (not rsf)")
+    # the shared expert is a dense gated MLP of its own intermediate size Is
+    # (the SGLang DeepseekV2MoE builds it with moe_intermediate_size *
+    # n_shared_experts), added with weight 1
+    for Is in (0, 384):
+        L, ref = make_layer(8, 2, 128, 128, 5, seed=7, shared=True, scoring=O.SIGMOID,
+                            n_group=4, topk_group=2, bias=True, rsf=2.5, shared_I=Is)
+        with_shared = _forward(L, lib_=lib_)
+        L2 = {k: v for k, v in L.items() if not k.startswith("shared")}
+        without = _forward(L2, lib_=lib_)
+        _close(with_shared - without, dense_swiglu(ref["x"], ref["sw13"], ref["sw2"]).numpy(), 1e-11,
+               "shared expert (Is=%d) adds its dense MLP with weight 1 (not rsf)" % Is)
 
 
 def check_layer_fp8(lib_=None):
     """fp8 layer rebuilt with torch's e4m3 encoder and float32 scale arithmetic."""
     L, ref = make_layer(4, 2, 256, 256, 6, seed=8, w_dtype=O.E4M3, x_dtype=O.BF16, act_fp8=True,
                         shared=True, scoring=O.SIGMOID, n_group=2, topk_group=1, bias=True,
-                        rsf=2.5)
+                        rsf=2.5, shared_I=512)
     out = _forward(L, lib_=lib_)
 
     def q128(v64):  # per-row group-128 quantise-dequantise in float32 with torch's encoder

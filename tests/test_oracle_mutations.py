@@ -55,6 +55,8 @@ MUTANTS = {
                              "int64_t r = offsets[ids[i]] + offsets[ids[i] + 1] - 1 - cursor[ids[i]]++;"),
     "shared_scaled_by_rsf": ("            out[h] += s->y[h];",
                              "            out[h] += L->routed_scaling_factor * s->y[h];"),
+    "shared_uses_routed_I": ("or_expert_mlp(L, or_shared_I(L), L->shared_w13",
+                             "or_expert_mlp(L, L->I, L->shared_w13"),
     "combine_wrong_weight": ("(L->weight_on_input ? 1.0 : w[k]) * s->y[h];",
                              "(L->weight_on_input ? 1.0 : w[0]) * s->y[h];"),
     "w13_transposed": ("acc += x[h] * or_weight(w13, s13, L->w_dtype, H, n, h);",
