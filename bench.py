@@ -1,13 +1,18 @@
 """Benchmark of the fused MoE layer forward on one MI355X.
 
-Default workload: the Mixtral-shape layer (E=8, top_k=2, hidden=4096,
-intermediate=14336, bf16 weights, softmax + renormalize) at prefill size
-T=4096 tokens, with the decode-size T=32 measured beside it.  A step is one
-pass of the whole layer (routing, permutation, w13 + SiLU-and-mul, w2 +
-weighted combine) over one batch of synthetic inputs already resident in
-HBM.  Prints ONE JSON line.
+Default workload: the largest layer that fits one GPU, the DeepSeek-V3-shape
+MoE block of the SGLang page "srt/models/deepseek_v2.py" (DeepseekV2MoE:
+E=256 routed experts, top_k=8, hidden=7168, moe_intermediate_size=2048,
+sigmoid scoring with e_score_correction_bias, grouped top-k 8/4,
+routed_scaling_factor 2.5) with bf16 weights at prefill size T=8192 tokens,
+and its decode size T=64 beside it.  A step is one pass of the whole layer
+(routing, permutation, w13 + SiLU-and-mul, w2 + weighted combine) over one
+batch of synthetic inputs already resident in HBM.  Every other
+configuration (tiny, Mixtral-shape, Qwen-style, DeepSeek-V3 fp8 with its
+shared expert) is timed beside it under "configs".  Prints ONE JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--config mixtral] [--cpu-sample N]
+    python bench.py [--steps K] [--warmup W] [--config dsv3] [--cpu-sample N]
+    python bench.py --profile-config NAME   # only NAME's forward, for counter runs
 """
 from __future__ import annotations
 
@@ -38,16 +43,20 @@ def algorithmic_bytes(cfg, T, active_experts):
     """Weights of the experts that received rows (+ fp8 scales, + shared
     expert), hidden in, out, router logits, routing ids and weights."""
     wb = _weight_bytes(cfg)
-    per_expert = 3 * cfg.H * cfg.I * wb
-    if cfg.fp8:
-        per_expert += (2 * cfg.I // 128) * (cfg.H // 128) * 4 + (cfg.H // 128) * (cfg.I // 128) * 4
+
+    def mlp_bytes(I):
+        b = 3 * cfg.H * I * wb
+        if cfg.fp8:
+            b += (2 * I // 128) * (cfg.H // 128) * 4 + (cfg.H // 128) * (I // 128) * 4
+        return b
+
     act_b = 4 if cfg.act_dtype == "f32" else 2
-    return (per_expert * (active_experts + cfg.shared) + 2 * T * cfg.H * act_b
-            + T * cfg.E * 4 + T * cfg.K * 8)
+    return (mlp_bytes(cfg.I) * active_experts + mlp_bytes(cfg.Is) * cfg.shared
+            + 2 * T * cfg.H * act_b + T * cfg.E * 4 + T * cfg.K * 8)
 
 
 def w13_flops(cfg, T):
-    return 4.0 * T * (cfg.K + cfg.shared) * cfg.H * cfg.I
+    return 4.0 * T * cfg.H * (cfg.K * cfg.I + cfg.shared * cfg.Is)
 
 
 def w13_bytes(cfg, T, active_experts):
@@ -55,43 +64,80 @@ def w13_bytes(cfg, T, active_experts):
     that received rows (+ block scales), each token's hidden row once, and the
     activation rows written."""
     wb = _weight_bytes(cfg)
-    per_expert = 2 * cfg.I * cfg.H * wb
-    if cfg.fp8:
-        per_expert += (2 * cfg.I // 128) * (cfg.H // 128) * 4
+
+    def w13_of(I):
+        b = 2 * I * cfg.H * wb
+        if cfg.fp8:
+            b += (2 * I // 128) * (cfg.H // 128) * 4
+        return b
+
     act_b = 1 if cfg.fp8 else (4 if cfg.act_dtype == "f32" else 2)
     x_b = 4 if cfg.act_dtype == "f32" else 2
-    return (per_expert * (active_experts + cfg.shared) + T * cfg.H * x_b
-            + T * (cfg.K + cfg.shared) * cfg.I * act_b)
+    return (w13_of(cfg.I) * active_experts + w13_of(cfg.Is) * cfg.shared + T * cfg.H * x_b
+            + T * (cfg.K * cfg.I + cfg.shared * cfg.Is) * act_b)
 
 
-def time_layer(cfg, T, steps, warmup):
+def _stats(ms):
+    ms = np.asarray(ms, np.float64)
+    return {"median": float(np.median(ms)), "min": float(np.min(ms)), "mean": float(np.mean(ms))}
+
+
+def kernel_roofline(flops, byts, seconds, peak_tflops):
+    """Roofline of one kernel from its algorithmic FLOPs and bytes: the bound
+    is whichever takes longer at the published peaks; `frac` is the achieved
+    rate of that resource over its peak (= the attainable-roofline fraction
+    max(F/P, B/BW) / t), and both fractions are reported."""
+    t_f = flops / (peak_tflops * 1e12)
+    t_b = byts / (PEAK_HBM_GBS * 1e9)
+    tflops = flops / seconds / 1e12
+    gbs = byts / seconds / 1e9
+    if t_b >= t_f:
+        r = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        r = {"bound": "mfma", "achieved": tflops, "peak": peak_tflops, "unit": "TFLOP/s"}
+    r["frac"] = r["achieved"] / r["peak"]
+    r.update({"mfma_frac": tflops / peak_tflops, "hbm_frac": gbs / PEAK_HBM_GBS,
+              "attainable_frac": max(t_f, t_b) / seconds, "algorithmic_flops": flops,
+              "algorithmic_bytes": byts})
+    return r
+
+
+def time_layer(cfg, inp, steps, warmup):
     """Time `steps` passes of the whole layer through the library's entry
-    points, with HIP events around the w13 GEMM on the stream it runs on."""
+    points (wall clock around exactly `steps` steps, synchronised on both
+    sides), with HIP events on the launch stream around every step and
+    around the w13 GEMM; then the product entry point moe_forward alone."""
     import torch
 
-    from mixture_experts_layer_14_amd import synth
     from mixture_experts_layer_14_amd.layer import FusedMoE, Stages, params_for
 
-    inp = synth.make_inputs(cfg, T, device="cuda")
+    T = cfg.T
     layer = FusedMoE(params_for(cfg, T), inp)
     st = Stages(layer, T)
     hidden, logits = inp["hidden"], inp["router_logits"]
     bias = inp.get("e_score_correction_bias")
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+
+    def events(n):
+        return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+    s0, s1, w0, w1 = events(steps), events(steps), events(steps), events(steps)
 
     def step(i=None):
+        if i is not None:
+            s0[i].record(stream)
         st.topk(logits, bias)
         st.align()
         if st.xq is not None:
             st.quant(hidden)
         if i is not None:
-            ev[i][0].record(stream)
+            w0[i].record(stream)
         st.w13(hidden)
         if i is not None:
-            ev[i][1].record(stream)
+            w1[i].record(stream)
         st.w2()
+        if i is not None:
+            s1[i].record(stream)
 
     for _ in range(warmup):
         step()
@@ -101,22 +147,28 @@ def time_layer(cfg, T, steps, warmup):
         step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    w13_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    step_ms = [a.elapsed_time(b) for a, b in zip(s0, s1)]
+    w13_ms = [a.elapsed_time(b) for a, b in zip(w0, w1)]
     active = int((st.offsets[1:] - st.offsets[:-1] > 0).sum().item())
     # the product entry point (one call for the whole layer), timed alone
     out = torch.empty_like(st.out)
+    f0, f1 = events(steps), events(steps)
     for _ in range(max(1, warmup)):
         layer.forward(hidden, logits, bias, out=out)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    for _ in range(steps):
+    for i in range(steps):
+        f0[i].record(stream)
         layer.forward(hidden, logits, bias, out=out)
+        f1[i].record(stream)
     torch.cuda.synchronize()
-    fwd_ms = (time.perf_counter() - t1) / steps * 1e3
-    del layer, st, inp
+    fwd_wall = (time.perf_counter() - t1) / steps * 1e3
+    fwd_ms = [a.elapsed_time(b) for a, b in zip(f0, f1)]
+    del layer, st, out
     torch.cuda.empty_cache()
-    return {"ms_per_step": elapsed / steps * 1e3, "w13_ms": w13_ms, "active_experts": active,
-            "forward_ms_per_step": fwd_ms}
+    return {"ms_per_step": elapsed / steps * 1e3, "step_ms": _stats(step_ms),
+            "w13_ms": _stats(w13_ms), "active_experts": active,
+            "forward_ms_per_step": fwd_wall, "forward_ms": _stats(fwd_ms)}
 
 
 def time_router(cfg, T, gate_dtype, steps, warmup):
@@ -293,7 +345,7 @@ def cpu_sample(cfg, inp, tokens):
              w_dtype={"f32": O.F32, "bf16": O.BF16, "fp8": O.E4M3}[cfg.w_dtype], act_fp8=cfg.fp8,
              hidden=bits(inp["hidden"]), logits=logits, bias=bias,
              w13=per_expert("w13"), w2=per_expert("w2"), w13_scale=per_expert("w13_scale"),
-             w2_scale=per_expert("w2_scale"))
+             w2_scale=per_expert("w2_scale"), shared_I=cfg.shared_I if cfg.shared else 0)
     if cfg.shared:
         for k in ("shared_w13", "shared_w2", "shared_w13_scale", "shared_w2_scale"):
             L[k] = bits(inp.get(k))
@@ -310,10 +362,11 @@ PER_CONFIG = [("tiny", 64), ("mixtral_decode", 8), ("mixtral", 8), ("qwen", 32),
               ("dsv3_decode", 4), ("dsv3", 4), ("dsv3_fp8", 4)]
 
 
-def per_config(steps, warmup, peaks, with_cpu):
-    """Every configuration through moe_forward: tokens/s, TFLOP/s, GB/s of
-    algorithmic bytes, their fractions of the published and the measured
-    peaks, and the attainable-roofline fraction max(F/P, B/BW) / t."""
+def per_config(steps, warmup, peaks, with_cpu, names=None):
+    """Every configuration through moe_forward: median and min of the
+    per-forward HIP-event times, tokens/s, TFLOP/s, GB/s of algorithmic
+    bytes, their fractions of the published and the measured peaks, and the
+    attainable-roofline fraction max(F/P, B/BW) / t."""
     import torch
 
     from mixture_experts_layer_14_amd import synth
@@ -321,6 +374,8 @@ def per_config(steps, warmup, peaks, with_cpu):
 
     rows = []
     for name, sample in PER_CONFIG:
+        if names is not None and name not in names:
+            continue
         cfg = synth.CONFIGS[name]
         T = cfg.T
         inp = synth.make_inputs(cfg, T, device="cuda")
@@ -331,13 +386,16 @@ def per_config(steps, warmup, peaks, with_cpu):
         n = steps if T >= 1024 else max(steps, 50)
         for _ in range(warmup):
             layer.forward(x, lg, b, out=out)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(n):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        stream = torch.cuda.current_stream()
+        for e0, e1 in ev:
+            e0.record(stream)
             layer.forward(x, lg, b, out=out)
-        e1.record()
+            e1.record(stream)
         torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) / n * 1e-3
+        ms = _stats([e0.elapsed_time(e1) for e0, e1 in ev])
+        t = ms["median"] * 1e-3
         st = Stages(layer, T)
         st.topk(lg, b)
         st.align()
@@ -346,7 +404,8 @@ def per_config(steps, warmup, peaks, with_cpu):
         byts = algorithmic_bytes(cfg, T, active)
         peak = {"bf16": PEAK_BF16_TFLOPS, "fp8": PEAK_FP8_TFLOPS, "f32": PEAK_F32_TFLOPS}[cfg.w_dtype]
         t_f, t_b = flops / (peak * 1e12), byts / (PEAK_HBM_GBS * 1e9)
-        row = {"config": name, "T": T, "dtype": cfg.w_dtype, "ms": t * 1e3, "tokens_per_s": T / t,
+        row = {"config": name, "T": T, "dtype": cfg.w_dtype, "iters": n, "ms": ms["median"],
+               "ms_min": ms["min"], "ms_mean": ms["mean"], "tokens_per_s": T / t,
                "tflops": flops / t / 1e12, "GBps": byts / t / 1e9, "active_experts": active,
                "mfma_frac": flops / t / 1e12 / peak, "hbm_frac": byts / t / 1e9 / PEAK_HBM_GBS,
                "bound": "mfma" if t_f >= t_b else "hbm", "roofline_frac": max(t_f, t_b) / t}
@@ -357,10 +416,32 @@ def per_config(steps, warmup, peaks, with_cpu):
         if with_cpu:
             row["cpu_baseline"] = cpu_sample(cfg, inp, sample)
         rows.append(row)
-        print("config %s: %.3f ms" % (name, t * 1e3), file=sys.stderr, flush=True)
+        print("config %s: median %.3f ms, min %.3f ms" % (name, ms["median"], ms["min"]),
+              file=sys.stderr, flush=True)
         del layer, st, inp, out
         torch.cuda.empty_cache()
     return rows
+
+
+def profile_config(name, steps, warmup):
+    """Only `name`'s forward through moe_forward (warmup + steps calls): the
+    program a counter run (rocprofv3 --pmc) profiles, so each dispatch of a
+    moe kernel in its output belongs to this one configuration."""
+    import torch
+
+    from mixture_experts_layer_14_amd import synth
+    from mixture_experts_layer_14_amd.layer import FusedMoE, params_for
+
+    cfg = synth.CONFIGS[name]
+    inp = synth.make_inputs(cfg, cfg.T, device="cuda")
+    layer = FusedMoE(params_for(cfg, cfg.T), inp)
+    x, lg, b = inp["hidden"], inp["router_logits"], inp.get("e_score_correction_bias")
+    torch.cuda.synchronize()
+    print("profile %s: inputs ready" % name, flush=True)
+    for i in range(warmup + steps):
+        layer.forward(x, lg, b)
+        torch.cuda.synchronize()
+        print("profile %s: forward %d done" % (name, i), flush=True)
 
 
 def source_digest():
@@ -410,36 +491,23 @@ def calibrate_copy(nbytes=1 << 30, reps=3):
     print(json.dumps({"copy_bytes": nbytes, "reps": reps}))
 
 
-def cpu_baseline(cfg, T, sample_tokens):
-    """The CPU oracle, as it stands, on the first `sample_tokens` tokens of
-    the same workload, on all host threads."""
-    import torch
+WORKLOAD = {
+    "dsv3": "DeepSeek-V3-shape MoE layer forward (E=256, top_k=8, hidden=7168, "
+            "intermediate=2048, bf16 weights; sigmoid + correction bias, grouped top-k 8 groups / 4, "
+            "routed_scaling_factor 2.5), prefill T=8192",
+    "dsv3_decode": "DeepSeek-V3-shape MoE layer forward, bf16, decode T=64",
+    "dsv3_fp8": "DeepSeek-V3-shape MoE layer forward, fp8 e4m3 experts (128x128 block scales, "
+                "group-128 activation quant) + 1 shared expert, T=8192",
+    "mixtral": "Mixtral-shape MoE layer forward (E=8, top_k=2, hidden=4096, intermediate=14336, "
+               "bf16; softmax + renormalize), prefill T=4096",
+    "mixtral_decode": "Mixtral-shape MoE layer forward, bf16, decode T=32",
+    "qwen": "Qwen-style MoE layer forward (E=128, top_k=8, hidden=2048, intermediate=768, bf16; "
+            "Zipf-skewed softmax routing), T=16384",
+}
 
-    from mixture_experts_layer_14_amd import synth
-    from oracle import oracle as O
 
-    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
-    threads = max(1, min(threads, 16))
-    inp = synth.make_inputs(cfg, sample_tokens, device="cpu",
-                            weight_device="cuda" if torch.cuda.is_available() else "cpu")
-    bits = synth.tensor_bits
-    L = dict(T=sample_tokens, E=cfg.E, K=cfg.K, H=cfg.H, I=cfg.I,
-             scoring=O.SIGMOID if cfg.scoring == "sigmoid" else O.SOFTMAX,
-             renormalize=cfg.renormalize, n_group=cfg.n_group, topk_group=cfg.topk_group,
-             routed_scaling_factor=cfg.rsf,
-             x_dtype=O.F32 if cfg.act_dtype == "f32" else O.BF16,
-             w_dtype={"f32": O.F32, "bf16": O.BF16, "fp8": O.E4M3}[cfg.w_dtype],
-             act_fp8=cfg.fp8, hidden=bits(inp["hidden"]), logits=bits(inp["router_logits"]),
-             bias=bits(inp.get("e_score_correction_bias")),
-             w13=bits(inp["w13"]), w2=bits(inp["w2"]),
-             w13_scale=bits(inp.get("w13_scale")), w2_scale=bits(inp.get("w2_scale")))
-    del inp
-    t0 = time.perf_counter()
-    O.moe_forward_tokens(L, range(sample_tokens), nthreads=threads)
-    dt = time.perf_counter() - t0
-    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "first %d tokens of the %s workload, full layer in float64, %.1f s"
-                      % (sample_tokens, cfg.name, dt)}
+def _peak(cfg):
+    return {"bf16": PEAK_BF16_TFLOPS, "fp8": PEAK_FP8_TFLOPS, "f32": PEAK_F32_TFLOPS}[cfg.w_dtype]
 
 
 def main():
@@ -447,14 +515,19 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="mixtral")
-    ap.add_argument("--decode-config", default="mixtral_decode")
-    ap.add_argument("--cpu-sample", type=int, default=256)
+    ap.add_argument("--config", default="dsv3")
+    ap.add_argument("--decode-config", default="dsv3_decode")
+    ap.add_argument("--cpu-sample", type=int, default=256,
+                    help="tokens of the headline workload the CPU oracle computes")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-configuration table and the measured peaks")
+    ap.add_argument("--configs", default="",
+                    help="comma-separated subset of the per-configuration table")
+    ap.add_argument("--profile-config", default="",
+                    help="only run this configuration's forward (for counter runs)")
     ap.add_argument("--shared-streams", action="store_true",
                     help="only compare the shared expert as a GEMM slot with a second stream")
     args = ap.parse_args()
@@ -477,15 +550,26 @@ def main():
         shared_streams("dsv3_fp8", [1, 16, 64, 256, 8192])
         return
     binding.load()
+    if args.profile_config:
+        profile_config(args.profile_config, args.steps, args.warmup)
+        return
     cfg = synth.CONFIGS[args.config]
     T = cfg.T
-    r = time_layer(cfg, T, args.steps, args.warmup)
+    inp = synth.make_inputs(cfg, T, device="cuda")
+    r = time_layer(cfg, inp, args.steps, args.warmup)
     flops = cfg.flops()
-    peak = {"bf16": PEAK_BF16_TFLOPS, "fp8": PEAK_FP8_TFLOPS, "f32": PEAK_F32_TFLOPS}[cfg.w_dtype]
-    w13_tflops = w13_flops(cfg, T) / (r["w13_ms"] * 1e-3) / 1e12
+    peak = _peak(cfg)
+    w13_s = r["w13_ms"]["mean"] * 1e-3
+    roof = kernel_roofline(w13_flops(cfg, T), w13_bytes(cfg, T, r["active_experts"]), w13_s, peak)
+    roof.update({"kernel": "w13 grouped GEMM + SiLU-and-mul",
+                 "traffic": stored_traffic("%s_w13" % cfg.name),
+                 "avg_kernel_ms": r["w13_ms"]["mean"], "median_kernel_ms": r["w13_ms"]["median"],
+                 "min_kernel_ms": r["w13_ms"]["min"]})
+    t_step = r["ms_per_step"] * 1e-3
+    layer_bytes = algorithmic_bytes(cfg, T, r["active_experts"])
     line = {
         "metric": METRIC,
-        "value": T / (r["ms_per_step"] * 1e-3),
+        "value": T / t_step,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -496,49 +580,58 @@ def main():
         "vs_baseline": None,
         "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3", "f32": "f32"}[cfg.w_dtype],
         "data": "synthetic (seeded N(0,1) hidden and logits, N(0,0.02) weights)",
-        "config": {"workload": "%s MoE layer forward, prefill T=%d" % (cfg.name, T), "E": cfg.E,
-                   "top_k": cfg.K, "hidden": cfg.H, "intermediate": cfg.I, "T": T,
-                   "routing": "%s%s" % (cfg.scoring, "+renormalize" if cfg.renormalize else "")},
-        "tflops": flops / (r["ms_per_step"] * 1e-3) / 1e12,
-        "mfma_frac": flops / (r["ms_per_step"] * 1e-3) / 1e12 / peak,
+        "config": {"workload": WORKLOAD.get(cfg.name, cfg.name), "E": cfg.E, "top_k": cfg.K,
+                   "hidden": cfg.H, "intermediate": cfg.I, "T": T, "weights": cfg.w_dtype,
+                   "routing": "%s%s%s" % (cfg.scoring, "+renormalize" if cfg.renormalize else "",
+                                          " grouped %d/%d" % (cfg.n_group, cfg.topk_group)
+                                          if cfg.n_group > 1 else "")},
+        "step_ms": r["step_ms"],
+        "tflops": flops / t_step / 1e12,
+        "mfma_frac": flops / t_step / 1e12 / peak,
+        "hbm_GBps": layer_bytes / t_step / 1e9,
+        "layer_attainable_frac": max(flops / (peak * 1e12), layer_bytes / (PEAK_HBM_GBS * 1e9)) / t_step,
         "forward_ms_per_step": r["forward_ms_per_step"],
+        "forward_ms": r["forward_ms"],
         "active_experts": r["active_experts"],
-        "roofline": {"kernel": "w13 grouped GEMM + SiLU-and-mul", "bound": "mfma",
-                     "achieved": w13_tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": w13_tflops / peak, "traffic": stored_traffic("%s_w13" % cfg.name),
-                     "avg_kernel_ms": r["w13_ms"]},
+        "roofline": roof,
     }
+    if not args.no_cpu and args.cpu_sample > 0:
+        line["cpu_baseline"] = cpu_sample(cfg, inp, args.cpu_sample)
+    del inp
+    torch.cuda.empty_cache()
     if args.decode_config:
         dcfg = synth.CONFIGS[args.decode_config]
-        d = time_layer(dcfg, dcfg.T, max(args.steps, 50), args.warmup)
+        dinp = synth.make_inputs(dcfg, dcfg.T, device="cuda")
+        d = time_layer(dcfg, dinp, max(args.steps, 50), args.warmup)
+        del dinp
+        torch.cuda.empty_cache()
         byts = algorithmic_bytes(dcfg, dcfg.T, d["active_experts"])
         gbs = byts / (d["ms_per_step"] * 1e-3) / 1e9
-        line["decode"] = {"workload": "%s T=%d" % (dcfg.name, dcfg.T), "T": dcfg.T,
-                          "ms_per_step": d["ms_per_step"],
+        line["decode"] = {"workload": WORKLOAD.get(dcfg.name, dcfg.name), "T": dcfg.T,
+                          "ms_per_step": d["ms_per_step"], "step_ms": d["step_ms"],
                           "tokens_per_s": dcfg.T / (d["ms_per_step"] * 1e-3),
                           "hbm_GBps": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
                           "algorithmic_bytes": byts, "active_experts": d["active_experts"],
-                          "forward_ms_per_step": d["forward_ms_per_step"]}
-        wb = w13_bytes(dcfg, dcfg.T, d["active_experts"])
-        ach = wb / (d["w13_ms"] * 1e-3) / 1e9
-        line["decode"]["roofline"] = {"kernel": "w13 weight-streaming GEMM + SiLU-and-mul",
-                                      "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
-                                      "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
-                                      "traffic": stored_traffic("%s_w13" % dcfg.name),
-                                      "avg_kernel_ms": d["w13_ms"], "algorithmic_bytes": wb}
+                          "forward_ms_per_step": d["forward_ms_per_step"],
+                          "forward_ms": d["forward_ms"]}
+        droof = kernel_roofline(w13_flops(dcfg, dcfg.T), w13_bytes(dcfg, dcfg.T, d["active_experts"]),
+                                d["w13_ms"]["mean"] * 1e-3, _peak(dcfg))
+        droof.update({"kernel": "w13 weight-streaming GEMM + SiLU-and-mul",
+                      "traffic": stored_traffic("%s_w13" % dcfg.name),
+                      "avg_kernel_ms": d["w13_ms"]["mean"], "median_kernel_ms": d["w13_ms"]["median"],
+                      "min_kernel_ms": d["w13_ms"]["min"]})
+        line["decode"]["roofline"] = droof
     # the router gate GEMM (a separate entry point, not part of the step)
-    dsv3 = synth.CONFIGS["dsv3"]
-    line["router"] = [time_router(cfg, T, "bf16", 20, 3),
-                      time_router(synth.CONFIGS[args.decode_config], synth.CONFIGS[args.decode_config].T,
-                                  "bf16", 50, 3),
-                      time_router(dsv3, dsv3.T, "f32", 20, 3),
-                      time_router(dsv3, 64, "f32", 50, 3)]
-    if not args.no_cpu and args.cpu_sample > 0:
-        line["cpu_baseline"] = cpu_baseline(cfg, T, args.cpu_sample)
+    dsv3, mix = synth.CONFIGS["dsv3"], synth.CONFIGS["mixtral"]
+    line["router"] = [time_router(dsv3, dsv3.T, "f32", 20, 3),
+                      time_router(dsv3, 64, "f32", 50, 3),
+                      time_router(mix, mix.T, "bf16", 20, 3),
+                      time_router(mix, 32, "bf16", 50, 3)]
     if not args.no_configs:
         peaks = measured_peaks()
         line["measured_peaks"] = peaks
-        line["configs"] = per_config(10, 3, peaks, not args.no_cpu)
+        names = [n for n in args.configs.split(",") if n] or None
+        line["configs"] = per_config(10, 3, peaks, not args.no_cpu, names)
     print(json.dumps(line), flush=True)
 
 

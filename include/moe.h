@@ -30,8 +30,11 @@
  *     caller owns all buffers; the library never allocates in a call.
  *   - All arrays are dense row-major, except the expert weight matrices
  *     (w13, w2, shared_w13, shared_w2), which the GEMM calls take in the
- *     packed layout written by moe_pack_weights.  bf16 = IEEE binary32 upper
- *     half; fp8 = OCP e4m3 ("e4m3fn", max 448) stored one byte per value.
+ *     packed layout written by moe_pack_weights; moe_params.weight_layout
+ *     must say so (MOE_LAYOUT_PACKED), so that a caller handing over the
+ *     pages' row-major tensors gets an error, not a wrong result.
+ *     bf16 = IEEE binary32 upper half; fp8 = OCP e4m3 ("e4m3fn", max 448)
+ *     stored one byte per value.
  *     Weight block scales stay row-major.
  *   - `stream` is a hipStream_t passed as void* (NULL: the null stream).
  *     Calls only enqueue work: no host synchronisation, no allocation, so a
@@ -66,6 +69,13 @@ enum { MOE_SCORING_SOFTMAX = 0, MOE_SCORING_SIGMOID = 1 };
 /* Element types. */
 enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1, MOE_DTYPE_FP8_E4M3 = 2 };
 
+/* Storage layout of the expert weight matrices handed to the GEMM calls and
+ * moe_forward.  ROW_MAJOR (the pages' [N, K] tensors as loaded, and the value
+ * of a zero-initialised moe_params) is rejected by those calls with
+ * MOE_ERR_UNSUPPORTED; they read PACKED weights, written by moe_pack_weights
+ * once at load time. */
+enum { MOE_LAYOUT_ROW_MAJOR = 0, MOE_LAYOUT_PACKED = 1 };
+
 /* Layer description (host struct, read during the call only).
  *
  * Supported (act_dtype, weight_dtype, out_dtype):
@@ -90,8 +100,9 @@ typedef struct moe_params {
     int32_t weight_dtype;        /* dtype of w13 / w2                          */
     int32_t out_dtype;           /* dtype of out                               */
     int32_t num_shared_experts;  /* 0, or 1: a shared expert (same format as  */
-                                 /* the routed ones) of intermediate size I   */
-                                 /* added to every token with weight 1        */
+                                 /* the routed ones) of intermediate size Is  */
+                                 /* (shared_intermediate) added to every      */
+                                 /* token with weight 1                       */
     /* Activation variants; all zero gives the plain SiLU-and-mul layer.
      * Passages: FusedMoE is_act_and_mul and apply_router_weight_on_input
      * (vLLM page), is_gated, gemm1_alpha and gemm1_clamp_limit (SGLang layer
@@ -106,6 +117,15 @@ typedef struct moe_params {
     int32_t router_weight_on_input; /* 1: the routing weight scales the      */
                                  /* expert input, out_t = sum_k MLP(w_k x_t) */
                                  /* (+ shared MLP(x_t)); bf16/fp32 layers     */
+    /* Layout of w13 / w2 / shared_w13 / shared_w2 (MOE_LAYOUT_*); the GEMM
+     * calls and moe_forward require MOE_LAYOUT_PACKED. */
+    int32_t weight_layout;
+    /* Is, intermediate size of the shared expert; 0 means I.  Passage:
+     * DeepseekV2MoE (SGLang deepseek_v2 page) builds the shared MLP with
+     * moe_intermediate_size * n_shared_experts, so Is = m * I with m in
+     * 1..16 (other sizes: MOE_ERR_UNSUPPORTED).  Needs num_shared_experts =
+     * 1 (else it must be 0). */
+    int32_t shared_intermediate;
 } moe_params;
 
 /* Bytes of device workspace that moe_forward needs for `p` (the decomposed
@@ -199,6 +219,15 @@ int moe_align_permute(const moe_params *p, const int32_t *topk_ids,
 int moe_quant_act_fp8(const moe_params *p, const void *hidden, uint8_t *q,
                       float *scale, void *stream);
 
+/* Rows of the shared expert.  With Is = m * I the shared expert's
+ * intermediate dimension is taken as m consecutive slices of I (slice j:
+ * gate rows [j*I, (j+1)*I) and up rows [Is + j*I, Is + (j+1)*I) of
+ * shared_w13, columns [j*I, (j+1)*I) of shared_w2).  The down projection sums
+ * over that dimension, so the shared MLP is the sum of the m slices' MLPs;
+ * each slice is one more block of T rows of the grouped GEMMs: row
+ * T*K + j*T + t holds token t through slice j.  Below, S = m when
+ * num_shared_experts == 1, else 0. */
+
 /* Gate/up grouped GEMM with SiLU-and-mul, row by row of the permutation.
  * Passage: FusedMoE w13 = [w1 (gate); w3 (up)] along the output dimension
  * (_load_w13, vLLM page), activation "silu" with is_act_and_mul;
@@ -208,20 +237,21 @@ int moe_quant_act_fp8(const moe_params *p, const void *hidden, uint8_t *q,
  *   w13          [E, 2I, H] packed by moe_pack_weights (+ w13_scale
  *                [E, 2I/128, H/128] row-major for fp8); [E, I, H] with
  *                non_gated.
- *   shared_w13   [2I, H] ([I, H] non-gated) packed (+ scale) when
- *                num_shared_experts == 1, else NULL.
+ *   shared_w13   [2Is, H] ([Is, H] non-gated) packed (+ scale [2Is/128,
+ *                H/128]) when num_shared_experts == 1, else NULL.
  *   expert_offsets, sorted_slots: from moe_align_permute.
  *   topk_weights [T, K] fp32 from moe_topk when router_weight_on_input
  *                (the w13 output of routed row r is scaled by its slot's
  *                weight before the activation, which equals scaling the
  *                input); else ignored and may be NULL.
- *   act          [T*K + T*S, I] out (S = num_shared_experts): row r holds
- *                silu(g) * u (or its variant, see moe_params) for the token
- *                of sorted_slots[r] (rows T*K + t: token t through the shared
- *                expert).  bf16 for bf16 layers, fp32 for fp32 layers, e4m3
+ *   act          [T*K + T*S, I] out: row r < T*K holds silu(g) * u (or its
+ *                variant, see moe_params) for the token of sorted_slots[r];
+ *                rows T*K + j*T + t: token t through slice j of the shared
+ *                expert.  bf16 for bf16 layers, fp32 for fp32 layers, e4m3
  *                codes for fp8 layers with act_scale [T*K + T*S, I/128] fp32
  *                out.
- * Errors: MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE. */
+ * Errors: MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED (also weight_layout other
+ * than MOE_LAYOUT_PACKED), MOE_ERR_WORKSPACE. */
 int moe_grouped_gemm_w13_act(const moe_params *p, const void *hidden,
                              const float *hidden_scale, const void *w13,
                              const float *w13_scale, const void *shared_w13,
@@ -240,14 +270,15 @@ int moe_grouped_gemm_w13_act(const moe_params *p, const void *hidden,
  *   act, act_scale  from moe_grouped_gemm_w13_act.
  *   w2         [E, H, I] packed by moe_pack_weights (+ w2_scale
  *              [E, H/128, I/128] row-major for fp8).
- *   shared_w2  [H, I] packed (+ scale) or NULL.
+ *   shared_w2  [H, Is] packed (+ scale [H/128, Is/128]) or NULL.
  *   topk_weights [T, K] fp32 from moe_topk; slot_to_row [T*K].
  *   out        [T, H] out_dtype:  out_t = sum_k w_{t,k} y_{row(t,k)}
- *              (+ y_{T*K+t} of the shared expert); with
+ *              (+ sum_j y_{T*K+j*T+t} of the shared expert); with
  *              router_weight_on_input the rows are added unweighted (the
  *              weight went into the w13 call).  The sum over k runs in a
  *              fixed order in fp32, so results are bitwise reproducible.
- * Errors: MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE. */
+ * Errors: MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED (also weight_layout other
+ * than MOE_LAYOUT_PACKED), MOE_ERR_WORKSPACE. */
 int moe_grouped_gemm_w2_combine(const moe_params *p, const void *act,
                                 const float *act_scale, const void *w2,
                                 const float *w2_scale, const void *shared_w2,
@@ -268,7 +299,8 @@ int moe_grouped_gemm_w2_combine(const moe_params *p, const void *act,
  *   topk_ids_out [T, K] int32 / topk_weights_out [T, K] fp32: optional
  *   copies of the routing (NULL to skip).
  *   workspace >= moe_workspace_size(p) bytes.
- * Errors: as the calls it is made of. */
+ * Errors: as the calls it is made of (weight_layout must be
+ * MOE_LAYOUT_PACKED). */
 int moe_forward(const moe_params *p, const void *hidden,
                 const float *router_logits,
                 const float *e_score_correction_bias, const void *w13,

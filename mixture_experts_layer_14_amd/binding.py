@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 SOFTMAX, SIGMOID = 0, 1
 F32, BF16, FP8_E4M3 = 0, 1, 2
+LAYOUT_ROW_MAJOR, LAYOUT_PACKED = 0, 1
 
 # every entry point that include/moe.h declares
 ENTRY_POINTS = (
@@ -50,6 +51,8 @@ class MoeParams(ctypes.Structure):
         ("swiglu_alpha", ctypes.c_float),
         ("swiglu_limit", ctypes.c_float),
         ("router_weight_on_input", ctypes.c_int32),
+        ("weight_layout", ctypes.c_int32),
+        ("shared_intermediate", ctypes.c_int32),
     ]
 
 
@@ -104,13 +107,18 @@ def make_params(*, num_tokens, num_experts, top_k, hidden_size, intermediate_siz
                 scoring_func=SOFTMAX, renormalize=True, num_expert_group=0, topk_group=0,
                 routed_scaling_factor=1.0, act_dtype=BF16, weight_dtype=BF16, out_dtype=BF16,
                 num_shared_experts=0, non_gated=False, swiglu_alpha=0.0, swiglu_limit=0.0,
-                router_weight_on_input=False) -> MoeParams:
+                router_weight_on_input=False, weight_layout=LAYOUT_ROW_MAJOR,
+                shared_intermediate=0) -> MoeParams:
+    """moe_params; weight_layout defaults to row-major like a zero-initialised
+    C struct (the GEMM calls then refuse the weights: pass LAYOUT_PACKED with
+    weights from pack_weights)."""
     return MoeParams(int(num_tokens), int(num_experts), int(top_k), int(hidden_size),
                      int(intermediate_size), int(scoring_func), int(bool(renormalize)),
                      int(num_expert_group), int(topk_group), float(routed_scaling_factor),
                      int(act_dtype), int(weight_dtype), int(out_dtype), int(num_shared_experts),
                      int(bool(non_gated)), float(swiglu_alpha), float(swiglu_limit),
-                     int(bool(router_weight_on_input)))
+                     int(bool(router_weight_on_input)), int(weight_layout),
+                     int(shared_intermediate))
 
 
 def _ptr(t):

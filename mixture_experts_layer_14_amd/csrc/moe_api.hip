@@ -11,6 +11,7 @@ namespace {
 constexpr int kMaxExperts = 512;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxGroups = 64;
+constexpr int kMaxSharedSlices = 16;  // shared_intermediate <= 16 * I
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -22,9 +23,12 @@ size_t act_elt(const moe_params* p) {
 }
 
 int64_t routed_rows(const moe_params* p) { return p->num_tokens * p->top_k; }
-int64_t all_rows(const moe_params* p) {
-    return routed_rows(p) + (p->num_shared_experts ? p->num_tokens : 0);
+// I-wide slices of the shared expert (its intermediate size over I)
+int shared_slices(const moe_params* p) {
+    if (!p->num_shared_experts) return 0;
+    return p->shared_intermediate > 0 ? p->shared_intermediate / p->intermediate_size : 1;
 }
+int64_t all_rows(const moe_params* p) { return routed_rows(p) + shared_slices(p) * p->num_tokens; }
 
 // Shape/parameter checks shared by every call.
 int check_params(const moe_params* p) {
@@ -37,6 +41,15 @@ int check_params(const moe_params* p) {
         return MOE_ERR_INVALID;
     if (p->num_shared_experts < 0) return MOE_ERR_INVALID;
     if (p->num_shared_experts > 1) return MOE_ERR_UNSUPPORTED;
+    if (p->weight_layout != MOE_LAYOUT_ROW_MAJOR && p->weight_layout != MOE_LAYOUT_PACKED)
+        return MOE_ERR_INVALID;
+    if (p->shared_intermediate < 0) return MOE_ERR_INVALID;
+    if (p->shared_intermediate > 0) {
+        if (!p->num_shared_experts) return MOE_ERR_INVALID;
+        // the pages' shared expert is n_shared_experts routed-sized MLPs wide
+        if (p->shared_intermediate % p->intermediate_size) return MOE_ERR_UNSUPPORTED;
+        if (p->shared_intermediate / p->intermediate_size > kMaxSharedSlices) return MOE_ERR_UNSUPPORTED;
+    }
     const int G = p->num_expert_group;
     if (G < 0) return MOE_ERR_INVALID;
     if (G > 1) {
@@ -72,9 +85,10 @@ moe::GroupedProblem problem(const moe_params* p, moe::TileTableKey* built = null
     g.T = p->num_tokens;
     g.K = p->top_k;
     g.E = p->num_experts;
-    g.shared = p->num_shared_experts;
+    g.shared = shared_slices(p);
     g.H = p->hidden_size;
     g.I = p->intermediate_size;
+    g.Is = g.shared * g.I;
     g.gated = p->non_gated ? 0 : 1;
     g.alpha = p->swiglu_alpha > 0.0f ? p->swiglu_alpha : 1.0f;
     g.limit = p->swiglu_limit;
@@ -227,6 +241,7 @@ int w13_act(const moe_params* p, const void* hidden, const float* hidden_scale, 
             moe::TileTableKey* built) {
     int st = check_params(p);
     if (st != MOE_OK) return st;
+    if (p->weight_layout != MOE_LAYOUT_PACKED) return MOE_ERR_UNSUPPORTED;
     if (p->num_tokens == 0) return MOE_OK;  // empty batch: nothing to do
     if (!hidden || !w13 || !expert_offsets || !sorted_slots || !act) return MOE_ERR_INVALID;
     if (p->num_shared_experts && !shared_w13) return MOE_ERR_INVALID;
@@ -248,6 +263,7 @@ int w2_combine(const moe_params* p, const void* act, const float* act_scale, con
                size_t workspace_bytes, void* stream, moe::TileTableKey* built) {
     int st = check_params(p);
     if (st != MOE_OK) return st;
+    if (p->weight_layout != MOE_LAYOUT_PACKED) return MOE_ERR_UNSUPPORTED;
     if (p->num_tokens == 0) return MOE_OK;  // empty batch: nothing to do
     if (!act || !w2 || !expert_offsets || !sorted_slots || !slot_to_row || !topk_weights || !out)
         return MOE_ERR_INVALID;
@@ -312,6 +328,7 @@ int moe_forward(const moe_params* p, const void* hidden, const float* router_log
                 float* topk_weights_out, void* workspace, size_t workspace_bytes, void* stream) {
     int st = check_params(p);
     if (st != MOE_OK) return st;
+    if (p->weight_layout != MOE_LAYOUT_PACKED) return MOE_ERR_UNSUPPORTED;
     if (p->num_tokens == 0) return MOE_OK;  // empty batch: nothing to do
     if (!hidden || !router_logits || !w13 || !w2 || !out) return MOE_ERR_INVALID;
     if (e_score_correction_bias && p->scoring_func != MOE_SCORING_SIGMOID) return MOE_ERR_INVALID;

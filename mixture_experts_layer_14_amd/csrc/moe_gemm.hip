@@ -36,7 +36,7 @@ namespace moe {
 // ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets,
-                                                           int E, int32_t shared_rows,
+                                                           int E, int nshared, int32_t T,
                                                            int32_t shared_base, int BM, int gm_max,
                                                            int tail_rows, Tile* __restrict__ tiles,
                                                            int32_t* __restrict__ num_tiles,
@@ -44,15 +44,16 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
                                                            int32_t* __restrict__ num_units,
                                                            int split_nn, int32_t* __restrict__ split) {
     __shared__ int32_t wave_sums[16];
-    const int g = threadIdx.x;  // group: expert g, or the shared expert at g == E
+    // segment: expert g, or slice g - E of the shared expert (T rows each)
+    const int g = threadIdx.x;
     int32_t r0 = 0, r1 = 0;
     if (g < E) {
         // clamp to [0, routed rows] so the table can never outgrow its buffer
         r0 = min(max(offsets[g], 0), shared_base);
         r1 = min(max(offsets[g + 1], r0), shared_base);
-    } else if (g == E) {
-        r0 = shared_base;
-        r1 = shared_base + shared_rows;
+    } else if (g < E + nshared) {
+        r0 = shared_base + (g - E) * T;
+        r1 = r0 + T;
     }
     // main m-tiles of BM rows (the last one possibly ragged), unless a
     // remainder of at most tail_rows rows goes to a tail tile
@@ -176,9 +177,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void grouped_gemm_kernel(GemmArgs g)
     if (m_tile >= *g.num_tiles) return;
     const Tile tl = g.tiles[m_tile];
     const int64_t eltK = static_cast<int64_t>(g.Kd) * Pol::kElt;  // bytes per row
-    const uint8_t* Bexp = tl.expert < g.E
-                              ? g.B + static_cast<int64_t>(tl.expert) * g.N * eltK
-                              : g.B_shared;
+    const BSel bw = expert_weights<MODE>(g, tl.expert, Pol::kElt);
 
     // fixed global row addresses of this thread's load chunks
     const uint8_t* a_ptr[A_ITEMS];
@@ -191,13 +190,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void grouped_gemm_kernel(GemmArgs g)
         const int row = c / kChunks, c16 = c % kChunks;
         int64_t r = tl.row0 + row;
         if (r >= tl.row1) r = tl.row0;  // ragged tail: load a valid row, never stored
-        int64_t src;
-        if (MODE == kModeW13) {
-            src = r >= g.routed_rows ? r - g.routed_rows : g.sorted_slots[r] / g.topk;
-            src = src < 0 ? 0 : (src >= g.T ? g.T - 1 : src);
-        } else {
-            src = r;
-        }
+        const int64_t src = a_source_row<MODE>(g, r);
         a_ptr[q] = g.A + src * eltK + c16 * 16;
     }
 #pragma unroll
@@ -205,7 +198,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void grouped_gemm_kernel(GemmArgs g)
         const int c = tid + q * NT;
         b_on[q] = c < BN * kChunks;
         const int row = c / kChunks, c16 = c % kChunks;
-        b_ptr[q] = Bexp + packed_offset(b_weight_row<MODE, BN, 16>(g, n_tile, row), c16 * 16, eltK);
+        b_ptr[q] = bw.base + packed_offset(b_weight_row<MODE, BN, 16>(g, bw, n_tile, row), c16 * 16, bw.rb);
     }
 
     f32x4 acc[TM][TN];
@@ -307,7 +300,8 @@ __global__ __launch_bounds__(WM* WN* kWave) void grouped_gemm_kernel(GemmArgs g)
 }
 
 // ---------------------------------------------------------------------------
-// combine: out[t, :] = sum_k y[row(t,k), :] (+ y[T*K + t, :]), fixed order
+// combine: out[t, :] = sum_k y[row(t,k), :] (+ sum_j y[T*K + j*T + t, :]),
+// fixed order
 // ---------------------------------------------------------------------------
 
 template <class Pol>
@@ -330,16 +324,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
         const int np = r >= split_row ? parts : 1;
         for (int q = 0; q < np; ++q) s += Pol::load(y, q * part_stride + r * H + h);
     }
-    if (shared) {
-        const int np = T * K + t >= split_row ? parts : 1;
-        for (int q = 0; q < np; ++q) s += Pol::load(y, q * part_stride + (T * K + t) * H + h);
+    for (int j = 0; j < shared; ++j) {  // slices of the shared expert
+        const int64_t r = T * K + j * T + t;
+        const int np = r >= split_row ? parts : 1;
+        for (int q = 0; q < np; ++q) s += Pol::load(y, q * part_stride + r * H + h);
     }
     Pol::store(out, t * H + h, s);
 }
 
 // bf16 combine, 8 columns per thread (16-byte loads and stores).  y holds
 // `parts` partial outputs of every row (a K-split w2); the sum runs in fp32
-// in a fixed order: slot k = 0..K-1, then the shared row, each over parts.
+// in a fixed order: slot k = 0..K-1, then the shared expert's slices, each
+// over parts.
 __global__ __launch_bounds__(256) void combine_bf16x8_kernel(const uint16_t* __restrict__ y,
                                                              const int32_t* __restrict__ slot_to_row,
                                                              int64_t T, int K, int H, int shared,
@@ -371,7 +367,7 @@ __global__ __launch_bounds__(256) void combine_bf16x8_kernel(const uint16_t* __r
         int64_t r = slot_to_row[t * K + k];
         add_row(r < 0 ? 0 : (r >= rows ? rows - 1 : r));
     }
-    if (shared) add_row(T * K + t);
+    for (int j = 0; j < shared; ++j) add_row(T * K + j * T + t);
     u32x4 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -386,10 +382,12 @@ __global__ __launch_bounds__(256) void combine_bf16x8_kernel(const uint16_t* __r
 
 namespace {
 
-int64_t total_rows(const GroupedProblem& p) { return p.T * p.K + (p.shared ? p.T : 0); }
+int64_t total_rows(const GroupedProblem& p) { return p.T * p.K + p.shared * p.T; }
 
+// m-tiles of all segments (experts and shared slices): one partial tile per
+// segment at most
 int max_m_tiles(const GroupedProblem& p, int BM) {
-    return static_cast<int>((total_rows(p) + BM - 1) / BM + p.E + 1);
+    return static_cast<int>((total_rows(p) + BM - 1) / BM + p.E + p.shared);
 }
 
 // Average rows per expert that receives any: few rows -> weight streaming,
@@ -519,7 +517,7 @@ static void build_tiles(const GroupedProblem& p, const int32_t* offsets, int BM,
     const TileTableKey* b = p.built;
     if (!b || b->ws != key.ws || b->offsets != key.offsets || b->bm != key.bm ||
         b->tail_rows != key.tail_rows || b->split_nn != key.split_nn) {
-        build_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, p.E, p.shared ? static_cast<int32_t>(p.T) : 0,
+        build_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, p.E, p.shared, static_cast<int32_t>(p.T),
                                                    static_cast<int32_t>(p.T * p.K), BM, MOE_TILE_GM,
                                                    tail_rows, tiles, num_tiles, units, num_units,
                                                    split_nn, split);
@@ -722,6 +720,7 @@ hipError_t launch_w13(const GroupedProblem& p, const void* hidden, const float* 
     g.Kd = p.H;
     g.N = p.gated ? 2 * p.I : p.I;
     g.I = p.I;
+    g.Is = p.Is;
     g.E = p.E;
     if (p.dtype == MOE_DTYPE_BF16) return bf16_gemm<kModeW13>(p, g, offsets, ws, stream);
     if (p.dtype == MOE_DTYPE_F32) return w13_for<PolF32>(p, g, offsets, ws, stream);
@@ -751,6 +750,7 @@ hipError_t launch_w2_combine(const GroupedProblem& p, const void* act, const flo
     g.Kd = p.I;
     g.N = p.H;
     g.I = p.I;
+    g.Is = p.Is;
     g.E = p.E;
     g.A_scale = act_scale;
     g.B_scale = w2_scale;

@@ -96,10 +96,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
     const int n_tile = tp.n;
     const int64_t K = g.Kd;                        // bytes per row (1 byte per value)
     const int nkb = static_cast<int>(K / 128);
-    const bool shared = tl.expert >= g.E;
-    const uint8_t* Bexp = shared ? g.B_shared : g.B + static_cast<int64_t>(tl.expert) * g.N * K;
-    const float* Bsc = shared ? g.B_shared_scale
-                              : g.B_scale + static_cast<int64_t>(tl.expert) * (g.N / 128) * nkb;
+    const BSel bw = expert_weights<MODE>(g, tl.expert, 1);
 
     const uint8_t* src[COPIES];
 #pragma unroll
@@ -111,7 +108,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
             if (r >= tl.row1) r = tl.row0;
             src[q] = g.A + a_source_row<MODE>(g, r) * K + chunk * 16;
         } else {
-            src[q] = Bexp + packed_offset(b_weight_row<MODE, BN, 32>(g, n_tile, row - BM), chunk * 16, K);
+            src[q] = bw.base + packed_offset(b_weight_row<MODE, BN, 32>(g, bw, n_tile, row - BM), chunk * 16, bw.rb);
         }
     }
     // scale copied by this lane: an A-scale row (lanes < SROWS) or, in wave
@@ -128,8 +125,8 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
         const int slot = GROUPED ? p - BM : (wave == 0 ? lane - SROWS : -1);
         if (slot >= 0 && slot < NBS) {
             const int rep = MODE == kModeW13 ? slot * 32 : slot * 128;  // a local row of the block
-            const int b = static_cast<int>(b_weight_row<MODE, BN, 32>(g, n_tile, rep) / 128);
-            ssrc = Bsc + static_cast<int64_t>(b) * nkb;
+            const int b = static_cast<int>(b_weight_row<MODE, BN, 32>(g, bw, n_tile, rep) / 128);
+            ssrc = bw.scale + static_cast<int64_t>(b) * bw.scale_rs;
         }
     }
     // SG = 4: the scales of group grp into ring slot grp % 2

@@ -39,6 +39,7 @@ struct GemmArgs {
     int32_t Kd;                 // reduction length (elements)
     int32_t N;                  // rows of one expert's weight matrix (2I or H)
     int32_t I;
+    int32_t Is;                 // intermediate size of the shared expert (slices * I)
     int32_t E;
     int32_t n_tiles_n;          // tiles along N
     int32_t max_m_tiles;
@@ -68,11 +69,12 @@ constexpr int kLdsStride = kRowBytes + 16;   // padded row pitch in LDS
 constexpr int kChunks = kRowBytes / 16;      // 16-byte chunks per row
 
 // Source row of A for permuted row r: the token of its slot (w13; rows past
-// the routed ones belong to the shared expert), or r itself (w2).
+// the routed ones belong to the shared expert's slices, T rows each), or r
+// itself (w2).
 template <int MODE>
 __device__ __forceinline__ int64_t a_source_row(const GemmArgs& g, int64_t r) {
     if (MODE == kModeW2) return r;
-    int64_t src = r >= g.routed_rows ? r - g.routed_rows : g.sorted_slots[r] / g.topk;
+    int64_t src = r >= g.routed_rows ? (r - g.routed_rows) % g.T : g.sorted_slots[r] / g.topk;
     return src < 0 ? 0 : (src >= g.T ? g.T - 1 : src);
 }
 
@@ -112,15 +114,67 @@ __device__ __forceinline__ float glu_act(const GemmArgs& g, float gate, float up
     return silu_a(gate, g.act_alpha) * up;
 }
 
+// The weight matrix a tile multiplies with: routed expert e's, or slice j of
+// the shared expert (expert == E + j).  The shared expert's intermediate
+// dimension Is is cut into I-wide slices; the down projection sums over it,
+// so slice j is an MLP of its own: gate rows [jI, (j+1)I) and up rows
+// [Is + jI, Is + (j+1)I) of the [2Is, H] w13, columns [jI, (j+1)I) of the
+// [H, Is] w2.  Element (row, byte) of the matrix is at
+// base + packed_offset(row, byte, rb); gate0 / up0 are the first rows of the
+// gate and up blocks (w13); scale points at the fp8 block scale of block row
+// 0, k block 0, with scale_rs scales per block row.
+struct BSel {
+    const uint8_t* base;
+    int64_t rb;
+    int32_t gate0, up0;
+    const float* scale;
+    int32_t scale_rs;
+};
+
+template <int MODE>
+__device__ __forceinline__ BSel expert_weights(const GemmArgs& g, int expert, int elt) {
+    const int64_t rb = static_cast<int64_t>(g.Kd) * elt;
+    const int kb = g.Kd / 128;  // k blocks of a row (fp8 scales)
+    BSel s;
+    if (expert < g.E) {
+        s.base = g.B + static_cast<int64_t>(expert) * g.N * rb;
+        s.rb = rb;
+        s.gate0 = 0;
+        s.up0 = g.I;
+        s.scale = g.B_scale + static_cast<int64_t>(expert) * (g.N / 128) * kb;
+        s.scale_rs = kb;
+    } else if (MODE == kModeW13) {
+        const int j = expert - g.E;
+        s.base = g.B_shared;
+        s.rb = rb;
+        s.gate0 = j * g.I;
+        s.up0 = g.Is + j * g.I;
+        s.scale = g.B_shared_scale;
+        s.scale_rs = kb;
+    } else {
+        // a k offset of j*I*elt bytes is (j*I*elt / 64) KiB blocks of the
+        // packed layout (I*elt is a multiple of 64)
+        const int j = expert - g.E;
+        s.base = g.B_shared + static_cast<int64_t>(j) * g.I * elt * 16;
+        s.rb = static_cast<int64_t>(g.Is) * elt;
+        s.gate0 = 0;
+        s.up0 = 0;
+        s.scale = g.B_shared_scale + j * (g.I / 128);
+        s.scale_rs = g.Is / 128;
+    }
+    return s;
+}
+
 // Weight row of local B-tile row `row` for an n-tile of width BN.  w13 tiles
 // interleave gate and up rows in blocks of `blk` so that the accumulator
 // tile of gate column c and the one of up column c land in the same lanes.
 template <int MODE, int BN, int BLK>
-__device__ __forceinline__ int64_t b_weight_row(const GemmArgs& g, int n_tile, int row) {
-    if (MODE == kModeW2 || !g.gated) return static_cast<int64_t>(n_tile) * BN + row;
+__device__ __forceinline__ int64_t b_weight_row(const GemmArgs& g, const BSel& s, int n_tile, int row) {
+    if (MODE == kModeW2) return static_cast<int64_t>(n_tile) * BN + row;
+    if (!g.gated) return s.gate0 + static_cast<int64_t>(n_tile) * BN + row;
     const int b = row / BLK, pair = b / 2, up = b % 2;
     const int64_t col = static_cast<int64_t>(n_tile) * (BN / 2) + pair * BLK + row % BLK;
-    return up ? g.I + col : col;
+    return (up ? s.up0 : s.gate0) + col;
 }
 
 // Block -> (m-tile, n-tile).  Workgroups are handed to the 8 XCDs round-
@@ -276,9 +330,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile tl, cons
     const int wave = wave_index(tid);
     const int wm = wave / WN, wn = wave % WN;
     const int64_t eltK = static_cast<int64_t>(g.Kd) * 2;
-    const uint8_t* Bexp = tl.expert < g.E
-                              ? g.B + static_cast<int64_t>(tl.expert) * g.N * eltK
-                              : g.B_shared;
+    const BSel bw = expert_weights<MODE>(g, tl.expert, 2);
 
     // source of this lane's 16-byte slot in each of the wave's copies
     const uint8_t* src[COPIES];
@@ -291,7 +343,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile tl, cons
             if (r >= tl.row1) r = tl.row0;  // ragged tail: copy a valid row, never stored
             src[q] = g.A + a_source_row<MODE>(g, r) * eltK + chunk * 16;
         } else {
-            src[q] = Bexp + packed_offset(b_weight_row<MODE, BN, 32>(g, n_tile, row - BM), chunk * 16, eltK);
+            src[q] = bw.base + packed_offset(b_weight_row<MODE, BN, 32>(g, bw, n_tile, row - BM), chunk * 16, bw.rb);
         }
     }
     // this block's k-iterations: part kpart of the nk_all of a full row
@@ -668,9 +720,7 @@ __global__ __launch_bounds__(WAVES * kWave) void stream_kernel(GemmArgs g) {
     if (m_tile >= *g.num_tiles) return;
     const Tile tl = g.tiles[m_tile];
     const int64_t eltK = static_cast<int64_t>(g.Kd) * 2;
-    const uint8_t* Bexp = tl.expert < g.E
-                              ? g.B + static_cast<int64_t>(tl.expert) * g.N * eltK
-                              : g.B_shared;
+    const BSel bw = expert_weights<MODE>(g, tl.expert, 2);
     const int lrow = lane % 16, lk = (lane / 16) * 16;
 
     const uint8_t* a_ptr[TM];
@@ -683,7 +733,7 @@ __global__ __launch_bounds__(WAVES * kWave) void stream_kernel(GemmArgs g) {
     }
 #pragma unroll
     for (int j = 0; j < NPW; ++j)
-        b_ptr[j] = Bexp + packed_offset(b_weight_row<MODE, NPW * 16, 16>(g, n_grp, j * 16 + lrow), lk, eltK);
+        b_ptr[j] = bw.base + packed_offset(b_weight_row<MODE, NPW * 16, 16>(g, bw, n_grp, j * 16 + lrow), lk, bw.rb);
 
     f32x4 acc[TM][NPW];
 #pragma unroll

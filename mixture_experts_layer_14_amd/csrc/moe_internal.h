@@ -9,7 +9,8 @@
 namespace moe {
 
 // One m-tile of the grouped GEMMs: rows [row0, row1) of the permuted order,
-// all owned by `expert` (expert == E denotes the shared expert).
+// all owned by `expert` (expert == E + j denotes slice j of the shared
+// expert).
 struct Tile {
     int32_t expert;
     int32_t row0;
@@ -52,8 +53,10 @@ struct GroupedProblem {
     int64_t T;             // tokens
     int K;                 // top_k
     int E;                 // routed experts
-    int shared;            // 0/1 shared expert (rows T*K .. T*K+T-1)
+    int shared;            // slices of the shared expert (0 = none), each I
+                           // wide: slice j owns rows T*K + j*T .. T*K + j*T + T-1
     int H, I;              // hidden, intermediate
+    int Is;                // intermediate size of the shared expert (shared * I)
     // activation variants (moe_params): gated SiLU-and-mul (1) or SiLU of
     // one projection (0); SiLU slope; clamp limit (0: none); routing weight
     // applied to the expert input instead of its output

@@ -29,7 +29,8 @@ def params_for(cfg, T: int | None = None) -> B.MoeParams:
         routed_scaling_factor=cfg.rsf, act_dtype=_DT[cfg.act_dtype], weight_dtype=_DT[cfg.w_dtype],
         out_dtype=_DT[cfg.act_dtype], num_shared_experts=cfg.shared, non_gated=cfg.non_gated,
         swiglu_alpha=cfg.swiglu_alpha, swiglu_limit=cfg.swiglu_limit,
-        router_weight_on_input=cfg.weight_on_input)
+        router_weight_on_input=cfg.weight_on_input, weight_layout=B.LAYOUT_PACKED,
+        shared_intermediate=cfg.shared_I if cfg.shared else 0)
 
 
 _PACKED = ("w13", "w2", "shared_w13", "shared_w2")
@@ -42,7 +43,8 @@ class FusedMoE:
     (moe_pack_weights, done once here); scales stay as given."""
 
     def __init__(self, params: B.MoeParams, weights: dict):
-        self.params = params
+        self.params = B.MoeParams.from_buffer_copy(params)
+        self.params.weight_layout = B.LAYOUT_PACKED  # packed here, once
         self.w = {k: (B.pack_weights(v) if k in _PACKED and v is not None else v)
                   for k, v in weights.items()}
         self._ws = None
@@ -87,7 +89,9 @@ class Stages:
         self.layer = layer
         dev = "cuda"
         E, K, H, I = p.num_experts, p.top_k, p.hidden_size, p.intermediate_size
-        R = T * K + (T if p.num_shared_experts else 0)
+        # rows of the shared expert: T per I-wide slice of its intermediate size
+        slices = (p.shared_intermediate // I if p.shared_intermediate else 1) if p.num_shared_experts else 0
+        R = T * K + T * slices
         fp8 = p.weight_dtype == B.FP8_E4M3
         self.ids = torch.empty(T, K, dtype=torch.int32, device=dev)
         self.weights = torch.empty(T, K, dtype=torch.float32, device=dev)

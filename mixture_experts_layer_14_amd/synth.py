@@ -60,6 +60,7 @@ class MoEConfig:
     logit_skew: str = "none"       # "none" | "zipf"
     correction_bias: bool = False
     shared: int = 0                # number of shared experts (0 or 1)
+    shared_I: int = 0              # its intermediate size; 0 -> I
     seed: int = 0
     weight_seed: int = 0
     delta: float = 1e-3
@@ -76,6 +77,11 @@ class MoEConfig:
         return self.w_dtype == "fp8"
 
     @property
+    def Is(self) -> int:
+        """Intermediate size of the shared expert."""
+        return self.shared_I or self.I
+
+    @property
     def rows_drawn(self) -> int:
         return max(self.T, self.T_gen)
 
@@ -83,8 +89,8 @@ class MoEConfig:
         return dataclasses.replace(self, T=T, T_gen=max(self.T_gen, self.T))
 
     def flops(self) -> float:
-        """Algorithmic FLOPs of one forward: 6*T*K*H*I (+ 6*T*H*I for a shared expert)."""
-        return 6.0 * self.T * (self.K + self.shared) * self.H * self.I
+        """Algorithmic FLOPs of one forward: 6*T*K*H*I (+ 6*T*H*Is for a shared expert)."""
+        return 6.0 * self.T * self.H * (self.K * self.I + self.shared * self.Is)
 
 
 # The five layer configurations (sizes and distributions as stated above).
@@ -236,14 +242,16 @@ def _store_weights(cfg, count, stream, shape, device):
 def make_weights(cfg: MoEConfig, device="cpu") -> dict:
     """Expert weights: w13 [E, 2I, H] (gate rows first, then up rows) and
     w2 [E, H, I]; fp8 layers also get the 128x128 block scales and, with a
-    shared expert, shared_w13 [2I, H] / shared_w2 [H, I] in the same format."""
+    shared expert, shared_w13 [2Is, H] / shared_w2 [H, Is] in the same
+    format."""
     out = {}
     n13 = cfg.I if cfg.non_gated else 2 * cfg.I
     out["w13"], out["w13_scale"] = _store_weights(cfg, cfg.E, _W13, (n13, cfg.H), device)
     out["w2"], out["w2_scale"] = _store_weights(cfg, cfg.E, _W2, (cfg.H, cfg.I), device)
     if cfg.shared:
-        a, sa = _store_weights(cfg, 1, _SW13, (n13, cfg.H), device)
-        b, sb = _store_weights(cfg, 1, _SW2, (cfg.H, cfg.I), device)
+        s13 = cfg.Is if cfg.non_gated else 2 * cfg.Is
+        a, sa = _store_weights(cfg, 1, _SW13, (s13, cfg.H), device)
+        b, sb = _store_weights(cfg, 1, _SW2, (cfg.H, cfg.Is), device)
         out["shared_w13"], out["shared_w2"] = a[0], b[0]
         out["shared_w13_scale"] = None if sa is None else sa[0]
         out["shared_w2_scale"] = None if sb is None else sb[0]

@@ -47,7 +47,8 @@ def oracle_layer(cfg, inp: dict, T: int, experts=None) -> dict:
              w13_scale=per_expert("w13_scale"), w2_scale=per_expert("w2_scale"),
              gated=not cfg.non_gated,
              act_alpha=cfg.swiglu_alpha if cfg.swiglu_alpha > 0 else 1.0,
-             clamp_limit=cfg.swiglu_limit, weight_on_input=cfg.weight_on_input)
+             clamp_limit=cfg.swiglu_limit, weight_on_input=cfg.weight_on_input,
+             shared_I=cfg.shared_I if cfg.shared else 0)
     if cfg.shared:
         L["shared_w13"] = to_host_bits(inp["shared_w13"])
         L["shared_w2"] = to_host_bits(inp["shared_w2"])
@@ -61,6 +62,17 @@ def oracle_route(cfg, logits_np, bias_np):
                    scoring=O.SIGMOID if cfg.scoring == "sigmoid" else O.SOFTMAX,
                    renormalize=cfg.renormalize, n_group=cfg.n_group, topk_group=cfg.topk_group,
                    routed_scaling_factor=cfg.rsf)
+
+
+def last_row_tokens(offsets: np.ndarray, sorted_slots: np.ndarray, K: int, most: int = 64) -> list:
+    """Tokens of the last permuted row of each non-empty expert segment (the
+    rows of each expert's ragged or tail m-tile), thinned to at most `most`
+    experts taken evenly across the non-empty ones."""
+    E = offsets.size - 1
+    ends = [int(offsets[e + 1]) - 1 for e in range(E) if offsets[e + 1] > offsets[e]]
+    if len(ends) > most:
+        ends = [ends[i] for i in np.linspace(0, len(ends) - 1, most).round().astype(int)]
+    return (sorted_slots[ends] // K).tolist()
 
 
 def rel_err(got: np.ndarray, ref: np.ndarray) -> float:

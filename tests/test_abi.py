@@ -33,7 +33,8 @@ def test_library_exports_every_declared_symbol():
 
 def _p(**kw):
     base = dict(num_tokens=4, num_experts=8, top_k=2, hidden_size=128, intermediate_size=256,
-                act_dtype=B.BF16, weight_dtype=B.BF16, out_dtype=B.BF16)
+                act_dtype=B.BF16, weight_dtype=B.BF16, out_dtype=B.BF16,
+                weight_layout=B.LAYOUT_PACKED)
     base.update(kw)
     return B.make_params(**base)
 
@@ -54,6 +55,12 @@ FAKE = 0x1000  # never dereferenced: every call below fails validation first
     (dict(act_dtype=B.F32), B.MOE_ERR_UNSUPPORTED),                      # f32 act, bf16 w
     (dict(weight_dtype=B.F32), B.MOE_ERR_UNSUPPORTED),
     (dict(num_shared_experts=2), B.MOE_ERR_UNSUPPORTED),
+    # shared expert of its own intermediate size Is = m * I, m in 1..16
+    (dict(shared_intermediate=512), B.MOE_ERR_INVALID),                  # without a shared expert
+    (dict(num_shared_experts=1, shared_intermediate=-256), B.MOE_ERR_INVALID),
+    (dict(num_shared_experts=1, shared_intermediate=384), B.MOE_ERR_UNSUPPORTED),   # not m * I
+    (dict(num_shared_experts=1, shared_intermediate=17 * 256), B.MOE_ERR_UNSUPPORTED),
+    (dict(weight_layout=2), B.MOE_ERR_INVALID),
     (dict(scoring_func=7), B.MOE_ERR_INVALID),
     # activation variants
     (dict(swiglu_alpha=-1.0), B.MOE_ERR_INVALID),
@@ -173,3 +180,43 @@ def test_peak_helpers_validate_on_host():
     assert L.moe_peak_read(FAKE, 15, 4, FAKE, None) == B.MOE_ERR_INVALID   # not a multiple of 16
     assert L.moe_peak_read(FAKE + 4, 64, 4, FAKE, None) == B.MOE_ERR_INVALID  # misaligned
     assert L.moe_peak_read(None, 64, 4, FAKE, None) == B.MOE_ERR_INVALID
+
+
+def test_row_major_weights_rejected_by_the_weight_calls():
+    """The GEMM calls and moe_forward read packed weights only: a zero-
+    initialised moe_params (weight_layout = MOE_LAYOUT_ROW_MAJOR, the pages'
+    tensors as loaded) is refused before anything runs, while the calls that
+    take no weights accept it."""
+    L = B.load()
+    p = _p(weight_layout=B.LAYOUT_ROW_MAJOR)
+    need = B.moe_workspace_size(p)
+    assert need > 0
+    assert L.moe_forward(ctypes.byref(p), FAKE, FAKE, None, FAKE, None, FAKE, None, None, None,
+                         None, None, FAKE, None, None, FAKE, need, None) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_grouped_gemm_w13_act(ctypes.byref(p), FAKE, None, FAKE, None, None, None,
+                                      FAKE, FAKE, None, FAKE, None, FAKE, need,
+                                      None) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_grouped_gemm_w2_combine(ctypes.byref(p), FAKE, None, FAKE, None, None, None,
+                                         FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need,
+                                         None) == B.MOE_ERR_UNSUPPORTED
+    # a C caller's zero-initialised struct is row-major
+    z = B.MoeParams()
+    z.num_tokens, z.num_experts, z.top_k, z.hidden_size, z.intermediate_size = 4, 8, 2, 128, 256
+    z.act_dtype = z.weight_dtype = z.out_dtype = B.BF16
+    assert z.weight_layout == B.LAYOUT_ROW_MAJOR
+    assert L.moe_forward(ctypes.byref(z), FAKE, FAKE, None, FAKE, None, FAKE, None, None, None,
+                         None, None, FAKE, None, None, FAKE, need, None) == B.MOE_ERR_UNSUPPORTED
+    # routing and the permutation take no weights: the layout is irrelevant there
+    assert L.moe_topk(ctypes.byref(p), None, None, FAKE, FAKE, None) == B.MOE_ERR_INVALID
+    assert L.moe_align_permute(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, 0,
+                               None) == B.MOE_ERR_WORKSPACE
+
+
+def test_shared_intermediate_sizes_the_workspace():
+    """Each I-wide slice of the shared expert adds T rows of activations."""
+    one = B.moe_workspace_size(_p(num_tokens=64, num_shared_experts=1))
+    two = B.moe_workspace_size(_p(num_tokens=64, num_shared_experts=1, shared_intermediate=512))
+    four = B.moe_workspace_size(_p(num_tokens=64, num_shared_experts=1, shared_intermediate=1024))
+    assert 0 < one < two < four
+    assert B.moe_workspace_size(_p(num_tokens=64, num_shared_experts=1,
+                                   shared_intermediate=256)) == one

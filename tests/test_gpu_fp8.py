@@ -35,6 +35,14 @@ FP8_SMALL = {
     "fp8_clipped_swiglu": MC("fp8_clipped_swiglu", E=8, K=2, H=512, I=384, T=77, w_dtype="fp8",
                              shared=1, seed=24, weight_seed=24, swiglu_alpha=1.702,
                              swiglu_limit=0.5),
+    # shared expert of twice the routed intermediate size: per-k-block scale
+    # copies (I = 256, two k-blocks) and grouped ones (I = 512, four)
+    "fp8_shared_2I": MC("fp8_shared_2I", E=16, K=4, H=256, I=256, T=100, w_dtype="fp8",
+                        scoring="sigmoid", n_group=4, topk_group=2, rsf=2.5, correction_bias=True,
+                        shared=1, shared_I=512, seed=26, weight_seed=26, delta=1e-4),
+    "fp8_shared_2I_grouped_scales": MC("fp8_shared_2I_grouped_scales", E=8, K=2, H=512, I=512,
+                                       T=77, w_dtype="fp8", shared=1, shared_I=1024, seed=27,
+                                       weight_seed=27),
 }
 
 
@@ -120,13 +128,21 @@ def test_full_size_dsv3_fp8():
     got_w = wts.cpu().numpy().astype(np.float64)
     assert np.max(np.abs(got_w - ref_w) / np.abs(ref_w)) <= U.WEIGHT_RTOL
     rng = np.random.default_rng(5)
-    sample = sorted(set([0, T - 1] + rng.choice(T, size=10, replace=False).tolist()))
+    # random tokens, T-1 (the last row of the shared expert), and the tokens
+    # of the last row of up to 64 experts spread over all of them: rows of
+    # each expert's ragged last m-tile
+    st = Stages(layer, T)
+    st.topk(inp["router_logits"], inp.get("e_score_correction_bias"))
+    st.align()
+    torch.cuda.synchronize()
+    last_tokens = U.last_row_tokens(st.offsets.cpu().numpy(), st.sorted.cpu().numpy(), cfg.K)
+    sample = sorted(set([0, T - 1] + rng.choice(T, size=10, replace=False).tolist() + last_tokens))
     experts = np.unique(ref_ids[sample])
     ref = O.moe_forward_tokens(U.oracle_layer(cfg, inp, T, experts=experts), sample, nthreads=16)
     err = U.rel_err(U.out_to_f64(out[sample]), ref)
     print("  sampled %d rows: max|err|/max|ref| = %.3e" % (len(sample), err), flush=True)
     assert err <= U.TOL["fp8"]
-    del layer, inp
+    del layer, st, inp
     torch.cuda.empty_cache()
 
 

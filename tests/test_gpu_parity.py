@@ -78,6 +78,19 @@ SMALL = {
     # shared expert's 880 rows one of 112, and w2 splits K in two
     "tail_tiles": MC("tail_tiles", E=3, K=1, H=512, I=2048, T=880, shared=1, seed=31,
                      weight_seed=31),
+    # a shared expert wider than the routed ones (Is = m * I, computed as m
+    # I-wide slices): tile, 256 x 256 / tail / K-split, weight-streaming,
+    # fp32 and non-gated paths
+    "shared_2I": MC("shared_2I", E=8, K=2, H=512, I=448, T=300, shared=1, shared_I=896, seed=33,
+                    weight_seed=33),
+    "shared_3I_tail": MC("shared_3I_tail", E=3, K=1, H=512, I=2048, T=880, shared=1,
+                         shared_I=6144, seed=34, weight_seed=34),
+    "shared_2I_decode": MC("shared_2I_decode", E=8, K=2, H=512, I=256, T=5, shared=1,
+                           shared_I=512, seed=35, weight_seed=35),
+    "shared_2I_f32": MC("shared_2I_f32", E=6, K=3, H=192, I=320, T=97, act_dtype="f32",
+                        w_dtype="f32", shared=1, shared_I=640, seed=36, weight_seed=36),
+    "shared_2I_non_gated": MC("shared_2I_non_gated", E=8, K=2, H=512, I=448, T=300,
+                              non_gated=True, shared=1, shared_I=896, seed=37, weight_seed=37),
 }
 
 
@@ -185,11 +198,10 @@ def test_full_size_layer(name):
     torch.cuda.synchronize()
     _check_permutation(cfg, st, ref_ids)
     rng = np.random.default_rng(cfg.seed)
-    # random tokens, plus the token of the last row of the first 8 non-empty
-    # expert segments (rows of ragged or tail m-tiles)
-    off = st.offsets.cpu().numpy()
-    ends = [off[e + 1] - 1 for e in range(cfg.E) if off[e + 1] > off[e]][:8]
-    last_tokens = (st.sorted.cpu().numpy()[ends] // cfg.K).tolist()
+    # random tokens, plus the token of the last row of non-empty expert
+    # segments (rows of ragged or tail m-tiles), of at most 64 experts spread
+    # evenly over all of them
+    last_tokens = U.last_row_tokens(st.offsets.cpu().numpy(), st.sorted.cpu().numpy(), cfg.K)
     sample = sorted(set([0, T - 1] + rng.choice(T, size=min(T, 10), replace=False).tolist() + last_tokens))
     experts = np.unique(ref_ids[sample])
     ref = O.moe_forward_tokens(U.oracle_layer(cfg, inp, T, experts=experts), sample, nthreads=16)

@@ -13,18 +13,27 @@ import pytest
 BM, GM, TAIL = 256, 8, 128
 
 
-def _segments(counts, shared_rows):
+def _segments(counts, shared):
+    """Expert segments, then the shared expert's slices: shared = (T, slices),
+    each slice one segment of T rows."""
+    T, slices = shared
     offs = np.concatenate([[0], np.cumsum(counts)])
     segs = [(int(offs[e]), int(offs[e + 1])) for e in range(len(counts))]
     base = int(offs[-1])
-    segs.append((base, base + shared_rows))
+    for j in range(slices):
+        segs.append((base + j * T, base + (j + 1) * T))
     return segs
 
 
-def build_tail(counts, shared_rows):
+def _max_m(counts, shared, E):
+    T, slices = shared
+    return -(-(sum(counts) + T * slices) // BM) + E + slices
+
+
+def build_tail(counts, shared):
     """Tiles and unit table of the schedule with tail tiles."""
     tiles, units = [], []
-    for r0, r1 in _segments(counts, shared_rows):
+    for r0, r1 in _segments(counts, shared):
         rem = (r1 - r0) % BM
         tail = 1 if 0 < rem <= TAIL else 0
         nmain = (r1 - r0) // BM + (1 if rem > 0 and not tail else 0)
@@ -45,10 +54,10 @@ def build_tail(counts, shared_rows):
     return tiles, units
 
 
-def run_tail(counts, shared_rows, n_tiles_n, nparts, E):
-    tiles, units = build_tail(counts, shared_rows)
+def run_tail(counts, shared, n_tiles_n, nparts, E):
+    tiles, units = build_tail(counts, shared)
     assert all(u is not None for u in units)
-    max_m = -(-(sum(counts) + shared_rows) // BM) + E + 1
+    max_m = _max_m(counts, shared, E)
     assert len(tiles) <= max_m and len(units) <= 2 * max_m
     half = n_tiles_n * nparts // 2
     blocks = 8 * -(-(2 * max_m * half) // 8)
@@ -78,16 +87,16 @@ def run_tail(counts, shared_rows, n_tiles_n, nparts, E):
             assert k not in seen
             seen.add(k)
     assert len(seen) == len(tiles) * nparts * n_tiles_n
-    rows = np.zeros(sum(counts) + shared_rows, int)
+    rows = np.zeros(sum(counts) + shared[0] * shared[1], int)
     for r0, r1 in tiles:
         rows[r0:r1] += 1
     assert (rows == 1).all()
 
 
-def build_split(counts, shared_rows, nn):
+def build_split(counts, shared, nn):
     """Tiles (row0, row1, group) and the split of the K-split schedule."""
     tiles = []
-    for r0, r1 in _segments(counts, shared_rows):
+    for r0, r1 in _segments(counts, shared):
         nt = -(-(r1 - r0) // BM)
         start = len(tiles)
         ng = -(-nt // GM) if nt else 0
@@ -113,10 +122,10 @@ def _tile_at(t, m0, nn, tiles):
     return first + w % cnt, w // cnt
 
 
-def run_split(counts, shared_rows, nn, parts, E):
-    tiles, ns, split_row = build_split(counts, shared_rows, nn)
+def run_split(counts, shared, nn, parts, E):
+    tiles, ns, split_row = build_split(counts, shared, nn)
     nt = len(tiles)
-    max_m = -(-(sum(counts) + shared_rows) // BM) + E + 1
+    max_m = _max_m(counts, shared, E)
     blocks = 8 * (-(-(max_m * nn) // 8) + -(-(max_m * nn * parts) // 8))
     pos_a, pos_b = (nt - ns) * nn, ns * nn * parts
     per_a, per_b = -(-pos_a // 8), -(-pos_b // 8)
@@ -152,13 +161,15 @@ def run_split(counts, shared_rows, nn, parts, E):
 _RNG = np.random.default_rng(2)
 _Z = 1.0 / np.arange(1, 129) ** 1.2
 CASES = [
-    ("mixtral", _RNG.multinomial(8192, [1 / 8] * 8), 0, 8),
-    ("dsv3", _RNG.multinomial(65536, [1 / 256] * 256), 8192, 256),
-    ("qwen_zipf", _RNG.multinomial(131072, _Z / _Z.sum()), 0, 128),
-    ("edges", np.array([0, 1, 128, 129, 255, 256, 257, 384, 385, 512, 2053, 2248, 4096, 2404]), 300, 14),
-    ("many_groups", np.array([3000, 10, 0, 2600]), 0, 4),
-    ("one_small_expert", np.array([100]), 0, 1),
-    ("empty", np.array([0, 0, 0]), 0, 3),
+    ("mixtral", _RNG.multinomial(8192, [1 / 8] * 8), (4096, 0), 8),
+    ("dsv3", _RNG.multinomial(65536, [1 / 256] * 256), (8192, 1), 256),
+    ("dsv3_shared_2I", _RNG.multinomial(65536, [1 / 256] * 256), (8192, 2), 256),
+    ("qwen_zipf", _RNG.multinomial(131072, _Z / _Z.sum()), (16384, 0), 128),
+    ("edges", np.array([0, 1, 128, 129, 255, 256, 257, 384, 385, 512, 2053, 2248, 4096, 2404]),
+     (300, 3), 14),
+    ("many_groups", np.array([3000, 10, 0, 2600]), (2000, 0), 4),
+    ("one_small_expert", np.array([100]), (100, 0), 1),
+    ("empty", np.array([0, 0, 0]), (0, 0), 3),
 ]
 
 
