@@ -310,6 +310,30 @@ int moe_forward(const moe_params *p, const void *hidden,
                 void *out, int32_t *topk_ids_out, float *topk_weights_out,
                 void *workspace, size_t workspace_bytes, void *stream);
 
+/* moe_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same layer, arguments and result as moe_forward (bitwise), but no
+ * workspace argument.  The workspace is a 64 MiB device array of the library
+ * itself, one per GPU, held from the first call on that GPU until the process
+ * ends.  Layers whose moe_workspace_size exceeds 64 MiB (decode and small
+ * prefill batches fit: e.g. the DeepSeek-V3 shape up to a few hundred
+ * tokens) return MOE_ERR_WORKSPACE before anything is launched; use
+ * moe_forward with a workspace for those.  The call allocates nothing.  All
+ * calls on one GPU share its array: calls that overlap in time on one GPU
+ * (different streams, or host threads) race and give wrong results, so
+ * serialise them (one stream).  `stream` must belong to the current device
+ * (else MOE_ERR_INVALID).  Errors: as moe_forward, plus MOE_ERR_WORKSPACE
+ * for layers beyond the array. */
+int moe_forward_noalloc(const moe_params *p, const void *hidden,
+                        const float *router_logits,
+                        const float *e_score_correction_bias, const void *w13,
+                        const float *w13_scale, const void *w2,
+                        const float *w2_scale, const void *shared_w13,
+                        const float *shared_w13_scale, const void *shared_w2,
+                        const float *shared_w2_scale, void *out,
+                        int32_t *topk_ids_out, float *topk_weights_out,
+                        void *stream);
+
 /* Measurement helpers (not steps of the method): what this GPU reaches, to
  * print beside the published peaks.  The caller times the launch.
  *   moe_peak_mfma_bf16: `blocks` blocks of 256 threads; every wave runs

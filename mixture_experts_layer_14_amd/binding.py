@@ -26,7 +26,7 @@ ENTRY_POINTS = (
     "moe_workspace_size", "moe_status_string", "moe_pack_weights", "moe_topk",
     "moe_align_permute", "moe_quant_act_fp8", "moe_grouped_gemm_w13_act",
     "moe_grouped_gemm_w2_combine", "moe_forward", "moe_router_gemm",
-    "moe_peak_mfma_bf16", "moe_peak_read",
+    "moe_peak_mfma_bf16", "moe_peak_read", "moe_forward_noalloc",
 )
 
 
@@ -86,6 +86,7 @@ def load(path: str = LIB_PATH):
     L.moe_grouped_gemm_w13_act.argtypes = [_P] + [_VP] * 12 + [ctypes.c_size_t, _VP]
     L.moe_grouped_gemm_w2_combine.argtypes = [_P] + [_VP] * 12 + [ctypes.c_size_t, _VP]
     L.moe_forward.argtypes = [_P] + [_VP] * 15 + [ctypes.c_size_t, _VP]
+    L.moe_forward_noalloc.argtypes = [_P] + [_VP] * 14 + [_VP]
     L.moe_router_gemm.argtypes = [_P, _VP, _VP, ctypes.c_int32, _VP, _VP, ctypes.c_size_t, _VP]
     L.moe_peak_mfma_bf16.argtypes = [ctypes.c_int64, ctypes.c_int32, _VP, _VP]
     L.moe_peak_read.argtypes = [_VP, ctypes.c_int64, ctypes.c_int32, _VP, _VP]
@@ -230,6 +231,17 @@ def moe_forward(p, hidden, router_logits, e_score_correction_bias, w13, w13_scal
         _ptr(topk_ids_out), _ptr(topk_weights_out), _ptr(workspace), _nbytes(workspace),
         _stream(stream))
     return _check("moe_forward", st, raise_on_error)
+
+
+def moe_forward_noalloc(p, hidden, router_logits, e_score_correction_bias, w13, w13_scale, w2,
+                        w2_scale, shared_w13, shared_w13_scale, shared_w2, shared_w2_scale, out,
+                        topk_ids_out, topk_weights_out, stream=None, raise_on_error=True):
+    st = load().moe_forward_noalloc(
+        ctypes.byref(p), _ptr(hidden), _ptr(router_logits), _ptr(e_score_correction_bias),
+        _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), _ptr(shared_w13),
+        _ptr(shared_w13_scale), _ptr(shared_w2), _ptr(shared_w2_scale), _ptr(out),
+        _ptr(topk_ids_out), _ptr(topk_weights_out), _stream(stream))
+    return _check("moe_forward_noalloc", st, raise_on_error)
 
 
 def moe_peak_mfma_bf16(iters, blocks, sink, stream=None, raise_on_error=True):

@@ -3,6 +3,8 @@
 // allocates memory.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "moe_internal.h"
 
@@ -371,6 +373,76 @@ int moe_forward(const moe_params* p, const void* hidden, const float* router_log
     if (st != MOE_OK) return st;
     return w2_combine(p, act, act_scale, w2, w2_scale, shared_w2, shared_w2_scale, offsets,
                       sorted, inv, wts, out, scratch, scratch_bytes, stream, &built);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// moe_forward_noalloc: moe_forward on a workspace of the library's own, for
+// callers that cannot allocate device memory.
+// ---------------------------------------------------------------------------
+
+// The workspace of moe_forward_noalloc: a device array of the library, one
+// copy on each GPU the library runs on, held until the process ends.  In host
+// code `scratch` names a host-side stand-in, never the device memory: the
+// device address comes from hipGetSymbolAddress, once per device, with that
+// device current, and only that address is handed to kernels.
+static constexpr size_t kNoAllocBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocBytes];
+
+namespace {
+
+constexpr int kNoAllocMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kNoAllocMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on that device).
+int scratch_address(void* stream, void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+    if (dev < 0 || dev >= kNoAllocMaxDevices) return MOE_ERR_UNSUPPORTED;
+    if (stream) {  // the stream must belong to the current device
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess) return MOE_ERR_HIP;
+        if (sdev != dev) return MOE_ERR_INVALID;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MOE_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward_noalloc(const moe_params* p, const void* hidden, const float* router_logits,
+                        const float* e_score_correction_bias, const void* w13,
+                        const float* w13_scale, const void* w2, const float* w2_scale,
+                        const void* shared_w13, const float* shared_w13_scale,
+                        const void* shared_w2, const float* shared_w2_scale, void* out,
+                        int32_t* topk_ids_out, float* topk_weights_out, void* stream) {
+    int st = check_params(p);
+    if (st != MOE_OK) return st;
+    // larger layers than the array holds take moe_forward with a workspace
+    if (forward_layout(p).total > kNoAllocBytes) return MOE_ERR_WORKSPACE;
+    if (p->num_tokens == 0) return moe_forward(p, hidden, router_logits, e_score_correction_bias, w13,
+                                               w13_scale, w2, w2_scale, shared_w13, shared_w13_scale,
+                                               shared_w2, shared_w2_scale, out, topk_ids_out,
+                                               topk_weights_out, nullptr, 0, stream);
+    void* ws = nullptr;
+    st = scratch_address(stream, &ws);
+    if (st != MOE_OK) return st;
+    // every kernel of moe_forward writes the workspace regions it reads
+    // later in the same call, so nothing has to start at zero
+    return moe_forward(p, hidden, router_logits, e_score_correction_bias, w13, w13_scale, w2,
+                       w2_scale, shared_w13, shared_w13_scale, shared_w2, shared_w2_scale, out,
+                       topk_ids_out, topk_weights_out, ws, kNoAllocBytes, stream);
 }
 
 }  // extern "C"

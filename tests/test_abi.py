@@ -220,3 +220,13 @@ def test_shared_intermediate_sizes_the_workspace():
     assert 0 < one < two < four
     assert B.moe_workspace_size(_p(num_tokens=64, num_shared_experts=1,
                                    shared_intermediate=256)) == one
+
+
+def test_noalloc_rejects_layers_beyond_its_array_on_the_host():
+    """moe_forward_noalloc refuses, before touching any device, a layer whose
+    workspace exceeds its 64 MiB array."""
+    L = B.load()
+    p = _p(num_tokens=65536, num_experts=256, top_k=8, hidden_size=7168, intermediate_size=2048)
+    assert B.moe_workspace_size(p) > 64 << 20
+    assert L.moe_forward_noalloc(ctypes.byref(p), *([FAKE] * 2), None, *([FAKE] * 11),
+                                 None) == B.MOE_ERR_WORKSPACE
