@@ -172,9 +172,11 @@ def time_layer(cfg, inp, steps, warmup):
 
 
 def time_router(cfg, T, gate_dtype, steps, warmup):
-    """moe_router_gemm (the router gate GEMM ahead of moe_topk) alone, HIP
-    events on its stream; algorithmic bytes = hidden + gate + logits, FLOPs =
-    2 T E H; its roofline is the larger of the two times at the MI355X peaks."""
+    """moe_router_gemm (the router gate GEMM ahead of moe_topk) alone, and
+    moe_router_topk (gate GEMM and top-k, no logits kept), HIP events on their
+    stream; algorithmic bytes = hidden + gate + logits (GEMM) or + ids and
+    weights (fused), FLOPs = 2 T E H; the roofline is the larger of the two
+    times at the MI355X peaks."""
     import torch
 
     from mixture_experts_layer_14_amd import binding, synth
@@ -185,25 +187,40 @@ def time_router(cfg, T, gate_dtype, steps, warmup):
     p = params_for(cfg, T)
     ws = torch.empty(max(binding.moe_workspace_size(p), 256), dtype=torch.uint8, device="cuda")
     out = torch.empty(T, cfg.E, dtype=torch.float32, device="cuda")
+    ids = torch.empty(T, cfg.K, dtype=torch.int32, device="cuda")
+    wts = torch.empty(T, cfg.K, dtype=torch.float32, device="cuda")
+    b_ = synth.make_correction_bias(cfg)
+    bias = None if b_ is None else torch.from_numpy(b_).cuda()
+    p.scoring_func = binding.SIGMOID if cfg.scoring == "sigmoid" else binding.SOFTMAX
+    p.num_expert_group, p.topk_group, p.routed_scaling_factor = cfg.n_group, cfg.topk_group, cfg.rsf
     stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        binding.moe_router_gemm(p, x, g, out, ws)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(steps):
-        binding.moe_router_gemm(p, x, g, out, ws)
-    b.record(stream)
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / steps
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    ms = timed(lambda: binding.moe_router_gemm(p, x, g, out, ws))
+    ms_f = timed(lambda: binding.moe_router_topk(p, x, g, bias, ids, wts, None, ws))
     x_b = 4 if cfg.act_dtype == "f32" else 2
-    byts = T * cfg.H * x_b + cfg.E * cfg.H * (4 if gate_dtype == "f32" else 2) + T * cfg.E * 4
+    base = T * cfg.H * x_b + cfg.E * cfg.H * (4 if gate_dtype == "f32" else 2)
+    byts, byts_f = base + T * cfg.E * 4, base + T * cfg.K * 8
     flops = 2.0 * T * cfg.E * cfg.H
-    t_roof = max(byts / (PEAK_HBM_GBS * 1e9), flops / (PEAK_BF16_TFLOPS * 1e12))
+    t_f = flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_roof = max(byts / (PEAK_HBM_GBS * 1e9), t_f)
+    t_roof_f = max(byts_f / (PEAK_HBM_GBS * 1e9), t_f)
     del x, g, ws, out
     return {"workload": "%s router T=%d E=%d H=%d gate %s" % (cfg.name, T, cfg.E, cfg.H, gate_dtype),
             "us": ms * 1e3, "GBps": byts / (ms * 1e-3) / 1e9,
             "tflops": flops / (ms * 1e-3) / 1e12, "roofline_frac": t_roof / (ms * 1e-3),
-            "bound": "hbm" if byts / (PEAK_HBM_GBS * 1e9) >= flops / (PEAK_BF16_TFLOPS * 1e12) else "mfma"}
+            "bound": "hbm" if byts / (PEAK_HBM_GBS * 1e9) >= t_f else "mfma",
+            "router_topk_us": ms_f * 1e3, "router_topk_roofline_frac": t_roof_f / (ms_f * 1e-3)}
 
 
 def shared_streams(cfg_name, Ts, iters=50, warmup=5):

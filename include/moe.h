@@ -169,6 +169,28 @@ int moe_router_gemm(const moe_params *p, const void *hidden, const void *gate_w,
                     int32_t gate_dtype, float *router_logits, void *workspace,
                     size_t workspace_bytes, void *stream);
 
+/* Router gate GEMM and top-k in one call (the gate, then select_experts),
+ * with no fp32 [T, E] logits written unless asked for.
+ * Passages: MoEGate (SGLang deepseek_v2 page: gate [n_routed_experts,
+ * hidden_size], fp32 logits; a skinny GEMM at decode that the page gives
+ * its own kernel) ahead of FusedMoE.select_experts (vLLM page) with the
+ * DeepseekV2MoE grouped top-k arguments.
+ *   hidden, gate_w, gate_dtype: as moe_router_gemm.
+ *   e_score_correction_bias, topk_ids, topk_weights: as moe_topk.
+ *   router_logits  [T, E] fp32 out, or NULL: the logits (bitwise those of
+ *                  moe_router_gemm).
+ * The GEMM writes partial logits of a split hidden dimension (decode sizes)
+ * into the workspace, and the top-k kernel adds them in a fixed order as it
+ * reads them, so the ids and weights are bitwise those of moe_router_gemm
+ * followed by moe_topk; two launches in all.
+ *   workspace      >= moe_workspace_size(p) bytes (unused when there is one
+ *                  part and router_logits is given).
+ * Errors: as moe_router_gemm and moe_topk. */
+int moe_router_topk(const moe_params *p, const void *hidden, const void *gate_w,
+                    int32_t gate_dtype, const float *e_score_correction_bias,
+                    int32_t *topk_ids, float *topk_weights, float *router_logits,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
 /* Router: top-k expert selection and routing weights per token.
  * Passage: FusedMoE.select_experts (vLLM page), grouped top-k and
  * e_score_correction_bias (vLLM page; DeepseekV2MoE TopK arguments and

@@ -26,7 +26,7 @@ ENTRY_POINTS = (
     "moe_workspace_size", "moe_status_string", "moe_pack_weights", "moe_topk",
     "moe_align_permute", "moe_quant_act_fp8", "moe_grouped_gemm_w13_act",
     "moe_grouped_gemm_w2_combine", "moe_forward", "moe_router_gemm",
-    "moe_peak_mfma_bf16", "moe_peak_read", "moe_forward_noalloc",
+    "moe_peak_mfma_bf16", "moe_peak_read", "moe_forward_noalloc", "moe_router_topk",
 )
 
 
@@ -88,6 +88,8 @@ def load(path: str = LIB_PATH):
     L.moe_forward.argtypes = [_P] + [_VP] * 15 + [ctypes.c_size_t, _VP]
     L.moe_forward_noalloc.argtypes = [_P] + [_VP] * 14 + [_VP]
     L.moe_router_gemm.argtypes = [_P, _VP, _VP, ctypes.c_int32, _VP, _VP, ctypes.c_size_t, _VP]
+    L.moe_router_topk.argtypes = [_P, _VP, _VP, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP,
+                                  ctypes.c_size_t, _VP]
     L.moe_peak_mfma_bf16.argtypes = [ctypes.c_int64, ctypes.c_int32, _VP, _VP]
     L.moe_peak_read.argtypes = [_VP, ctypes.c_int64, ctypes.c_int32, _VP, _VP]
     # every entry point taking pointers must declare them (a bare Python int
@@ -219,6 +221,19 @@ def moe_router_gemm(p, hidden, gate_w, router_logits, workspace, gate_dtype=None
                                 _ptr(router_logits), _ptr(workspace), _nbytes(workspace),
                                 _stream(stream))
     return _check("moe_router_gemm", st, raise_on_error)
+
+
+def moe_router_topk(p, hidden, gate_w, e_score_correction_bias, topk_ids, topk_weights,
+                    router_logits, workspace, gate_dtype=None, stream=None, raise_on_error=True):
+    """Router gate GEMM and top-k in one call: ids and weights into topk_ids /
+    topk_weights, the logits into router_logits unless it is None."""
+    if gate_dtype is None:
+        gate_dtype = F32 if gate_w is not None and gate_w.dtype == torch.float32 else BF16
+    st = load().moe_router_topk(ctypes.byref(p), _ptr(hidden), _ptr(gate_w), int(gate_dtype),
+                                _ptr(e_score_correction_bias), _ptr(topk_ids), _ptr(topk_weights),
+                                _ptr(router_logits), _ptr(workspace), _nbytes(workspace),
+                                _stream(stream))
+    return _check("moe_router_topk", st, raise_on_error)
 
 
 def moe_forward(p, hidden, router_logits, e_score_correction_bias, w13, w13_scale, w2, w2_scale,

@@ -184,7 +184,7 @@ int moe_topk(const moe_params* p, const float* router_logits, const float* e_sco
     st = check_topk_args(p, router_logits, e_score_correction_bias, topk_ids, topk_weights);
     if (st != MOE_OK) return st;
     const int G = p->num_expert_group > 1 ? p->num_expert_group : 1;
-    return hip_status(moe::launch_topk(router_logits, e_score_correction_bias, p->num_tokens,
+    return hip_status(moe::launch_topk(router_logits, 1, nullptr, e_score_correction_bias, p->num_tokens,
                                        p->num_experts, p->top_k, p->scoring_func,
                                        p->renormalize ? 1 : 0, G, G > 1 ? p->topk_group : 1,
                                        p->routed_scaling_factor, topk_ids, topk_weights,
@@ -314,12 +314,44 @@ int moe_router_gemm(const moe_params* p, const void* hidden, const void* gate_w,
     if (p->num_tokens == 0) return MOE_OK;  // empty batch: nothing to do
     if (!hidden || !gate_w || !router_logits) return MOE_ERR_INVALID;
     if (p->act_dtype != MOE_DTYPE_F32 && p->act_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
-    const size_t need = moe::router_workspace_bytes(p->num_tokens, p->num_experts,
-                                                    p->hidden_size, p->act_dtype);
+    // partial logits of a split H only
+    const int parts = p->act_dtype == MOE_DTYPE_BF16
+                          ? moe::router_parts(p->num_tokens, p->num_experts, p->hidden_size) : 1;
+    const size_t need = parts > 1 ? static_cast<size_t>(parts) * p->num_tokens * p->num_experts * 4 : 0;
     if (need && (!workspace || workspace_bytes < need)) return MOE_ERR_WORKSPACE;
     return hip_status(moe::launch_router(hidden, p->act_dtype, gate_w, gate_dtype, p->num_tokens,
                                          p->num_experts, p->hidden_size, router_logits, workspace,
                                          as_stream(stream)));
+}
+
+int moe_router_topk(const moe_params* p, const void* hidden, const void* gate_w, int32_t gate_dtype,
+                    const float* e_score_correction_bias, int32_t* topk_ids, float* topk_weights,
+                    float* router_logits, void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_params(p);
+    if (st != MOE_OK) return st;
+    if (gate_dtype != MOE_DTYPE_F32 && gate_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (p->num_tokens == 0) return MOE_OK;  // empty batch: nothing to do
+    if (!hidden || !gate_w || !topk_ids || !topk_weights) return MOE_ERR_INVALID;
+    if (e_score_correction_bias && p->scoring_func != MOE_SCORING_SIGMOID) return MOE_ERR_INVALID;
+    if (p->act_dtype != MOE_DTYPE_F32 && p->act_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+    const int64_t T = p->num_tokens;
+    const int E = p->num_experts, H = p->hidden_size;
+    const int parts = p->act_dtype == MOE_DTYPE_BF16 ? moe::router_parts(T, E, H) : 1;
+    // one part straight into the caller's logits when it keeps them
+    const bool direct = parts == 1 && router_logits;
+    const size_t need = direct ? 0 : static_cast<size_t>(parts) * T * E * 4;
+    if (need && (!workspace || workspace_bytes < need)) return MOE_ERR_WORKSPACE;
+    float* partials = direct ? router_logits : static_cast<float*>(workspace);
+    int got = 1;
+    hipError_t err = moe::launch_router_partials(hidden, p->act_dtype, gate_w, gate_dtype, T, E, H,
+                                                 partials, &got, as_stream(stream));
+    if (err != hipSuccess) return hip_status(err);
+    const int G = p->num_expert_group > 1 ? p->num_expert_group : 1;
+    return hip_status(moe::launch_topk(partials, got, direct ? nullptr : router_logits,
+                                       e_score_correction_bias, T, E, p->top_k, p->scoring_func,
+                                       p->renormalize ? 1 : 0, G, G > 1 ? p->topk_group : 1,
+                                       p->routed_scaling_factor, topk_ids, topk_weights,
+                                       as_stream(stream)));
 }
 
 int moe_forward(const moe_params* p, const void* hidden, const float* router_logits,

@@ -28,9 +28,11 @@ struct GroupUnit {
     int32_t first_unit;
 };
 
-hipError_t launch_topk(const float* logits, const float* bias, int64_t T, int E, int K,
-                       int scoring, int renorm, int G, int TG, float rsf, int32_t* ids,
-                       float* weights, hipStream_t stream);
+// Top-k routing of `parts` partial logit arrays [parts][T][E] (summed in
+// part order; 1: plain logits), optionally storing the summed logits.
+hipError_t launch_topk(const float* logits, int parts, float* logits_out, const float* bias,
+                       int64_t T, int E, int K, int scoring, int renorm, int G, int TG, float rsf,
+                       int32_t* ids, float* weights, hipStream_t stream);
 
 int64_t align_chunk(int64_t n);
 size_t align_workspace_bytes(int64_t n, int E);
@@ -91,8 +93,16 @@ hipError_t launch_w2_combine(const GroupedProblem& p, const void* act, const flo
                              hipStream_t stream);
 
 // Router gate logits (moe_router.hip); dtypes are MOE_DTYPE_* values.
+// Parts of H the bf16 GEMM splits into (partial logits summed by the consumer).
 int router_parts(int64_t T, int E, int H);
+// Workspace of the fused router + top-k: the partial logits, or one logits
+// array when there is one part (the larger of the two router uses).
 size_t router_workspace_bytes(int64_t T, int E, int H, int act_dtype);
+// Partial logits [parts][T][E] into `partials`; *parts_out = parts used.
+hipError_t launch_router_partials(const void* hidden, int act_dtype, const void* gate,
+                                  int gate_dtype, int64_t T, int E, int H, float* partials,
+                                  int* parts_out, hipStream_t stream);
+// Logits [T, E] (partials, when H is split, in ws, then summed).
 hipError_t launch_router(const void* hidden, int act_dtype, const void* gate, int gate_dtype,
                          int64_t T, int E, int H, float* logits, void* ws, hipStream_t stream);
 

@@ -4,12 +4,13 @@
 // forward returns F.linear(hidden.float(), weight) for an fp32 gate and a
 // bf16 GEMM with fp32 output for a bf16 gate).
 //
-// bf16 hidden: MFMA 32x32x16 bf16 tiles of 64 tokens x 64 experts, fp32
-// accumulation.  An fp32 gate is split on the fly into bf16 hi + lo parts
+// bf16 hidden: MFMA 32x32x16 bf16 tiles of 64 tokens x 64 experts (128 x 128
+// for many tokens), fp32 accumulation.  An fp32 gate is split on the fly into bf16 hi + lo parts
 // (hi = bf16(w), lo = bf16(w - hi), |w - hi - lo| <= 2^-16 |w|), two MFMAs per
 // step; each bf16 x bf16 product is exact in fp32, so the result keeps fp32
 // accuracy at bf16 MFMA rate.  Few tiles (decode) split H into parts whose
-// fp32 partial logits a second kernel sums in a fixed order.
+// fp32 partial logits a second kernel sums in a fixed order: the reduce
+// kernel (moe_router_gemm) or the top-k kernel itself (moe_router_topk).
 // fp32 hidden: one thread per logit, fp32 FMAs in order over H.
 #include "moe_device.h"
 #include "moe_internal.h"
@@ -17,50 +18,60 @@
 namespace moe {
 namespace {
 
-constexpr int kRBM = 64, kRBN = 64, kRK = 64;  // tile: tokens x experts x k per step
-constexpr int kRThreads = 256;                  // 4 waves, 2 x 2, each 32 x 32
+constexpr int kRK = 64;  // k per step (one 128-byte bf16 row slab)
 
 // 16-byte slot s of LDS row r (128-byte rows): XOR swizzle so the 32 rows one
 // MFMA operand read touches spread over all banks
 __device__ __forceinline__ int rslot(int r, int s) { return s ^ (r & 7); }
 
-template <bool GATE_F32>
-__global__ __launch_bounds__(kRThreads) void router_gemm_kernel(
+// Tile of BM tokens x BN experts on WM x WN waves (each wave (BM/WM) x
+// (BN/WN), 32 x 32 MFMA blocks); 64 x 64 on 4 waves for few tokens, 128 x
+// 128 on 8 waves for many (half the hidden and gate re-reads per logit, and
+// two independent MFMA chains per wave).
+template <bool GATE_F32, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM* WN* kWave) void router_gemm_kernel(
     const uint16_t* __restrict__ x, const void* __restrict__ gate, int64_t T, int E, int H,
     int parts, float* __restrict__ out) {
+    constexpr int NT = WM * WN * kWave;
+    constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
     constexpr int NB = GATE_F32 ? 2 : 1;  // gate planes in LDS: hi (and lo)
-    constexpr int STAGE = (kRBM + NB * kRBN) * kRK * 2;
+    constexpr int STAGE = (BM + NB * BN) * kRK * 2;
+    constexpr int A_LD = BM * 8 / NT;                        // 16-byte A loads per thread
+    constexpr int B_LD = BN * (GATE_F32 ? 16 : 8) / NT;      // 16-byte gate loads per thread
+    static_assert(BM * 8 % NT == 0 && BN * (GATE_F32 ? 16 : 8) % NT == 0, "loads split evenly");
+    static_assert(TM >= 1 && TN >= 1, "wave tile of whole 32 x 32 blocks");
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = wave_index(tid);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
     // block -> (token tile, expert tile): block b runs on XCD b % 8; each XCD
     // takes a contiguous eighth of the tiles in token-major order, so the
     // expert tiles of one token tile run together on one XCD and read its
     // hidden rows from that XCD's L2 (token-tile-fastest order re-read every
     // hidden row once per expert tile)
-    const int tiles_e = (E + kRBN - 1) / kRBN;
-    const int64_t tiles = ((T + kRBM - 1) / kRBM) * tiles_e;
+    const int tiles_e = (E + BN - 1) / BN;
+    const int64_t tiles = ((T + BM - 1) / BM) * tiles_e;
     const int64_t per = (tiles + 7) / 8;
     const int64_t pos = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
     if ((blockIdx.x >> 3) >= per || pos >= tiles) return;
-    const int64_t t0 = pos / tiles_e * kRBM;
-    const int e0 = static_cast<int>(pos % tiles_e) * kRBN;
+    const int64_t t0 = pos / tiles_e * BM;
+    const int e0 = static_cast<int>(pos % tiles_e) * BN;
     const int part = blockIdx.z;
     const int nk_all = H / kRK;
     const int k_first = part * nk_all / parts;
     const int nk = (part + 1) * nk_all / parts - k_first;
 
-    // loads of one k-step into registers: A 2 x 16 B, gate 2 x 16 B (bf16)
-    // or 4 x 16 B (fp32) per thread; rows past T or E repeat the last row
-    u32x4 ra[2], rb[GATE_F32 ? 4 : 2];
+    // loads of one k-step into registers: A (bf16) 8 chunks of 16 bytes per
+    // row, the gate 8 (bf16) or 16 (fp32) per row; rows past T or E repeat
+    // the last row (computed, never stored)
+    u32x4 ra[A_LD], rb[B_LD];
     auto load = [&](int kit) {
         const int64_t k0 = static_cast<int64_t>(k_first + kit) * kRK;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int idx = tid + j * kRThreads;
+        for (int j = 0; j < A_LD; ++j) {
+            const int idx = tid + j * NT;
             const int r = idx >> 3, s = idx & 7;
             const int64_t t = t0 + r < T ? t0 + r : T - 1;
             ra[j] = *reinterpret_cast<const u32x4*>(x + t * H + k0 + s * 8);
@@ -68,8 +79,8 @@ __global__ __launch_bounds__(kRThreads) void router_gemm_kernel(
         if constexpr (!GATE_F32) {
             const uint16_t* g = static_cast<const uint16_t*>(gate);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int idx = tid + j * kRThreads;
+            for (int j = 0; j < B_LD; ++j) {
+                const int idx = tid + j * NT;
                 const int r = idx >> 3, s = idx & 7;
                 const int64_t e = e0 + r < E ? e0 + r : E - 1;
                 rb[j] = *reinterpret_cast<const u32x4*>(g + e * H + k0 + s * 8);
@@ -77,8 +88,8 @@ __global__ __launch_bounds__(kRThreads) void router_gemm_kernel(
         } else {
             const float* g = static_cast<const float*>(gate);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int idx = tid + j * kRThreads;  // 4 floats each: 16 per row
+            for (int j = 0; j < B_LD; ++j) {
+                const int idx = tid + j * NT;  // 4 floats each: 16 per row
                 const int r = idx >> 4, c = (idx & 15) * 4;
                 const int64_t e = e0 + r < E ? e0 + r : E - 1;
                 rb[j] = *reinterpret_cast<const u32x4*>(g + e * H + k0 + c);
@@ -87,25 +98,25 @@ __global__ __launch_bounds__(kRThreads) void router_gemm_kernel(
     };
     auto store = [&](int buf) {
         uint8_t* sA = smem + buf * STAGE;
-        uint8_t* sB = sA + kRBM * kRK * 2;
+        uint8_t* sB = sA + BM * kRK * 2;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int idx = tid + j * kRThreads;
+        for (int j = 0; j < A_LD; ++j) {
+            const int idx = tid + j * NT;
             const int r = idx >> 3, s = idx & 7;
             *reinterpret_cast<u32x4*>(sA + r * 128 + rslot(r, s) * 16) = ra[j];
         }
         if constexpr (!GATE_F32) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int idx = tid + j * kRThreads;
+            for (int j = 0; j < B_LD; ++j) {
+                const int idx = tid + j * NT;
                 const int r = idx >> 3, s = idx & 7;
                 *reinterpret_cast<u32x4*>(sB + r * 128 + rslot(r, s) * 16) = rb[j];
             }
         } else {
-            uint8_t* sL = sB + kRBN * kRK * 2;
+            uint8_t* sL = sB + BN * kRK * 2;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int idx = tid + j * kRThreads;
+            for (int j = 0; j < B_LD; ++j) {
+                const int idx = tid + j * NT;
                 const int r = idx >> 4, c = (idx & 15) * 4;
                 uint32_t hi[2], lo[2];
 #pragma unroll
@@ -125,10 +136,14 @@ __global__ __launch_bounds__(kRThreads) void router_gemm_kernel(
         }
     };
 
-    f32x16 acc;
+    f32x16 acc[TM][TN];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-    const int ar = wm * 32 + (lane & 31), br = wn * 32 + (lane & 31), kh = lane >> 5;
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    const int kh = lane >> 5;
 
     load(0);
     store(0);
@@ -137,20 +152,34 @@ __global__ __launch_bounds__(kRThreads) void router_gemm_kernel(
         const int buf = kit & 1;
         if (kit + 1 < nk) load(kit + 1);
         const uint8_t* sA = smem + buf * STAGE;
-        const uint8_t* sB = sA + kRBM * kRK * 2;
+        const uint8_t* sB = sA + BM * kRK * 2;
 #pragma unroll
         for (int ks = 0; ks < kRK / 16; ++ks) {
             const int s = ks * 2 + kh;
-            const u32x4 a = *reinterpret_cast<const u32x4*>(sA + ar * 128 + rslot(ar, s) * 16);
-            const u32x4 b = *reinterpret_cast<const u32x4*>(sB + br * 128 + rslot(br, s) * 16);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                          __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
-            if constexpr (GATE_F32) {
-                const uint8_t* sL = sB + kRBN * kRK * 2;
-                const u32x4 bl = *reinterpret_cast<const u32x4*>(sL + br * 128 + rslot(br, s) * 16);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                              __builtin_bit_cast(bf16x8, bl), acc, 0, 0, 0);
+            u32x4 a[TM], b[TN], bl[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int ar = wm * (BM / WM) + i * 32 + (lane & 31);
+                a[i] = *reinterpret_cast<const u32x4*>(sA + ar * 128 + rslot(ar, s) * 16);
             }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int br = wn * (BN / WN) + j * 32 + (lane & 31);
+                b[j] = *reinterpret_cast<const u32x4*>(sB + br * 128 + rslot(br, s) * 16);
+                if constexpr (GATE_F32)
+                    bl[j] = *reinterpret_cast<const u32x4*>(sB + BN * kRK * 2 + br * 128 + rslot(br, s) * 16);
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, a[i]), __builtin_bit_cast(bf16x8, b[j]), acc[i][j], 0, 0, 0);
+                    if constexpr (GATE_F32)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8, a[i]), __builtin_bit_cast(bf16x8, bl[j]), acc[i][j], 0, 0,
+                            0);
+                }
         }
         __syncthreads();  // every wave is done with `buf` and with the other buffer
         if (kit + 1 < nk) {
@@ -159,14 +188,20 @@ __global__ __launch_bounds__(kRThreads) void router_gemm_kernel(
         }
     }
 
-    // acc[v] holds token row 8*(v/4) + 4*(lane/32) + v%4, expert column lane%32
+    // acc[i][j][v] holds token row i*32 + 8*(v/4) + 4*(lane/32) + v%4 and
+    // expert column j*32 + lane%32 of the wave tile
     float* o = out + static_cast<int64_t>(part) * T * E;
-    const int e = e0 + wn * 32 + (lane & 31);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int64_t t = t0 + wm * 32 + 8 * (v / 4) + 4 * (lane >> 5) + (v % 4);
-        if (t < T && e < E) o[t * E + e] = acc[v];
-    }
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int e = e0 + wn * (BN / WN) + j * 32 + (lane & 31);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t t = t0 + wm * (BM / WM) + i * 32 + 8 * (v / 4) + 4 * (lane >> 5) + (v % 4);
+                if (t < T && e < E) o[t * E + e] = acc[i][j][v];
+            }
+        }
 }
 
 // logits = sum of the parts' partial logits, in part order
@@ -198,47 +233,81 @@ __global__ __launch_bounds__(256) void router_f32_kernel(const float* __restrict
     out[i] = s;
 }
 
-}  // namespace
+// Tile and parts of H for the MFMA path.  Many tokens take the 128 x 128
+// tile; few take 64 x 64 with H split into parts (at least two k-steps each)
+// so that the blocks cover the chip, their fp32 partial logits summed in
+// part order by the consumer (router_reduce_kernel or the top-k kernel).
+struct RouterPlan {
+    bool big;
+    int parts;
+};
 
-// Parts of H for the MFMA path: enough blocks to cover the chip when there
-// are few tiles, at least two k-steps per part.
-int router_parts(int64_t T, int E, int H) {
-    const int64_t tiles = ((T + kRBM - 1) / kRBM) * ((E + kRBN - 1) / kRBN);
+RouterPlan router_plan(int64_t T, int E, int H) {
     const int nk_all = H / kRK;
-    int parts = 1;
-    while (parts < 32 && tiles * parts < 512 && nk_all / (parts * 2) >= 2) parts *= 2;
-    return parts;
+    const int64_t big_tiles = ((T + 127) / 128) * ((E + 127) / 128);
+    RouterPlan pl{big_tiles >= 64, 1};
+    const int64_t tiles = pl.big ? big_tiles : ((T + 63) / 64) * ((E + 63) / 64);
+    const int64_t want = pl.big ? 256 : 512;
+    while (pl.parts < 32 && tiles * pl.parts < want && nk_all / (pl.parts * 2) >= 2) pl.parts *= 2;
+    return pl;
 }
 
+}  // namespace
+
+int router_parts(int64_t T, int E, int H) { return router_plan(T, E, H).parts; }
+
 size_t router_workspace_bytes(int64_t T, int E, int H, int act_dtype) {
-    if (act_dtype != 1 /* bf16 */ || T <= 0) return 0;
-    const int parts = router_parts(T, E, H);
-    return parts > 1 ? static_cast<size_t>(parts) * T * E * sizeof(float) : 0;
+    if (T <= 0) return 0;
+    // the partial logits (bf16 hidden, split H), or one logits buffer for the
+    // fused router + top-k when the caller keeps no logits
+    const int parts = act_dtype == 1 /* bf16 */ ? router_parts(T, E, H) : 1;
+    return static_cast<size_t>(parts) * T * E * sizeof(float);
+}
+
+hipError_t launch_router_partials(const void* hidden, int act_dtype, const void* gate,
+                                  int gate_dtype, int64_t T, int E, int H, float* partials,
+                                  int* parts_out, hipStream_t stream) {
+    const bool gf32 = gate_dtype == 0;
+    if (act_dtype != 1) {  // fp32 hidden: one pass, no parts
+        const unsigned blocks = static_cast<unsigned>((T * E + 255) / 256);
+        if (gf32)
+            router_f32_kernel<true><<<blocks, 256, 0, stream>>>(static_cast<const float*>(hidden), gate, T, E, H, partials);
+        else
+            router_f32_kernel<false><<<blocks, 256, 0, stream>>>(static_cast<const float*>(hidden), gate, T, E, H, partials);
+        *parts_out = 1;
+        return hipGetLastError();
+    }
+    const RouterPlan pl = router_plan(T, E, H);
+    const uint16_t* x = static_cast<const uint16_t*>(hidden);
+    if (pl.big) {
+        const int64_t tiles = ((T + 127) / 128) * ((E + 127) / 128);
+        const dim3 grid(static_cast<unsigned>(8 * ((tiles + 7) / 8)), 1, static_cast<unsigned>(pl.parts));
+        if (gf32)
+            router_gemm_kernel<true, 128, 128, 2, 4><<<grid, 512, 0, stream>>>(x, gate, T, E, H, pl.parts, partials);
+        else
+            router_gemm_kernel<false, 128, 128, 2, 4><<<grid, 512, 0, stream>>>(x, gate, T, E, H, pl.parts, partials);
+    } else {
+        const int64_t tiles = ((T + 63) / 64) * ((E + 63) / 64);
+        const dim3 grid(static_cast<unsigned>(8 * ((tiles + 7) / 8)), 1, static_cast<unsigned>(pl.parts));
+        if (gf32)
+            router_gemm_kernel<true, 64, 64, 2, 2><<<grid, 256, 0, stream>>>(x, gate, T, E, H, pl.parts, partials);
+        else
+            router_gemm_kernel<false, 64, 64, 2, 2><<<grid, 256, 0, stream>>>(x, gate, T, E, H, pl.parts, partials);
+    }
+    *parts_out = pl.parts;
+    return hipGetLastError();
 }
 
 hipError_t launch_router(const void* hidden, int act_dtype, const void* gate, int gate_dtype,
                          int64_t T, int E, int H, float* logits, void* ws, hipStream_t stream) {
-    const bool gf32 = gate_dtype == 0;
-    if (act_dtype != 1) {  // fp32 hidden
-        const unsigned blocks = static_cast<unsigned>((T * E + 255) / 256);
-        if (gf32)
-            router_f32_kernel<true><<<blocks, 256, 0, stream>>>(static_cast<const float*>(hidden), gate, T, E, H, logits);
-        else
-            router_f32_kernel<false><<<blocks, 256, 0, stream>>>(static_cast<const float*>(hidden), gate, T, E, H, logits);
-        return hipGetLastError();
-    }
-    const int parts = router_parts(T, E, H);
+    const int parts = act_dtype == 1 ? router_parts(T, E, H) : 1;
     float* dst = parts > 1 ? static_cast<float*>(ws) : logits;
-    const int64_t tiles = ((T + kRBM - 1) / kRBM) * ((E + kRBN - 1) / kRBN);
-    const dim3 grid(static_cast<unsigned>(8 * ((tiles + 7) / 8)), 1, static_cast<unsigned>(parts));
-    const uint16_t* x = static_cast<const uint16_t*>(hidden);
-    if (gf32)
-        router_gemm_kernel<true><<<grid, kRThreads, 0, stream>>>(x, gate, T, E, H, parts, dst);
-    else
-        router_gemm_kernel<false><<<grid, kRThreads, 0, stream>>>(x, gate, T, E, H, parts, dst);
-    if (parts > 1) {
+    int got = 1;
+    hipError_t err = launch_router_partials(hidden, act_dtype, gate, gate_dtype, T, E, H, dst, &got, stream);
+    if (err != hipSuccess) return err;
+    if (got > 1) {
         const int64_t n = T * E;
-        router_reduce_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, stream>>>(dst, n, parts, logits);
+        router_reduce_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, stream>>>(dst, n, got, logits);
     }
     return hipGetLastError();
 }

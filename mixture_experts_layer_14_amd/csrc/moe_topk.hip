@@ -15,6 +15,12 @@
 // Layout: lane l holds experts e = l + 64*v, v < VPL, so every row load is
 // a run of coalesced 256-byte wave accesses.  A selection round is one wave
 // arg-max over packed (ordered key bits << 32 | ~expert) 64-bit values.
+//
+// The logits may come as `parts` partial sums (the router gate GEMM with H
+// split into parts, parts * T * E floats): the kernel adds them in part
+// order, the order of router_reduce_kernel, so routing the router GEMM's
+// output through moe_router_gemm + moe_topk or through moe_router_topk gives
+// the same bits; with logits_out the summed logits are stored as well.
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -22,9 +28,9 @@ namespace moe {
 
 template <int VPL>
 __global__ __launch_bounds__(256) void topk_kernel(
-    const float* __restrict__ logits, const float* __restrict__ bias, int64_t T, int E, int K,
-    int scoring, int renorm, int G, int TG, float rsf, int32_t* __restrict__ ids,
-    float* __restrict__ weights) {
+    const float* __restrict__ logits, int parts, int64_t part_stride, float* __restrict__ logits_out,
+    const float* __restrict__ bias, int64_t T, int E, int K, int scoring, int renorm, int G, int TG,
+    float rsf, int32_t* __restrict__ ids, float* __restrict__ weights) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t t = static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave;
     if (t >= T) return;  // wave-uniform exit
@@ -37,6 +43,27 @@ __global__ __launch_bounds__(256) void topk_kernel(
         const int e = lane + kWave * v;
         cand[v] = e < E;
         key[v] = cand[v] ? row[e] : -INFINITY;
+    }
+    // the other parts, added in part order; the loads of 8 parts are issued
+    // before their adds, so a long split is not a chain of dependent loads
+    constexpr int PB = 8;
+    for (int p0 = 1; p0 < parts; p0 += PB) {
+        float pl[PB][VPL];
+#pragma unroll
+        for (int q = 0; q < PB; ++q)
+#pragma unroll
+            for (int v = 0; v < VPL; ++v)
+                pl[q][v] = (p0 + q < parts && cand[v]) ? row[(p0 + q) * part_stride + lane + kWave * v] : 0.0f;
+#pragma unroll
+        for (int q = 0; q < PB; ++q)
+#pragma unroll
+            for (int v = 0; v < VPL; ++v)
+                if (p0 + q < parts) key[v] += pl[q][v];
+    }
+    if (logits_out) {
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+            if (cand[v]) logits_out[t * E + lane + kWave * v] = key[v];
     }
 
     float softmax_sum = 0.0f, softmax_max = 0.0f;
@@ -144,21 +171,26 @@ __global__ __launch_bounds__(256) void topk_kernel(
     }
 }
 
-hipError_t launch_topk(const float* logits, const float* bias, int64_t T, int E, int K,
-                       int scoring, int renorm, int G, int TG, float rsf, int32_t* ids,
-                       float* weights, hipStream_t stream) {
+hipError_t launch_topk(const float* logits, int parts, float* logits_out, const float* bias,
+                       int64_t T, int E, int K, int scoring, int renorm, int G, int TG, float rsf,
+                       int32_t* ids, float* weights, hipStream_t stream) {
     const int waves_per_block = 4;
     const dim3 block(kWave * waves_per_block);
     const dim3 grid(static_cast<unsigned>((T + waves_per_block - 1) / waves_per_block));
     const int vpl = (E + kWave - 1) / kWave;
+    const int64_t ps = T * E;
+#define MOE_TOPK_LAUNCH(V)                                                                          \
+    topk_kernel<V><<<grid, block, 0, stream>>>(logits, parts, ps, logits_out, bias, T, E, K, scoring, \
+                                               renorm, G, TG, rsf, ids, weights)
     if (vpl <= 1)
-        topk_kernel<1><<<grid, block, 0, stream>>>(logits, bias, T, E, K, scoring, renorm, G, TG, rsf, ids, weights);
+        MOE_TOPK_LAUNCH(1);
     else if (vpl <= 2)
-        topk_kernel<2><<<grid, block, 0, stream>>>(logits, bias, T, E, K, scoring, renorm, G, TG, rsf, ids, weights);
+        MOE_TOPK_LAUNCH(2);
     else if (vpl <= 4)
-        topk_kernel<4><<<grid, block, 0, stream>>>(logits, bias, T, E, K, scoring, renorm, G, TG, rsf, ids, weights);
+        MOE_TOPK_LAUNCH(4);
     else
-        topk_kernel<8><<<grid, block, 0, stream>>>(logits, bias, T, E, K, scoring, renorm, G, TG, rsf, ids, weights);
+        MOE_TOPK_LAUNCH(8);
+#undef MOE_TOPK_LAUNCH
     return hipGetLastError();
 }
 

@@ -115,3 +115,93 @@ def test_router_then_topk_matches_oracle_routing():
     assert far.sum() > 0.9 * T
     assert np.array_equal(ids.cpu().numpy()[far], r_ids[far])
     np.testing.assert_allclose(w.cpu().numpy()[far], r_w[far], rtol=U.WEIGHT_RTOL, atol=0)
+
+
+FUSED = [
+    # name, config, T, gate dtype: split-H decode shapes (partials summed by
+    # the top-k kernel), the 128 x 128 prefill tile, fp32 hidden, softmax
+    ("dsv3_decode_f32", "dsv3", 64, "f32"),
+    ("dsv3_decode_bf16", "dsv3", 64, "bf16"),
+    ("dsv3_one_token", "dsv3", 1, "f32"),
+    ("dsv3_prefill_f32", "dsv3", 8192, "f32"),
+    ("mixtral_decode", "mixtral", 32, "bf16"),
+    ("mixtral_prefill", "mixtral", 4096, "bf16"),
+    ("qwen_tiles", "qwen", 300, "bf16"),
+    ("tiny_f32_hidden", "tiny", 64, "f32"),
+]
+
+
+def _routing_params(cfg, T):
+    return B.make_params(num_tokens=T, num_experts=cfg.E, top_k=cfg.K, hidden_size=cfg.H,
+                         intermediate_size=cfg.I,
+                         scoring_func=B.SIGMOID if cfg.scoring == "sigmoid" else B.SOFTMAX,
+                         renormalize=cfg.renormalize, num_expert_group=cfg.n_group,
+                         topk_group=cfg.topk_group, routed_scaling_factor=cfg.rsf,
+                         act_dtype=B.F32 if cfg.act_dtype == "f32" else B.BF16,
+                         weight_dtype=B.F32 if cfg.w_dtype == "f32" else B.BF16,
+                         out_dtype=B.F32 if cfg.act_dtype == "f32" else B.BF16)
+
+
+@pytest.mark.parametrize("name,cfg,T,gdt", FUSED, ids=[c[0] for c in FUSED])
+def test_router_topk_is_router_gemm_then_topk(name, cfg, T, gdt):
+    """moe_router_topk gives bitwise the ids, weights and logits of
+    moe_router_gemm followed by moe_topk, with and without logits out."""
+    cfg = _cfg(cfg)
+    print("fused router case", name, flush=True)
+    x = synth.make_hidden(cfg, T, device="cuda")
+    g = synth.make_gate(cfg, gdt, device="cuda")
+    b = synth.make_correction_bias(cfg)
+    bias = None if b is None else torch.from_numpy(b).cuda()
+    p = _routing_params(cfg, T)
+    ws = torch.empty(max(B.moe_workspace_size(p), 256), dtype=torch.uint8, device="cuda")
+    lg = torch.empty(T, cfg.E, dtype=torch.float32, device="cuda")
+    ids0 = torch.empty(T, cfg.K, dtype=torch.int32, device="cuda")
+    w0 = torch.empty(T, cfg.K, dtype=torch.float32, device="cuda")
+    B.moe_router_gemm(p, x, g, lg, ws)
+    B.moe_topk(p, lg, bias, ids0, w0)
+    for keep_logits in (True, False):
+        ids = torch.full_like(ids0, -1)
+        w = torch.full_like(w0, float("nan"))
+        lg2 = torch.full_like(lg, float("nan")) if keep_logits else None
+        B.moe_router_topk(p, x, g, bias, ids, w, lg2, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(ids, ids0), "ids differ (logits kept: %s)" % keep_logits
+        assert torch.equal(w, w0), "weights differ (logits kept: %s)" % keep_logits
+        if keep_logits:
+            assert torch.equal(lg2, lg), "logits differ"
+
+
+def test_router_topk_routes_like_the_oracle_dsv3_prefill():
+    """moe_router_topk at the DeepSeek-V3 prefill shape (fp32 gate) against
+    the oracle: its logits lie within the derived bound of the oracle's
+    float64 logits, and the oracle's logits, rounded to fp32 and routed by the
+    oracle, give bit-exact ids on every sampled row whose decision is farther
+    from a tie than twice the largest logit error seen on the sample (times
+    1/4, the largest slope of a sigmoid key, plus fp32 rounding): on those
+    rows no error of that size can change a decision."""
+    cfg = synth.CONFIGS["dsv3"]
+    T = cfg.T
+    x = synth.make_hidden(cfg, T, device="cuda")
+    g = synth.make_gate(cfg, "f32", device="cuda")
+    b = synth.make_correction_bias(cfg)
+    p = _routing_params(cfg, T)
+    ws = torch.empty(max(B.moe_workspace_size(p), 256), dtype=torch.uint8, device="cuda")
+    ids = torch.empty(T, cfg.K, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, cfg.K, dtype=torch.float32, device="cuda")
+    lg = torch.empty(T, cfg.E, dtype=torch.float32, device="cuda")
+    B.moe_router_topk(p, x, g, torch.from_numpy(b).cuda(), ids, w, lg, ws)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, 32), np.arange(T - 32, T),
+                                     np.random.default_rng(6).integers(0, T, 192)]))
+    xh = U.to_host_bits(x)[rows]
+    gh = U.to_host_bits(g)
+    ref = O.router_logits(xh, O.BF16, gh, O.F32)
+    bound = (2.0 ** -16 + (cfg.H + 1) * 2.0 ** -24) * (np.abs(_f64(xh, O.BF16)) @ np.abs(_f64(gh, O.F32)).T)
+    err = np.abs(lg.cpu().numpy()[rows].astype(np.float64) - ref)
+    assert (err <= bound).all(), "logits beyond the bound"
+    delta = 2.0 * (0.25 * float(err.max()) + 1e-6)
+    far = synth._rows_without_near_ties(dataclasses.replace(cfg, delta=delta), ref.astype(np.float32), b)
+    assert far.sum() >= 32, "too few rows far from a tie (%d)" % far.sum()
+    r_ids, _ = U.oracle_route(cfg, ref.astype(np.float32), b)
+    got = ids.cpu().numpy()[rows]
+    assert np.array_equal(got[far], r_ids[far])
