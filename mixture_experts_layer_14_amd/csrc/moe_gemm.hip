@@ -42,7 +42,9 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
                                                            int32_t* __restrict__ num_tiles,
                                                            GroupUnit* __restrict__ units,
                                                            int32_t* __restrict__ num_units,
-                                                           int split_nn, int32_t* __restrict__ split) {
+                                                           int split_nn, int32_t* __restrict__ split,
+                                                           Tile* __restrict__ tails,
+                                                           int32_t* __restrict__ num_tails) {
     __shared__ int32_t wave_sums[16];
     // segment: expert g, or slice g - E of the shared expert (T rows each)
     const int g = threadIdx.x;
@@ -58,12 +60,28 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
     // main m-tiles of BM rows (the last one possibly ragged), unless a
     // remainder of at most tail_rows rows goes to a tail tile
     const int32_t rem = (r1 - r0) % BM;
-    const int32_t tail = rem > 0 && rem <= tail_rows ? 1 : 0;
-    const int32_t nmain = (r1 - r0) / BM + (rem > 0 && !tail ? 1 : 0);
+    const int32_t has_rem_tail = rem > 0 && rem <= tail_rows ? 1 : 0;
+    const int32_t nmain = (r1 - r0) / BM + (rem > 0 && !has_rem_tail ? 1 : 0);
+    // with a separate tail table, the tail tile goes there (a group of its
+    // own, for a kernel of its own) and the main table holds the rest
+    const int32_t tail = tails ? 0 : has_rem_tail;
     const int32_t nt = nmain + tail;
     int32_t all_tiles, all_units;
     const int32_t start = block_exclusive_sum_i32<1024>(nt, wave_sums, &all_tiles);
     const int32_t ustart = block_exclusive_sum_i32<1024>(2 * nmain + tail, wave_sums, &all_units);
+    if (tails) {
+        int32_t all_tails;
+        const int32_t tstart = block_exclusive_sum_i32<1024>(has_rem_tail, wave_sums, &all_tails);
+        if (has_rem_tail) {
+            Tile t;
+            t.expert = g;
+            t.row0 = r1 - rem;
+            t.row1 = r1;
+            t.group = tstart * 256 + 1;
+            tails[tstart] = t;
+        }
+        if (g == 0) *num_tails = all_tails;
+    }
     // an expert's m-tiles form groups of at most gm_max, balanced in size; a
     // group's tiles sweep the n-tiles together so they share each weight
     // tile; the tail tile joins the expert's last group
@@ -503,24 +521,29 @@ size_t w2_rows_workspace_bytes(const GroupedProblem& p) {
 
 // Tile table of BM-row m-tiles; with tail_rows > 0 (BM = 256 only) an
 // expert's remainder of at most tail_rows rows becomes a tail tile and the
-// unit table is written too.
+// unit table is written too.  With `tails` (and tail_rows > 0), the tail
+// tiles go to a table of their own instead, placed where the unit table
+// would be (one tile per segment at most), each a group of one m-tile, for
+// a second kernel with tail_rows-row tiles; `tails` receives its arguments.
 static void build_tiles(const GroupedProblem& p, const int32_t* offsets, int BM, GemmArgs& g,
-                        void* ws, hipStream_t stream, int tail_rows = 0, int split_nn = 0) {
+                        void* ws, hipStream_t stream, int tail_rows = 0, int split_nn = 0,
+                        GemmArgs* tails = nullptr) {
     int32_t* num_tiles = static_cast<int32_t*>(ws);
     int32_t* num_units = num_tiles + 1;
     int32_t* split = num_tiles + 2;
+    int32_t* num_tails = num_tiles + 4;
     Tile* tiles = reinterpret_cast<Tile*>(static_cast<uint8_t*>(ws) + 256);
-    GroupUnit* units = tail_rows > 0 ? reinterpret_cast<GroupUnit*>(static_cast<uint8_t*>(ws) + 256 +
-                                                                    tile_table_bytes(p))
-                                     : nullptr;
-    const TileTableKey key{ws, offsets, BM, tail_rows, split_nn};
+    uint8_t* after = static_cast<uint8_t*>(ws) + 256 + tile_table_bytes(p);
+    GroupUnit* units = tail_rows > 0 && !tails ? reinterpret_cast<GroupUnit*>(after) : nullptr;
+    Tile* tail_tiles = tail_rows > 0 && tails ? reinterpret_cast<Tile*>(after) : nullptr;
+    const TileTableKey key{ws, offsets, BM, tail_rows, split_nn, tails != nullptr};
     const TileTableKey* b = p.built;
     if (!b || b->ws != key.ws || b->offsets != key.offsets || b->bm != key.bm ||
-        b->tail_rows != key.tail_rows || b->split_nn != key.split_nn) {
+        b->tail_rows != key.tail_rows || b->split_nn != key.split_nn || b->tail_table != key.tail_table) {
         build_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, p.E, p.shared, static_cast<int32_t>(p.T),
                                                    static_cast<int32_t>(p.T * p.K), BM, MOE_TILE_GM,
                                                    tail_rows, tiles, num_tiles, units, num_units,
-                                                   split_nn, split);
+                                                   split_nn, split, tail_tiles, num_tails);
         if (p.built) *p.built = key;
     }
     g.split = split_nn > 0 ? split : nullptr;
@@ -529,6 +552,14 @@ static void build_tiles(const GroupedProblem& p, const int32_t* offsets, int BM,
     g.units = units;
     g.num_units = num_units;
     g.max_m_tiles = max_m_tiles(p, BM);
+    if (tails) {
+        *tails = g;
+        tails->split = nullptr;
+        tails->units = nullptr;
+        tails->tiles = tail_tiles;
+        tails->num_tiles = num_tails;
+        tails->max_m_tiles = p.E + p.shared;  // one tail tile per segment at most
+    }
 }
 
 // generic 16x16 MFMA kernel (the fp32 layers)
@@ -660,9 +691,45 @@ static hipError_t launch_tile_fp8(const GroupedProblem& p, GemmArgs g, const int
     return hipGetLastError();
 }
 
+// 256 x 256 fp8 tiles (tile_kernel_fp8_256) once experts average this many
+// rows, when the rows' k blocks come in groups of four and the scale arrays
+// are 16-byte aligned (its scale copies are the grouped ones)
+#ifndef MOE_FP8_BIG
+#define MOE_FP8_BIG 1
+#endif
+#ifndef MOE_FP8_BIG_MIN_ROWS
+#define MOE_FP8_BIG_MIN_ROWS 128
+#endif
+// 256-row tiles for every expert's full m-tiles and remainders of more than
+// 128 rows (tile_kernel_fp8_256), then, in a second launch, one 128-row tile
+// per remainder of at most 128 rows (tile_kernel_fp8 128 x 256): a 256 x 256
+// tile costs its copies and LDS reads whatever its live rows, so a short
+// remainder is cheaper as half a tile.  Measured on the DeepSeek-V3 fp8
+// layer: the 256 x 256 tile is 12-20 % cheaper per flop than the 128 x 256
+// one, and without the split it loses that to the longer padding.
+template <int MODE>
+static hipError_t launch_tile_fp8_256(const GroupedProblem& p, GemmArgs g, const int32_t* offsets,
+                                      void* ws, hipStream_t stream) {
+    GemmArgs t = g;
+    build_tiles(p, offsets, 256, g, ws, stream, 128, 0, &t);
+    g.n_tiles_n = g.N / 256;
+    t.n_tiles_n = g.N / 256;
+    const int64_t total = static_cast<int64_t>(g.max_m_tiles) * g.n_tiles_n;
+    tile_kernel_fp8_256<MODE><<<static_cast<unsigned>(8 * ((total + 7) / 8)), 8 * kWave, 0, stream>>>(g);
+    const int64_t tail_total = static_cast<int64_t>(t.max_m_tiles) * t.n_tiles_n;
+    tile_kernel_fp8<128, 256, 2, 4, MODE, 4>
+        <<<static_cast<unsigned>(8 * ((tail_total + 7) / 8)), 8 * kWave, 0, stream>>>(t);
+    return hipGetLastError();
+}
+
 template <int MODE>
 static hipError_t fp8_gemm(const GroupedProblem& p, GemmArgs g, const int32_t* offsets, void* ws,
                            hipStream_t stream) {
+    const uintptr_t sc = reinterpret_cast<uintptr_t>(g.A_scale) | reinterpret_cast<uintptr_t>(g.B_scale) |
+                         reinterpret_cast<uintptr_t>(g.B_shared_scale);
+    if (MOE_FP8_BIG && (g.Kd / 128) % 4 == 0 && sc % 16 == 0 && g.N % 256 == 0 &&
+        rows_per_active_expert(p) >= MOE_FP8_BIG_MIN_ROWS)
+        return launch_tile_fp8_256<MODE>(p, g, offsets, ws, stream);
     if constexpr (MODE == kModeW13) {
         return launch_tile_fp8<128, 256, 2, 4, MODE>(p, g, offsets, ws, stream);
     } else {

@@ -371,4 +371,330 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// tile_kernel_fp8_256: 256 x 256 fp8 tiles on 8 waves (128 tokens x 64
+// features each), for rows whose k blocks come in whole groups of four.
+// ---------------------------------------------------------------------------
+//
+// The 128 x 256 tile above reads, per k block, as many LDS bytes (each wave
+// its 64 tokens and 64 features) as its MFMAs take cycles, so LDS and the
+// copy path, not the matrix cores, set its pace.  A 256 x 256 tile halves the
+// LDS reads per flop (a wave's 128 tokens are reused across its 64 features)
+// and cuts the copies per flop by a third; its stage (64 bytes of k of 512
+// rows) moves exactly the bytes of the bf16 256 x 256 stage at twice the
+// flops.  Its 128 accumulators per lane leave no room for a separate block
+// product, so each accumulator is kept in units of the current k block's
+// scale product s_kb = sa * sw: before the MFMAs of block kb it is multiplied
+// by s_{kb-1} / s_kb, the MFMAs add the raw block product, and the epilogue
+// multiplies by the last s.  That is sum_kb s_kb P_kb up to fp32 rounding
+// (one extra rounding per k block), with one multiply per element and k
+// block, as before.  A k block spans two stages of 64 bytes; four stages fit
+// beside a two-slot ring of per-group scales (as above, SG = 4).
+template <int MODE>
+__global__ __launch_bounds__(8 * kWave) void tile_kernel_fp8_256(GemmArgs g) {
+    constexpr int BM = 256, BN = 256, WM = 2, WN = 4, NW = WM * WN;
+    constexpr int ROWB = 64;                       // bytes of k per stage
+    constexpr int WTM = BM / WM, WTN = BN / WN;    // 128 tokens x 64 features per wave
+    constexpr int TM = WTM / 32, TN = WTN / 32;    // 4 x 2 MFMA tiles
+    constexpr int ROWS = BM + BN;
+    constexpr int SLOTS = ROWB / 16;
+    constexpr int RPC = kWave / SLOTS;             // rows per copy instruction
+    constexpr int COPIES = ROWS / RPC / NW;        // copy instructions per wave per stage
+    constexpr int STAGE = ROWS * ROWB;
+    constexpr int STAGES = 4;
+    constexpr int SG = 4;                          // k blocks per scale group
+    constexpr int SROWS = BM / NW;                 // A-scale rows copied per wave
+    constexpr int NBS = MODE == kModeW13 ? 2 : BN / 128;
+    constexpr int SPOS = (NW - 1) * SROWS + kWave;
+    constexpr int RING_SLOT = (SPOS * 16 + 255) / 256 * 256;
+    constexpr int RING = 2 * RING_SLOT;
+    constexpr int ROW_W_BYTES = MODE == kModeW2 ? BM * 4 : 0;
+    constexpr int SMEM = STAGES * STAGE + RING + ROW_W_BYTES;
+    constexpr int kMfma = TM * TN, HALF = kMfma / 2;
+    constexpr int kReads = 2 * (TM + TN);          // ds_read_b128 per stage per wave
+    static_assert(ROWS % (RPC * NW) == 0 && BM % RPC == 0, "copy split");
+    static_assert(BM + NBS <= SPOS && SROWS + NBS <= kWave, "ring positions");
+    static_assert(SMEM <= 160 * 1024, "LDS budget");
+    static_assert(COPIES * (STAGES - 2) + 1 <= 63, "vmcnt immediate range");
+    static_assert(MODE != kModeW13 || (TN == 2 && WN == 4), "w13: a wave holds one gate/up pair of 32 features");
+    static_assert(MODE != kModeW13 || BM * WN * 4 <= STAGE, "w13 amax exchange fits one stage");
+    static_assert(HALF % TN == 0, "each half holds whole token blocks");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
+    uint8_t* const ring = smem + STAGES * STAGE;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = wave_index(tid);
+    const int wm = wave / WN, wn = wave % WN;
+
+    const TilePos tp = map_block(blockIdx.x, *g.num_tiles, g.n_tiles_n, g.tiles);
+    if (!tp.ok) return;
+    const Tile tl = g.tiles[tp.m];
+    const int n_tile = tp.n;
+    const int64_t K = g.Kd;                        // bytes per row
+    const int nkb = static_cast<int>(K / 128);
+    const int nk = 2 * nkb;                        // stages
+    const BSel bw = expert_weights<MODE>(g, tl.expert, 1);
+
+    // source of this lane's 16-byte slot in each of the wave's copies
+    const uint8_t* src[COPIES];
+#pragma unroll
+    for (int q = 0; q < COPIES; ++q) {
+        const int row = (wave * COPIES + q) * RPC + lane / SLOTS;
+        const int chunk = lds_slot<ROWB>(row, lane % SLOTS);
+        if (row < BM) {
+            int64_t r = tl.row0 + row;
+            if (r >= tl.row1) r = tl.row0;  // ragged tail: copy a valid row, never stored
+            src[q] = g.A + a_source_row<MODE>(g, r) * K + chunk * 16;
+        } else {
+            src[q] = bw.base + packed_offset(b_weight_row<MODE, BN, 32>(g, bw, n_tile, row - BM), chunk * 16, bw.rb);
+        }
+    }
+    // scales of ring position wave*SROWS + lane: a token's A scales, a weight
+    // block's scales, or (past them) a copy of token 0's
+    const float* ssrc;
+    {
+        const int p = wave * SROWS + lane;
+        int64_t r = tl.row0 + (p < BM ? p : 0);
+        if (r >= tl.row1) r = tl.row0;
+        ssrc = g.A_scale + a_source_row<MODE>(g, r) * nkb;
+        const int slot = p - BM;
+        if (slot >= 0 && slot < NBS) {
+            const int rep = MODE == kModeW13 ? slot * 32 : slot * 128;  // a local row of the block
+            const int b = static_cast<int>(b_weight_row<MODE, BN, 32>(g, bw, n_tile, rep) / 128);
+            ssrc = bw.scale + static_cast<int64_t>(b) * bw.scale_rs;
+        }
+    }
+    auto issue_scales = [&](int grp) {
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const void*>(ssrc + grp * SG),
+            (__attribute__((address_space(3))) void*)(ring + (grp & 1) * RING_SLOT + wave * SROWS * 16), 16, 0, 0);
+    };
+    // copies of stage `kit` (64 bytes of k); past the last stage the source is
+    // clamped to it, keeping the copy count per stage fixed
+    auto issue_copies = [&](int kit) {
+        int kc = kit < nk ? kit : nk - 1;
+        int sb = (kit % STAGES) * STAGE;
+        asm volatile("" : "+s"(kc), "+s"(sb));
+        uint8_t* st = smem + sb;
+        const int64_t off = static_cast<int64_t>(kc) * ROWB;
+#pragma unroll
+        for (int q = 0; q < COPIES; ++q)
+            __builtin_amdgcn_global_load_lds(
+                // packed B (the later copies) advances 16x faster along k
+                reinterpret_cast<const void*>(src[q] + ((wave * COPIES + q) * RPC >= BM ? off << 4 : off)),
+                (__attribute__((address_space(3))) void*)(st + (wave * COPIES + q) * 1024), 16, 0, 0);
+    };
+
+    // accumulators in units of the current k block's scale product
+    f32x16 acc[TM][TN];
+    float sprev[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            sprev[i][j] = 1.0f;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+        }
+
+    const int lrow = lane % 32, khalf = lane / 32;
+    float* row_w = reinterpret_cast<float*>(smem + STAGES * STAGE + RING);
+    float my_w = 1.0f;
+    if (MODE == kModeW2 && tid < BM) {
+        const int64_t r = tl.row0 + tid;
+        if (r < tl.row1) my_w = row_weight(g, r);
+    }
+
+    // 32 bytes of row r of a stage: 16-byte chunks 2*khalf and 2*khalf + 1
+    auto read_frag = [&](uint32_t base, int r) {
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(smem + base + r * ROWB + lds_slot<ROWB>(r, 2 * khalf) * 16);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(smem + base + r * ROWB + lds_slot<ROWB>(r, 2 * khalf + 1) * 16);
+        return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    };
+    auto read_stage = [&](uint32_t base, i32x8 (&fa)[TM], i32x8 (&fb)[TN]) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[i] = read_frag(base, wm * WTM + i * 32 + lrow);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[j] = read_frag(base, BM + wn * WTN + j * 32 + lrow);
+    };
+    // weights first: lane l holds token l%32 of block i and 16 features of
+    // the 32 of block j, so both scales are one value per lane and tile
+    auto mfma_range = [&](int lo, int hi, const i32x8 (&fa)[TM], const i32x8 (&fb)[TN]) {
+#pragma unroll
+        for (int m = lo; m < hi; ++m)
+            acc[m / TN][m % TN] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                fb[m % TN], fa[m / TN], acc[m / TN][m % TN], 0, 0, 0, 127, 0, 127);
+    };
+    // rescale tiles lo..hi-1 to k block kb's units (ratio[m] precomputed)
+    float ratio[kMfma], snext[TM][TN];
+    // scale products of k block `kb_in_group` of the group in ring slot
+    // `slot`, and the ratios to them from the current ones
+    auto next_scales = [&](int slot, int kb_in_group) {
+        const float* rs = reinterpret_cast<const float*>(ring + slot * RING_SLOT);
+        float sa[TM], sw[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) sa[i] = rs[(wm * WTM + i * 32 + lrow) * 4 + kb_in_group];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int lr = wn * WTN + j * 32;
+            sw[j] = rs[(BM + (MODE == kModeW13 ? (lr / 32) % 2 : lr / 128)) * 4 + kb_in_group];
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                snext[i][j] = sa[i] * sw[j];
+                ratio[i * TN + j] = sprev[i][j] * __builtin_amdgcn_rcpf(snext[i][j]);
+            }
+    };
+    auto rescale = [&](int lo, int hi) {
+#pragma unroll
+        for (int m = lo; m < hi; ++m)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[m / TN][m % TN][v] *= ratio[m];
+    };
+    auto wait_later_stages = [&](auto sub_tag) {
+        // stage it+1's copies landed, those of stages it+2 .. it+STAGES-1
+        // (and a scale copy issued after stage it+1's) still in flight
+        constexpr int sub = decltype(sub_tag)::value;
+        constexpr int n = (STAGES - 2) * COPIES + (sub < STAGES - 2 ? 1 : 0);
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
+    };
+
+    issue_scales(0);
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st) issue_copies(st);
+    {
+        constexpr int n = (STAGES - 2) * COPIES;
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
+    }
+    __builtin_amdgcn_s_barrier();
+    i32x8 af[2][TM], bfr[2][TN];
+    read_stage(0, af[0], bfr[0]);
+    next_scales(0, 0);  // k block 0
+    const int ngroups = nkb / SG;
+    // one group = SG k blocks = 2 * SG stages; sub = the stage's place in it
+    for (int it0 = 0; it0 < nk; it0 += 2 * SG) static_for<2 * SG>([&](auto sub_tag) {
+        constexpr int sub = decltype(sub_tag)::value;
+        constexpr int F = sub & 1;                  // fragment buffer of this stage
+        const int it = it0 + sub;
+        if constexpr (sub % 2 == 0) {
+            // first stage of k block kb: the scale products read during the
+            // previous stage become the current ones
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) sprev[i][j] = snext[i][j];
+        } else {
+            // second stage of k block kb: the next block's scales and ratios
+            // (its group's ring slot landed by the barrier that opened this
+            // stage: it waited for copies issued after that slot's copy).
+            // Past the last block this reads a repeated group whose values
+            // are never committed.
+            next_scales(sub == 2 * SG - 1 ? ((it0 / (2 * SG)) + 1) & 1 : (it0 / (2 * SG)) & 1,
+                        sub == 2 * SG - 1 ? 0 : sub / 2 + 1);
+        }
+        // the next group's scales (first stage of a group) and this wave's
+        // copies of stage it+STAGES-1, into the buffer of stage it-1
+        if constexpr (sub == 0) {
+            const int nxt = it0 / (2 * SG) + 1;
+            issue_scales(nxt < ngroups ? nxt : ngroups - 1);
+        }
+        issue_copies(it + STAGES - 1);
+        if constexpr (sub % 2 == 0) rescale(0, HALF);
+        mfma_range(0, HALF, af[F], bfr[F]);
+        mix_sched<HALF, 0, COPIES + (sub == 0 ? 1 : 0)>();
+        __builtin_amdgcn_sched_barrier(0);
+        // next stage's read offsets before the barrier, reads right after it
+        uint32_t nb = ((it + 1) % STAGES) * STAGE;
+        asm volatile("" : "+v"(nb));
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads landed
+        wait_later_stages(std::integral_constant<int, sub % (2 * SG)>{});
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        read_stage(nb, af[F ^ 1], bfr[F ^ 1]);
+        if constexpr (sub % 2 == 0) rescale(HALF, kMfma);
+        mfma_range(HALF, kMfma, af[F], bfr[F]);
+        mix_sched<kMfma - HALF, kReads, 0>();
+        __builtin_amdgcn_sched_barrier(0);
+    });
+    // no copy may still write LDS when the block ends or LDS is reused
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+
+    // back to the real scale: acc * s of the last k block
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] *= sprev[i][j];
+
+    // lane holds token wm*WTM + i*32 + lrow and, of each 32-feature tile j,
+    // the features 8*(v/4) + 4*khalf + v%4
+    if constexpr (MODE == kModeW13) {
+        __syncthreads();
+        float* red = reinterpret_cast<float*>(smem);  // [BM][WN]
+        float act[TM][16];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            float m = 0.0f;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                act[i][v] = glu_act(g, acc[i][0][v], acc[i][1][v]);
+                m = fmaxf(m, fabsf(act[i][v]));
+            }
+            m = fmaxf(m, __shfl_xor(m, 32, kWave));
+            if (khalf == 0) red[(wm * WTM + i * 32 + lrow) * WN + wn] = m;
+        }
+        __syncthreads();
+        uint8_t* q = static_cast<uint8_t*>(g.C);
+        const int ngroups_i = g.I / 128;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int lt = wm * WTM + i * 32 + lrow;
+            float amax = red[lt * WN];
+#pragma unroll
+            for (int w = 1; w < WN; ++w) amax = fmaxf(amax, red[lt * WN + w]);
+            const float scale = fmaxf(amax, 1e-10f) / 448.0f;
+            const int64_t r = tl.row0 + lt;
+            if (r < tl.row1) {
+                uint8_t* qrow = q + r * g.I + static_cast<int64_t>(n_tile) * 128 + wn * 32 + 4 * khalf;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    uint32_t word = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        word |= static_cast<uint32_t>(f32_to_e4m3(act[i][4 * b + e] / scale)) << (8 * e);
+                    *reinterpret_cast<uint32_t*>(qrow + 8 * b) = word;
+                }
+                if (wn == 0 && khalf == 0) g.C_scale[r * ngroups_i + n_tile] = scale;
+            }
+        }
+    } else {
+        if (tid < BM) row_w[tid] = my_w;
+        __syncthreads();
+        uint16_t* y = static_cast<uint16_t*>(g.C);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int lt = wm * WTM + i * 32 + lrow;
+            const int64_t r = tl.row0 + lt;
+            if (r >= tl.row1) continue;
+            const float w = row_w[lt];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                uint16_t* yrow = y + r * g.N + static_cast<int64_t>(n_tile) * BN + wn * WTN + j * 32 + 4 * khalf;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const uint32_t lo = static_cast<uint32_t>(f32_to_bf16_bits(acc[i][j][4 * b] * w)) |
+                                        (static_cast<uint32_t>(f32_to_bf16_bits(acc[i][j][4 * b + 1] * w)) << 16);
+                    const uint32_t hi = static_cast<uint32_t>(f32_to_bf16_bits(acc[i][j][4 * b + 2] * w)) |
+                                        (static_cast<uint32_t>(f32_to_bf16_bits(acc[i][j][4 * b + 3] * w)) << 16);
+                    *reinterpret_cast<uint2*>(yrow + 8 * b) = make_uint2(lo, hi);
+                }
+            }
+        }
+    }
+}
+
 }  // namespace moe

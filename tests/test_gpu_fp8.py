@@ -43,6 +43,18 @@ FP8_SMALL = {
     "fp8_shared_2I_grouped_scales": MC("fp8_shared_2I_grouped_scales", E=8, K=2, H=512, I=512,
                                        T=77, w_dtype="fp8", shared=1, shared_I=1024, seed=27,
                                        weight_seed=27),
+    # experts of >= 128 rows with k blocks in groups of four: 256 x 256 fp8
+    # tiles, ragged last tiles of each expert and of the shared slices
+    "fp8_big_tiles": MC("fp8_big_tiles", E=4, K=2, H=512, I=512, T=700, w_dtype="fp8",
+                        shared=1, seed=28, weight_seed=28),
+    "fp8_big_tiles_grouped_shared_2I": MC("fp8_big_tiles_grouped_shared_2I", E=8, K=2, H=1024,
+                                          I=512, T=1000, w_dtype="fp8", scoring="sigmoid",
+                                          n_group=4, topk_group=2, rsf=2.5, correction_bias=True,
+                                          shared=1, shared_I=1024, seed=29, weight_seed=29,
+                                          delta=1e-4),
+    "fp8_big_tiles_clipped": MC("fp8_big_tiles_clipped", E=4, K=1, H=512, I=1024, T=900,
+                                w_dtype="fp8", seed=30, weight_seed=30, swiglu_alpha=1.702,
+                                swiglu_limit=0.5),
 }
 
 
