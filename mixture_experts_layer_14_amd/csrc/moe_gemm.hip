@@ -42,9 +42,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
                                                            int32_t* __restrict__ num_tiles,
                                                            GroupUnit* __restrict__ units,
                                                            int32_t* __restrict__ num_units,
-                                                           int split_nn, int32_t* __restrict__ split,
-                                                           Tile* __restrict__ tails,
-                                                           int32_t* __restrict__ num_tails) {
+                                                           int split_nn, int32_t* __restrict__ split) {
     __shared__ int32_t wave_sums[16];
     // segment: expert g, or slice g - E of the shared expert (T rows each)
     const int g = threadIdx.x;
@@ -60,28 +58,12 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
     // main m-tiles of BM rows (the last one possibly ragged), unless a
     // remainder of at most tail_rows rows goes to a tail tile
     const int32_t rem = (r1 - r0) % BM;
-    const int32_t has_rem_tail = rem > 0 && rem <= tail_rows ? 1 : 0;
-    const int32_t nmain = (r1 - r0) / BM + (rem > 0 && !has_rem_tail ? 1 : 0);
-    // with a separate tail table, the tail tile goes there (a group of its
-    // own, for a kernel of its own) and the main table holds the rest
-    const int32_t tail = tails ? 0 : has_rem_tail;
+    const int32_t tail = rem > 0 && rem <= tail_rows ? 1 : 0;
+    const int32_t nmain = (r1 - r0) / BM + (rem > 0 && !tail ? 1 : 0);
     const int32_t nt = nmain + tail;
     int32_t all_tiles, all_units;
     const int32_t start = block_exclusive_sum_i32<1024>(nt, wave_sums, &all_tiles);
     const int32_t ustart = block_exclusive_sum_i32<1024>(2 * nmain + tail, wave_sums, &all_units);
-    if (tails) {
-        int32_t all_tails;
-        const int32_t tstart = block_exclusive_sum_i32<1024>(has_rem_tail, wave_sums, &all_tails);
-        if (has_rem_tail) {
-            Tile t;
-            t.expert = g;
-            t.row0 = r1 - rem;
-            t.row1 = r1;
-            t.group = tstart * 256 + 1;
-            tails[tstart] = t;
-        }
-        if (g == 0) *num_tails = all_tails;
-    }
     // an expert's m-tiles form groups of at most gm_max, balanced in size; a
     // group's tiles sweep the n-tiles together so they share each weight
     // tile; the tail tile joins the expert's last group
@@ -521,29 +503,24 @@ size_t w2_rows_workspace_bytes(const GroupedProblem& p) {
 
 // Tile table of BM-row m-tiles; with tail_rows > 0 (BM = 256 only) an
 // expert's remainder of at most tail_rows rows becomes a tail tile and the
-// unit table is written too.  With `tails` (and tail_rows > 0), the tail
-// tiles go to a table of their own instead, placed where the unit table
-// would be (one tile per segment at most), each a group of one m-tile, for
-// a second kernel with tail_rows-row tiles; `tails` receives its arguments.
+// unit table is written too.
 static void build_tiles(const GroupedProblem& p, const int32_t* offsets, int BM, GemmArgs& g,
-                        void* ws, hipStream_t stream, int tail_rows = 0, int split_nn = 0,
-                        GemmArgs* tails = nullptr) {
+                        void* ws, hipStream_t stream, int tail_rows = 0, int split_nn = 0) {
     int32_t* num_tiles = static_cast<int32_t*>(ws);
     int32_t* num_units = num_tiles + 1;
     int32_t* split = num_tiles + 2;
-    int32_t* num_tails = num_tiles + 4;
     Tile* tiles = reinterpret_cast<Tile*>(static_cast<uint8_t*>(ws) + 256);
-    uint8_t* after = static_cast<uint8_t*>(ws) + 256 + tile_table_bytes(p);
-    GroupUnit* units = tail_rows > 0 && !tails ? reinterpret_cast<GroupUnit*>(after) : nullptr;
-    Tile* tail_tiles = tail_rows > 0 && tails ? reinterpret_cast<Tile*>(after) : nullptr;
-    const TileTableKey key{ws, offsets, BM, tail_rows, split_nn, tails != nullptr};
+    GroupUnit* units = tail_rows > 0 ? reinterpret_cast<GroupUnit*>(static_cast<uint8_t*>(ws) + 256 +
+                                                                    tile_table_bytes(p))
+                                     : nullptr;
+    const TileTableKey key{ws, offsets, BM, tail_rows, split_nn};
     const TileTableKey* b = p.built;
     if (!b || b->ws != key.ws || b->offsets != key.offsets || b->bm != key.bm ||
-        b->tail_rows != key.tail_rows || b->split_nn != key.split_nn || b->tail_table != key.tail_table) {
+        b->tail_rows != key.tail_rows || b->split_nn != key.split_nn) {
         build_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, p.E, p.shared, static_cast<int32_t>(p.T),
                                                    static_cast<int32_t>(p.T * p.K), BM, MOE_TILE_GM,
                                                    tail_rows, tiles, num_tiles, units, num_units,
-                                                   split_nn, split, tail_tiles, num_tails);
+                                                   split_nn, split);
         if (p.built) *p.built = key;
     }
     g.split = split_nn > 0 ? split : nullptr;
@@ -552,14 +529,6 @@ static void build_tiles(const GroupedProblem& p, const int32_t* offsets, int BM,
     g.units = units;
     g.num_units = num_units;
     g.max_m_tiles = max_m_tiles(p, BM);
-    if (tails) {
-        *tails = g;
-        tails->split = nullptr;
-        tails->units = nullptr;
-        tails->tiles = tail_tiles;
-        tails->num_tiles = num_tails;
-        tails->max_m_tiles = p.E + p.shared;  // one tail tile per segment at most
-    }
 }
 
 // generic 16x16 MFMA kernel (the fp32 layers)
@@ -700,25 +669,18 @@ static hipError_t launch_tile_fp8(const GroupedProblem& p, GemmArgs g, const int
 #ifndef MOE_FP8_BIG_MIN_ROWS
 #define MOE_FP8_BIG_MIN_ROWS 128
 #endif
-// 256-row tiles for every expert's full m-tiles and remainders of more than
-// 128 rows (tile_kernel_fp8_256), then, in a second launch, one 128-row tile
-// per remainder of at most 128 rows (tile_kernel_fp8 128 x 256): a 256 x 256
-// tile costs its copies and LDS reads whatever its live rows, so a short
-// remainder is cheaper as half a tile.  Measured on the DeepSeek-V3 fp8
-// layer: the 256 x 256 tile is 12-20 % cheaper per flop than the 128 x 256
-// one, and without the split it loses that to the longer padding.
+// 256-row tiles; an expert's remainder of at most 128 rows runs as a
+// 128-row tile inside the expert's group (tile_kernel_fp8_256 picks the body
+// per tile): a 256 x 256 tile costs its copies and LDS reads whatever its
+// live rows, so a short remainder is cheaper as half a tile, and in the
+// group it shares the weight tiles the group streams through L2.
 template <int MODE>
 static hipError_t launch_tile_fp8_256(const GroupedProblem& p, GemmArgs g, const int32_t* offsets,
                                       void* ws, hipStream_t stream) {
-    GemmArgs t = g;
-    build_tiles(p, offsets, 256, g, ws, stream, 128, 0, &t);
+    build_tiles(p, offsets, 256, g, ws, stream);
     g.n_tiles_n = g.N / 256;
-    t.n_tiles_n = g.N / 256;
     const int64_t total = static_cast<int64_t>(g.max_m_tiles) * g.n_tiles_n;
     tile_kernel_fp8_256<MODE><<<static_cast<unsigned>(8 * ((total + 7) / 8)), 8 * kWave, 0, stream>>>(g);
-    const int64_t tail_total = static_cast<int64_t>(t.max_m_tiles) * t.n_tiles_n;
-    tile_kernel_fp8<128, 256, 2, 4, MODE, 4>
-        <<<static_cast<unsigned>(8 * ((tail_total + 7) / 8)), 8 * kWave, 0, stream>>>(t);
     return hipGetLastError();
 }
 

@@ -390,47 +390,58 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
 // (one extra rounding per k block), with one multiply per element and k
 // block, as before.  A k block spans two stages of 64 bytes; four stages fit
 // beside a two-slot ring of per-group scales (as above, SG = 4).
-template <int MODE>
-__global__ __launch_bounds__(8 * kWave) void tile_kernel_fp8_256(GemmArgs g) {
-    constexpr int BM = 256, BN = 256, WM = 2, WN = 4, NW = WM * WN;
-    constexpr int ROWB = 64;                       // bytes of k per stage
-    constexpr int WTM = BM / WM, WTN = BN / WN;    // 128 tokens x 64 features per wave
-    constexpr int TM = WTM / 32, TN = WTN / 32;    // 4 x 2 MFMA tiles
-    constexpr int ROWS = BM + BN;
+// LDS plan of the body below for BM rows (stages, then the scale ring, then
+// the w2 row weights).
+template <int BM, int MODE>
+struct Fp8BigShape {
+    static constexpr int BN = 256, NW = 8, ROWB = 64, STAGES = 4;
+    static constexpr int ROWS = BM + BN;
+    static constexpr int STAGE = ROWS * ROWB;
+    static constexpr int SROWS = BM / NW;
+    static constexpr int SPOS = (NW - 1) * SROWS + kWave;
+    static constexpr int RING_SLOT = (SPOS * 16 + 255) / 256 * 256;
+    static constexpr int RING = 2 * RING_SLOT;
+    static constexpr int ROW_W_BYTES = MODE == kModeW2 ? BM * 4 : 0;
+    static constexpr int SMEM = STAGES * STAGE + RING + ROW_W_BYTES;
+};
+
+// One BM x 256 tile (BM = 256, or 128 for a remainder of at most 128 rows:
+// half the copies, LDS reads and MFMAs of a 256-row tile) of m-tile `tl`,
+// n-tile `n_tile`; `smem` is the kernel's one LDS array.
+template <int BM, int MODE>
+__device__ __forceinline__ void fp8_big_body(const GemmArgs& g, const Tile tl, const int n_tile,
+                                             uint8_t* smem) {
+    using Shape = Fp8BigShape<BM, MODE>;
+    constexpr int BN = 256, WM = 2, WN = 4, NW = WM * WN;
+    constexpr int ROWB = Shape::ROWB;              // bytes of k per stage
+    constexpr int WTM = BM / WM, WTN = BN / WN;    // tokens x 64 features per wave
+    constexpr int TM = WTM / 32, TN = WTN / 32;
+    constexpr int ROWS = Shape::ROWS;
     constexpr int SLOTS = ROWB / 16;
     constexpr int RPC = kWave / SLOTS;             // rows per copy instruction
     constexpr int COPIES = ROWS / RPC / NW;        // copy instructions per wave per stage
-    constexpr int STAGE = ROWS * ROWB;
-    constexpr int STAGES = 4;
+    constexpr int STAGE = Shape::STAGE;
+    constexpr int STAGES = Shape::STAGES;
     constexpr int SG = 4;                          // k blocks per scale group
-    constexpr int SROWS = BM / NW;                 // A-scale rows copied per wave
+    constexpr int SROWS = Shape::SROWS;            // A-scale rows copied per wave
     constexpr int NBS = MODE == kModeW13 ? 2 : BN / 128;
-    constexpr int SPOS = (NW - 1) * SROWS + kWave;
-    constexpr int RING_SLOT = (SPOS * 16 + 255) / 256 * 256;
-    constexpr int RING = 2 * RING_SLOT;
-    constexpr int ROW_W_BYTES = MODE == kModeW2 ? BM * 4 : 0;
-    constexpr int SMEM = STAGES * STAGE + RING + ROW_W_BYTES;
+    constexpr int SPOS = Shape::SPOS;
+    constexpr int RING_SLOT = Shape::RING_SLOT;
     constexpr int kMfma = TM * TN, HALF = kMfma / 2;
     constexpr int kReads = 2 * (TM + TN);          // ds_read_b128 per stage per wave
     static_assert(ROWS % (RPC * NW) == 0 && BM % RPC == 0, "copy split");
     static_assert(BM + NBS <= SPOS && SROWS + NBS <= kWave, "ring positions");
-    static_assert(SMEM <= 160 * 1024, "LDS budget");
+    static_assert(Shape::SMEM <= 160 * 1024, "LDS budget");
     static_assert(COPIES * (STAGES - 2) + 1 <= 63, "vmcnt immediate range");
     static_assert(MODE != kModeW13 || (TN == 2 && WN == 4), "w13: a wave holds one gate/up pair of 32 features");
     static_assert(MODE != kModeW13 || BM * WN * 4 <= STAGE, "w13 amax exchange fits one stage");
     static_assert(HALF % TN == 0, "each half holds whole token blocks");
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
     uint8_t* const ring = smem + STAGES * STAGE;
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = wave_index(tid);
     const int wm = wave / WN, wn = wave % WN;
-
-    const TilePos tp = map_block(blockIdx.x, *g.num_tiles, g.n_tiles_n, g.tiles);
-    if (!tp.ok) return;
-    const Tile tl = g.tiles[tp.m];
-    const int n_tile = tp.n;
     const int64_t K = g.Kd;                        // bytes per row
     const int nkb = static_cast<int>(K / 128);
     const int nk = 2 * nkb;                        // stages
@@ -499,7 +510,7 @@ __global__ __launch_bounds__(8 * kWave) void tile_kernel_fp8_256(GemmArgs g) {
         }
 
     const int lrow = lane % 32, khalf = lane / 32;
-    float* row_w = reinterpret_cast<float*>(smem + STAGES * STAGE + RING);
+    float* row_w = reinterpret_cast<float*>(smem + STAGES * STAGE + Shape::RING);
     float my_w = 1.0f;
     if (MODE == kModeW2 && tid < BM) {
         const int64_t r = tl.row0 + tid;
@@ -695,6 +706,22 @@ __global__ __launch_bounds__(8 * kWave) void tile_kernel_fp8_256(GemmArgs g) {
             }
         }
     }
+}
+
+// 256 x 256 fp8 tiles over the ordinary 256-row tile table: a tile of at
+// most 128 rows (an expert's short remainder) runs the 128-row body, inside
+// its expert's group, so it shares the group's weight tiles in L2.
+template <int MODE>
+__global__ __launch_bounds__(8 * kWave) void tile_kernel_fp8_256(GemmArgs g) {
+    constexpr int SM = Fp8BigShape<256, MODE>::SMEM, SH = Fp8BigShape<128, MODE>::SMEM;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[SM > SH ? SM : SH];
+    const TilePos tp = map_block(blockIdx.x, *g.num_tiles, g.n_tiles_n, g.tiles);
+    if (!tp.ok) return;
+    const Tile tl = g.tiles[tp.m];
+    if (tl.row1 - tl.row0 <= 128)
+        fp8_big_body<128, MODE>(g, tl, tp.n, smem);
+    else
+        fp8_big_body<256, MODE>(g, tl, tp.n, smem);
 }
 
 }  // namespace moe

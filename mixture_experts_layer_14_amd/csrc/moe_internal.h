@@ -48,7 +48,6 @@ struct TileTableKey {
     const void* ws = nullptr;
     const int32_t* offsets = nullptr;
     int bm = 0, tail_rows = 0, split_nn = 0;
-    bool tail_table = false;  // tail tiles in a table of their own
 };
 
 struct GroupedProblem {

@@ -204,6 +204,172 @@ __global__ __launch_bounds__(WM* WN* kWave) void router_gemm_kernel(
         }
 }
 
+// 128 tokens x 128 experts on 8 waves (64 x 32 each), for many tokens: the
+// hidden rows and the gate rows (bf16, or fp32 as stored) are copied global
+// -> LDS by global_load_lds into a ring of 3 stages of 64 k (the copies of
+// the next two steps stay in flight while one multiplies; one barrier per
+// step), and an fp32 gate is split into bf16 hi + lo as its fragments are
+// read (round to nearest even, as the staged split of the 64 x 64 kernel),
+// so the logits are the same bits.  LDS rows: 128 bytes (bf16, 8 slots of 16
+// bytes) or 256 bytes (fp32, 16 slots), slot s of row r stored at s ^ (r % 8)
+// or s ^ (r % 16): the rows an operand read touches spread over all banks.
+template <bool GATE_F32>
+__global__ __launch_bounds__(512) void router_gemm_lds_kernel(const uint16_t* __restrict__ x,
+                                                              const void* __restrict__ gate, int64_t T,
+                                                              int E, int H, int parts,
+                                                              float* __restrict__ out) {
+    constexpr int BM = 128, BN = 128, WM = 2, WN = 4, NW = 8;
+    constexpr int GROWB = GATE_F32 ? 256 : 128;          // gate bytes per row and step
+    constexpr int GSLOTS = GROWB / 16;
+    constexpr int A_BYTES = BM * 128, G_BYTES = BN * GROWB;
+    constexpr int STAGE = A_BYTES + G_BYTES;
+    constexpr int STAGES = 3;
+    constexpr int A_CP = A_BYTES / 1024 / NW, G_CP = G_BYTES / 1024 / NW;  // copies per wave and step
+    constexpr int CP = A_CP + G_CP;
+    constexpr int TM = BM / WM / 32, TN = BN / WN / 32;  // 2 x 1
+    static_assert(A_BYTES % (1024 * NW) == 0 && G_BYTES % (1024 * NW) == 0, "copies split evenly");
+    static_assert(STAGES * STAGE <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = wave_index(tid);
+    const int wm = wave / WN, wn = wave % WN;
+    // block -> (token tile, expert tile), XCD-aware as in router_gemm_kernel
+    const int tiles_e = (E + BN - 1) / BN;
+    const int64_t tiles = ((T + BM - 1) / BM) * tiles_e;
+    const int64_t per = (tiles + 7) / 8;
+    const int64_t pos = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if ((blockIdx.x >> 3) >= per || pos >= tiles) return;
+    const int64_t t0 = pos / tiles_e * BM;
+    const int e0 = static_cast<int>(pos % tiles_e) * BN;
+    const int part = blockIdx.z;
+    const int nk_all = H / kRK;
+    const int k_first = part * nk_all / parts;
+    const int nk = (part + 1) * nk_all / parts - k_first;
+
+    // sources of this lane's 16-byte slot in each copy (the swizzle is an
+    // involution: the lane filling slot s of row r loads chunk s ^ f(r));
+    // rows past T or E repeat the last row (computed, never stored)
+    const uint8_t* src[CP];
+#pragma unroll
+    for (int q = 0; q < A_CP; ++q) {
+        const int c = wave * A_CP + q;
+        const int row = c * 8 + lane / 8, chunk = (lane % 8) ^ (row % 8);
+        const int64_t t = t0 + row < T ? t0 + row : T - 1;
+        src[q] = reinterpret_cast<const uint8_t*>(x + t * H) + static_cast<int64_t>(k_first) * 128 + chunk * 16;
+    }
+#pragma unroll
+    for (int q = 0; q < G_CP; ++q) {
+        const int c = wave * G_CP + q;
+        const int row = c * (1024 / GROWB) + lane / GSLOTS;
+        const int chunk = (lane % GSLOTS) ^ (row % GSLOTS);
+        const int64_t e = e0 + row < E ? e0 + row : E - 1;
+        src[A_CP + q] = static_cast<const uint8_t*>(gate) + e * H * (GATE_F32 ? 4 : 2) +
+                        static_cast<int64_t>(k_first) * GROWB + chunk * 16;
+    }
+    auto issue = [&](int kit) {
+        const int kc = kit < nk ? kit : nk - 1;  // past the end: a repeat nobody reads
+        uint8_t* st = smem + (kit % STAGES) * STAGE;
+#pragma unroll
+        for (int q = 0; q < A_CP; ++q)
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src[q] + static_cast<int64_t>(kc) * 128),
+                                             (__attribute__((address_space(3))) void*)(st + (wave * A_CP + q) * 1024),
+                                             16, 0, 0);
+#pragma unroll
+        for (int q = 0; q < G_CP; ++q)
+            __builtin_amdgcn_global_load_lds(
+                reinterpret_cast<const void*>(src[A_CP + q] + static_cast<int64_t>(kc) * GROWB),
+                (__attribute__((address_space(3))) void*)(st + A_BYTES + (wave * G_CP + q) * 1024), 16, 0, 0);
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    const int kh = lane >> 5, lr = lane & 31;
+
+    issue(0);
+    issue(1);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (CP & 15) | ((CP >> 4) << 14));  // stage 0 landed
+    __builtin_amdgcn_s_barrier();
+    for (int kit = 0; kit < nk; ++kit) {
+        // stage kit+2 into the buffer of stage kit-1 (read before the last barrier)
+        issue(kit + 2);
+        const uint8_t* sA = smem + (kit % STAGES) * STAGE;
+        const uint8_t* sG = sA + A_BYTES;
+#pragma unroll
+        for (int ks = 0; ks < kRK / 16; ++ks) {
+            const int s = ks * 2 + kh;  // bf16 chunk of this lane's 8 k values
+            u32x4 a[TM], b[TN], bl[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int r = wm * (BM / WM) + i * 32 + lr;
+                a[i] = *reinterpret_cast<const u32x4*>(sA + r * 128 + (s ^ (r % 8)) * 16);
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int r = wn * (BN / WN) + j * 32 + lr;
+                if constexpr (!GATE_F32) {
+                    b[j] = *reinterpret_cast<const u32x4*>(sG + r * 128 + (s ^ (r % 8)) * 16);
+                } else {
+                    // 8 floats: chunks 2s and 2s + 1 of the 256-byte row
+                    const u32x4 w0 = *reinterpret_cast<const u32x4*>(sG + r * 256 + ((2 * s) ^ (r % 16)) * 16);
+                    const u32x4 w1 = *reinterpret_cast<const u32x4*>(sG + r * 256 + ((2 * s + 1) ^ (r % 16)) * 16);
+                    const float f[8] = {__uint_as_float(w0[0]), __uint_as_float(w0[1]), __uint_as_float(w0[2]),
+                                        __uint_as_float(w0[3]), __uint_as_float(w1[0]), __uint_as_float(w1[1]),
+                                        __uint_as_float(w1[2]), __uint_as_float(w1[3])};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        bf16x2 h;
+                        h[0] = static_cast<__bf16>(f[2 * q]);
+                        h[1] = static_cast<__bf16>(f[2 * q + 1]);
+                        const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+                        bf16x2 l;
+                        l[0] = static_cast<__bf16>(f[2 * q] - __uint_as_float(hb << 16));
+                        l[1] = static_cast<__bf16>(f[2 * q + 1] - __uint_as_float(hb & 0xFFFF0000u));
+                        b[j][q] = hb;
+                        bl[j][q] = __builtin_bit_cast(uint32_t, l);
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, a[i]), __builtin_bit_cast(bf16x8, b[j]), acc[i][j], 0, 0, 0);
+                    if constexpr (GATE_F32)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8, a[i]), __builtin_bit_cast(bf16x8, bl[j]), acc[i][j], 0, 0,
+                            0);
+                }
+        }
+        // this wave's reads of stage kit are done and its copies of stage
+        // kit+1 landed (stage kit+2's may stay in flight); then everyone's
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (CP & 15) | ((CP >> 4) << 14));
+        __builtin_amdgcn_s_barrier();
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no copy may still write LDS
+
+    float* o = out + static_cast<int64_t>(part) * T * E;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int e = e0 + wn * (BN / WN) + j * 32 + lr;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t t = t0 + wm * (BM / WM) + i * 32 + 8 * (v / 4) + 4 * kh + (v % 4);
+                if (t < T && e < E) o[t * E + e] = acc[i][j][v];
+            }
+        }
+}
+
 // logits = sum of the parts' partial logits, in part order
 __global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restrict__ partial,
                                                             int64_t n, int parts,
@@ -283,9 +449,9 @@ hipError_t launch_router_partials(const void* hidden, int act_dtype, const void*
         const int64_t tiles = ((T + 127) / 128) * ((E + 127) / 128);
         const dim3 grid(static_cast<unsigned>(8 * ((tiles + 7) / 8)), 1, static_cast<unsigned>(pl.parts));
         if (gf32)
-            router_gemm_kernel<true, 128, 128, 2, 4><<<grid, 512, 0, stream>>>(x, gate, T, E, H, pl.parts, partials);
+            router_gemm_lds_kernel<true><<<grid, 512, 0, stream>>>(x, gate, T, E, H, pl.parts, partials);
         else
-            router_gemm_kernel<false, 128, 128, 2, 4><<<grid, 512, 0, stream>>>(x, gate, T, E, H, pl.parts, partials);
+            router_gemm_lds_kernel<false><<<grid, 512, 0, stream>>>(x, gate, T, E, H, pl.parts, partials);
     } else {
         const int64_t tiles = ((T + 63) / 64) * ((E + 63) / 64);
         const dim3 grid(static_cast<unsigned>(8 * ((tiles + 7) / 8)), 1, static_cast<unsigned>(pl.parts));
