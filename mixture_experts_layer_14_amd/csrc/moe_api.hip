@@ -342,11 +342,17 @@ int moe_router_topk(const moe_params* p, const void* hidden, const void* gate_w,
     const size_t need = direct ? 0 : static_cast<size_t>(parts) * T * E * 4;
     if (need && (!workspace || workspace_bytes < need)) return MOE_ERR_WORKSPACE;
     float* partials = direct ? router_logits : static_cast<float*>(workspace);
+    const int G = p->num_expert_group > 1 ? p->num_expert_group : 1;
+    if (moe::router_topk_one_launch(T, E, H, p->act_dtype))
+        return hip_status(moe::launch_router_topk(hidden, gate_w, gate_dtype, T, E, H, partials,
+                                                  direct ? nullptr : router_logits, e_score_correction_bias,
+                                                  p->top_k, p->scoring_func, p->renormalize ? 1 : 0, G,
+                                                  G > 1 ? p->topk_group : 1, p->routed_scaling_factor,
+                                                  topk_ids, topk_weights, as_stream(stream)));
     int got = 1;
     hipError_t err = moe::launch_router_partials(hidden, p->act_dtype, gate_w, gate_dtype, T, E, H,
                                                  partials, &got, as_stream(stream));
     if (err != hipSuccess) return hip_status(err);
-    const int G = p->num_expert_group > 1 ? p->num_expert_group : 1;
     return hip_status(moe::launch_topk(partials, got, direct ? nullptr : router_logits,
                                        e_score_correction_bias, T, E, p->top_k, p->scoring_func,
                                        p->renormalize ? 1 : 0, G, G > 1 ? p->topk_group : 1,

@@ -103,6 +103,14 @@ hipError_t launch_router_partials(const void* hidden, int act_dtype, const void*
                                   int gate_dtype, int64_t T, int E, int H, float* partials,
                                   int* parts_out, hipStream_t stream);
 // Logits [T, E] (partials, when H is split, in ws, then summed).
+// Router gate GEMM and top-k in one launch (bf16 hidden, few tokens: the
+// shapes router_topk_one_launch accepts); partials as for
+// launch_router_partials.  Overlapping such launches on one device race.
+bool router_topk_one_launch(int64_t T, int E, int H, int act_dtype);
+hipError_t launch_router_topk(const void* hidden, const void* gate, int gate_dtype, int64_t T, int E,
+                              int H, float* partials, float* logits_out, const float* bias, int K,
+                              int scoring, int renorm, int G, int TG, float rsf, int32_t* ids,
+                              float* weights, hipStream_t stream);
 hipError_t launch_router(const void* hidden, int act_dtype, const void* gate, int gate_dtype,
                          int64_t T, int E, int H, float* logits, void* ws, hipStream_t stream);
 

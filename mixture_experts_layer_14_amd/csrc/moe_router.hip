@@ -11,14 +11,31 @@
 // accuracy at bf16 MFMA rate.  Few tiles (decode) split H into parts whose
 // fp32 partial logits a second kernel sums in a fixed order: the reduce
 // kernel (moe_router_gemm) or the top-k kernel itself (moe_router_topk).
+// For few tokens the router kernel can run the top-k itself: the last blocks
+// to finish their partial logits take the tokens' top-k in slices, so gate
+// GEMM and top-k are one launch.
 // fp32 hidden: one thread per logit, fp32 FMAs in order over H.
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "moe_topk.h"
 
 namespace moe {
 namespace {
 
 constexpr int kRK = 64;  // k per step (one 128-byte bf16 row slab)
+
+// Arrivals of the router kernel's blocks at the fused top-k (zero when no
+// launch is running: the last arrival wraps it back).  One per device, so
+// fused router launches that overlap on one device race.
+__device__ uint32_t router_arrivals;
+
+// Blocks that run the fused top-k: one token per wave, at most 64 blocks
+// (the blocks waiting for the others' partial logits).
+__host__ __device__ inline uint32_t fused_topk_blocks(int64_t T, int64_t total, int waves) {
+    int64_t f = (T + waves - 1) / waves;
+    f = f < 64 ? f : 64;
+    return static_cast<uint32_t>(f < total ? f : total);
+}
 
 // 16-byte slot s of LDS row r (128-byte rows): XOR swizzle so the 32 rows one
 // MFMA operand read touches spread over all banks
@@ -27,11 +44,13 @@ __device__ __forceinline__ int rslot(int r, int s) { return s ^ (r & 7); }
 // Tile of BM tokens x BN experts on WM x WN waves (each wave (BM/WM) x
 // (BN/WN), 32 x 32 MFMA blocks); 64 x 64 on 4 waves for few tokens, 128 x
 // 128 on 8 waves for many (half the hidden and gate re-reads per logit, and
-// two independent MFMA chains per wave).
-template <bool GATE_F32, int BM, int BN, int WM, int WN>
+// two independent MFMA chains per wave).  FUSE_VPL > 0: the kernel also
+// runs the top-k (tk; experts per lane FUSE_VPL) on `out` once all of it is
+// written.
+template <bool GATE_F32, int BM, int BN, int WM, int WN, int FUSE_VPL = 0>
 __global__ __launch_bounds__(WM* WN* kWave) void router_gemm_kernel(
     const uint16_t* __restrict__ x, const void* __restrict__ gate, int64_t T, int E, int H,
-    int parts, float* __restrict__ out) {
+    int parts, float* __restrict__ out, TopkArgs tk) {
     constexpr int NT = WM * WN * kWave;
     constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
     constexpr int NB = GATE_F32 ? 2 : 1;  // gate planes in LDS: hi (and lo)
@@ -199,9 +218,47 @@ __global__ __launch_bounds__(WM* WN* kWave) void router_gemm_kernel(
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int64_t t = t0 + wm * (BM / WM) + i * 32 + 8 * (v / 4) + 4 * (lane >> 5) + (v % 4);
-                if (t < T && e < E) o[t * E + e] = acc[i][j][v];
+                if (t < T && e < E) {
+                    if constexpr (FUSE_VPL > 0)  // written through to memory: read by other blocks below
+                        __hip_atomic_store(reinterpret_cast<uint32_t*>(o + t * E + e), __float_as_uint(acc[i][j][v]),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    else
+                        o[t * E + e] = acc[i][j][v];
+                }
             }
         }
+
+    if constexpr (FUSE_VPL > 0) {
+        // Every block counts its arrival once its partial logits are out; the
+        // last `fin` to arrive wait for the count to wrap (all arrived), then
+        // run the top-k of tokens slot*NW + wave, slot*NW + wave + fin*NW, ...
+        // No block waits before it arrives, and at most `fin` (<= 64) wait, so
+        // the blocks not yet arrived are running or find a free slot: the wait
+        // ends.  Its bound only keeps a wait finite.
+        // The partial logits went out as device-coherent stores: once they are
+        // complete, the arrival count may move (no write-back of the whole L2,
+        // as a release fence would do).
+        __shared__ uint32_t s_ticket;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        const uint32_t total = static_cast<uint32_t>(tiles * parts);
+        if (tid == 0) s_ticket = atomicInc(&router_arrivals, total - 1);  // the last arrival wraps to 0
+        __syncthreads();
+        const uint32_t ticket = s_ticket;
+        const uint32_t fin = fused_topk_blocks(T, total, WM * WN);
+        if (ticket + fin < total) return;
+        if (tid == 0 && ticket + 1 < total) {
+            for (uint32_t n = 0; n < (1u << 24); ++n) {
+                if (__hip_atomic_load(&router_arrivals, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) break;
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // no stale copy of the other blocks' partial logits
+        const int64_t slot = ticket - (total - fin);
+        for (int64_t t = slot * (WM * WN) + wave; t < T; t += static_cast<int64_t>(fin) * (WM * WN))
+            topk_row<FUSE_VPL, topk_part_batch(FUSE_VPL, 32)>(tk, t, lane);
+    }
 }
 
 // 128 tokens x 128 experts on 8 waves (64 x 32 each), for many tokens: the
@@ -455,12 +512,48 @@ hipError_t launch_router_partials(const void* hidden, int act_dtype, const void*
     } else {
         const int64_t tiles = ((T + 63) / 64) * ((E + 63) / 64);
         const dim3 grid(static_cast<unsigned>(8 * ((tiles + 7) / 8)), 1, static_cast<unsigned>(pl.parts));
+        const TopkArgs none{};
         if (gf32)
-            router_gemm_kernel<true, 64, 64, 2, 2><<<grid, 256, 0, stream>>>(x, gate, T, E, H, pl.parts, partials);
+            router_gemm_kernel<true, 64, 64, 2, 2><<<grid, 256, 0, stream>>>(x, gate, T, E, H, pl.parts, partials, none);
         else
-            router_gemm_kernel<false, 64, 64, 2, 2><<<grid, 256, 0, stream>>>(x, gate, T, E, H, pl.parts, partials);
+            router_gemm_kernel<false, 64, 64, 2, 2><<<grid, 256, 0, stream>>>(x, gate, T, E, H, pl.parts, partials, none);
     }
     *parts_out = pl.parts;
+    return hipGetLastError();
+}
+
+bool router_topk_one_launch(int64_t T, int E, int H, int act_dtype) {
+    return act_dtype == 1 && T > 0 && !router_plan(T, E, H).big && T <= 256;
+}
+
+template <int VPL>
+static void launch_fused(bool gf32, dim3 grid, const uint16_t* x, const void* gate, int64_t T, int E,
+                         int H, int parts, float* partials, const TopkArgs& tk, hipStream_t stream) {
+    if (gf32)
+        router_gemm_kernel<true, 64, 64, 2, 2, VPL><<<grid, 256, 0, stream>>>(x, gate, T, E, H, parts, partials, tk);
+    else
+        router_gemm_kernel<false, 64, 64, 2, 2, VPL><<<grid, 256, 0, stream>>>(x, gate, T, E, H, parts, partials, tk);
+}
+
+hipError_t launch_router_topk(const void* hidden, const void* gate, int gate_dtype, int64_t T, int E,
+                              int H, float* partials, float* logits_out, const float* bias, int K,
+                              int scoring, int renorm, int G, int TG, float rsf, int32_t* ids,
+                              float* weights, hipStream_t stream) {
+    const RouterPlan pl = router_plan(T, E, H);
+    const TopkArgs tk{partials, pl.parts, T * E, logits_out, bias, T, E, K, scoring, renorm, G, TG, rsf, ids, weights};
+    const int64_t tiles = ((T + 63) / 64) * ((E + 63) / 64);
+    const dim3 grid(static_cast<unsigned>(8 * ((tiles + 7) / 8)), 1, static_cast<unsigned>(pl.parts));
+    const uint16_t* x = static_cast<const uint16_t*>(hidden);
+    const bool gf32 = gate_dtype == 0;
+    const int vpl = (E + kWave - 1) / kWave;
+    if (vpl <= 1)
+        launch_fused<1>(gf32, grid, x, gate, T, E, H, pl.parts, partials, tk, stream);
+    else if (vpl <= 2)
+        launch_fused<2>(gf32, grid, x, gate, T, E, H, pl.parts, partials, tk, stream);
+    else if (vpl <= 4)
+        launch_fused<4>(gf32, grid, x, gate, T, E, H, pl.parts, partials, tk, stream);
+    else
+        launch_fused<8>(gf32, grid, x, gate, T, E, H, pl.parts, partials, tk, stream);
     return hipGetLastError();
 }
 

@@ -34,6 +34,8 @@ CASES = [
 
 
 def _cfg(name):
+    if isinstance(name, synth.MoEConfig):
+        return name
     if name is None:  # 72 experts (two expert tiles, ragged), H = 192 (three k-steps)
         return dataclasses.replace(synth.CONFIGS["qwen"], name="odd", E=72, K=4, H=192, I=128)
     return synth.CONFIGS[name]
@@ -117,17 +119,28 @@ def test_router_then_topk_matches_oracle_routing():
     np.testing.assert_allclose(w.cpu().numpy()[far], r_w[far], rtol=U.WEIGHT_RTOL, atol=0)
 
 
+_DS = synth.CONFIGS["dsv3"]
 FUSED = [
-    # name, config, T, gate dtype: split-H decode shapes (partials summed by
-    # the top-k kernel), the 128 x 128 prefill tile, fp32 hidden, softmax
+    # name, config, T, gate dtype.  Up to 256 tokens (bf16 hidden) the router
+    # kernel runs the top-k itself (one launch, split-H partials summed by
+    # its last blocks); more tokens, or an fp32 hidden, take the top-k kernel
     ("dsv3_decode_f32", "dsv3", 64, "f32"),
     ("dsv3_decode_bf16", "dsv3", 64, "bf16"),
     ("dsv3_one_token", "dsv3", 1, "f32"),
+    ("dsv3_T256", "dsv3", 256, "bf16"),
+    ("dsv3_T257", "dsv3", 257, "bf16"),
     ("dsv3_prefill_f32", "dsv3", 8192, "f32"),
     ("mixtral_decode", "mixtral", 32, "bf16"),
     ("mixtral_prefill", "mixtral", 4096, "bf16"),
     ("qwen_tiles", "qwen", 300, "bf16"),
+    ("qwen_decode", "qwen", 16, "bf16"),
     ("tiny_f32_hidden", "tiny", 64, "f32"),
+    # grouped top-k with other group sizes: 8 (E = 64), 64 (a whole wave),
+    # 8 over two slots per lane (E = 128), 24 (one reduction per group)
+    ("grouped_per8", dataclasses.replace(_DS, name="g8", E=64, K=6, n_group=8, topk_group=3, H=512), 64, "f32"),
+    ("grouped_per64", dataclasses.replace(_DS, name="g64", E=256, n_group=4, topk_group=2, H=1024), 48, "bf16"),
+    ("grouped_per8_e128", dataclasses.replace(_DS, name="g8b", E=128, n_group=16, topk_group=4, H=1024), 200, "bf16"),
+    ("grouped_per24", dataclasses.replace(_DS, name="g24", E=72, K=4, n_group=3, topk_group=2, H=512), 37, "f32"),
 ]
 
 
@@ -159,6 +172,15 @@ def test_router_topk_is_router_gemm_then_topk(name, cfg, T, gdt):
     w0 = torch.empty(T, cfg.K, dtype=torch.float32, device="cuda")
     B.moe_router_gemm(p, x, g, lg, ws)
     B.moe_topk(p, lg, bias, ids0, w0)
+    torch.cuda.synchronize()
+    # the top-k against the oracle's routing of the same fp32 logits (ids
+    # bit-exact, weights to fp32 rounding) on rows at least 1e-5 from a tie
+    lgh = lg.cpu().numpy()
+    r_ids, r_w = U.oracle_route(cfg, lgh, b)
+    far = synth._rows_without_near_ties(dataclasses.replace(cfg, delta=1e-5), lgh, b)
+    assert far.sum() >= 0.8 * T - 1
+    assert np.array_equal(ids0.cpu().numpy()[far], r_ids[far])
+    np.testing.assert_allclose(w0.cpu().numpy()[far], r_w[far], rtol=U.WEIGHT_RTOL, atol=0)
     for keep_logits in (True, False):
         ids = torch.full_like(ids0, -1)
         w = torch.full_like(w0, float("nan"))
@@ -205,3 +227,34 @@ def test_router_topk_routes_like_the_oracle_dsv3_prefill():
     r_ids, _ = U.oracle_route(cfg, ref.astype(np.float32), b)
     got = ids.cpu().numpy()[rows]
     assert np.array_equal(got[far], r_ids[far])
+
+
+def test_router_topk_one_launch_repeated():
+    """The one-launch router + top-k counts its blocks' arrivals in a
+    per-device counter that each launch leaves at zero: launches of changing
+    sizes back to back (with no synchronisation between them) each match the
+    separate calls bitwise."""
+    cfg = synth.CONFIGS["dsv3"]
+    g = synth.make_gate(cfg, "bf16", device="cuda")
+    bias = torch.from_numpy(synth.make_correction_bias(cfg)).cuda()
+    runs = []
+    for T in (64, 1, 37, 256, 5, 64, 200, 64):
+        print("one-launch router T", T, flush=True)
+        x = synth.make_hidden(cfg, T, device="cuda")
+        p = _routing_params(cfg, T)
+        ws = torch.empty(max(B.moe_workspace_size(p), 256), dtype=torch.uint8, device="cuda")
+        ids = torch.full((T, cfg.K), -1, dtype=torch.int32, device="cuda")
+        w = torch.full((T, cfg.K), float("nan"), dtype=torch.float32, device="cuda")
+        B.moe_router_topk(p, x, g, bias, ids, w, None, ws)
+        runs.append((T, x, p, ids, w))
+    torch.cuda.synchronize()
+    for T, x, p, ids, w in runs:
+        ws = torch.empty(max(B.moe_workspace_size(p), 256), dtype=torch.uint8, device="cuda")
+        lg = torch.empty(T, cfg.E, dtype=torch.float32, device="cuda")
+        ids0 = torch.empty_like(ids)
+        w0 = torch.empty_like(w)
+        B.moe_router_gemm(p, x, g, lg, ws)
+        B.moe_topk(p, lg, bias, ids0, w0)
+        torch.cuda.synchronize()
+        assert torch.equal(ids, ids0), "T=%d ids differ" % T
+        assert torch.equal(w, w0), "T=%d weights differ" % T

@@ -42,6 +42,12 @@ CASES = {
     "sigmoid_e256_grouped_zero_bias": (256, 8, O.SIGMOID, 8, 4, "zero", True, 2.5),
     "sigmoid_e16_bias": (16, 4, O.SIGMOID, 0, 0, "lattice", False, 1.0),
     "sigmoid_e8_grouped_no_bias": (8, 2, O.SIGMOID, 4, 2, "none", True, 1.0),
+    # group sizes 64 (a whole wave), 8 over two lanes' slots, 16 with a part
+    # filled second slot, and 24 (not a power of two: one reduction a group)
+    "sigmoid_e256_g4_bias": (256, 8, O.SIGMOID, 4, 2, "lattice", True, 2.5),
+    "softmax_e128_g16": (128, 8, O.SOFTMAX, 16, 4, "none", True, 1.0),
+    "softmax_e96_g6": (96, 4, O.SOFTMAX, 6, 2, "none", True, 1.0),
+    "sigmoid_e72_g3_bias": (72, 4, O.SIGMOID, 3, 2, "lattice", True, 1.0),
 }
 
 ROWS_PER_KIND = 48
