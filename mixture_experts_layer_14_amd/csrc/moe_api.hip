@@ -127,7 +127,8 @@ ForwardLayout forward_layout(const moe_params* p) {
     L.inv = off; off += align256(TK * 4);
     L.xq = off; off += fp8_layer(p) ? align256(T * H) : 0;
     L.xs = off; off += fp8_layer(p) ? align256(T * (H / 128) * 4) : 0;
-    L.act = off; off += align256(R * I * act_elt(p));
+    // rows rounded up to 16: moe_forward may keep act in the packed layout
+    L.act = off; off += align256((R + 15) / 16 * 16 * I * act_elt(p));
     L.act_scale = off; off += fp8_layer(p) ? align256(R * (I / 128) * 4) : 0;
     L.scratch = off;
     size_t s = align_scratch(p);
@@ -235,7 +236,8 @@ int moe_quant_act_fp8(const moe_params* p, const void* hidden, uint8_t* q, float
 namespace {
 
 // The two GEMM entry points; `built` (moe_forward only) records the tile
-// table in the workspace across them.
+// table in the workspace across them, and marks the act buffer as
+// moe_forward's own (its layout is then the kernels' choice).
 int w13_act(const moe_params* p, const void* hidden, const float* hidden_scale, const void* w13,
             const float* w13_scale, const void* shared_w13, const float* shared_w13_scale,
             const int32_t* expert_offsets, const int32_t* sorted_slots, const float* topk_weights,
@@ -252,7 +254,9 @@ int w13_act(const moe_params* p, const void* hidden, const float* hidden_scale, 
                          (p->num_shared_experts && !shared_w13_scale)))
         return MOE_ERR_INVALID;
     if (!workspace || workspace_bytes < w13_scratch(p)) return MOE_ERR_WORKSPACE;
-    return hip_status(moe::launch_w13(problem(p, built), hidden, hidden_scale, w13, w13_scale, shared_w13,
+    moe::GroupedProblem g = problem(p, built);
+    g.act_packed = built && moe::act_packed_ok(g);  // moe_forward's own act buffer
+    return hip_status(moe::launch_w13(g, hidden, hidden_scale, w13, w13_scale, shared_w13,
                                       shared_w13_scale, expert_offsets, sorted_slots,
                                       topk_weights, act, act_scale, workspace,
                                       as_stream(stream)));
@@ -273,7 +277,9 @@ int w2_combine(const moe_params* p, const void* act, const float* act_scale, con
     if (fp8_layer(p) && (!act_scale || !w2_scale || (p->num_shared_experts && !shared_w2_scale)))
         return MOE_ERR_INVALID;
     if (!workspace || workspace_bytes < w2_scratch(p)) return MOE_ERR_WORKSPACE;
-    return hip_status(moe::launch_w2_combine(problem(p, built), act, act_scale, w2, w2_scale, shared_w2,
+    moe::GroupedProblem g = problem(p, built);
+    g.act_packed = built && moe::act_packed_ok(g);  // moe_forward's own act buffer
+    return hip_status(moe::launch_w2_combine(g, act, act_scale, w2, w2_scale, shared_w2,
                                              shared_w2_scale, expert_offsets, sorted_slots,
                                              slot_to_row, topk_weights, out, workspace,
                                              as_stream(stream)));

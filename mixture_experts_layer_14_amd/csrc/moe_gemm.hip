@@ -535,6 +535,7 @@ static void build_tiles(const GroupedProblem& p, const int32_t* offsets, int BM,
 template <class Pol, int BM, int BN, int WM, int WN, int MODE>
 static hipError_t launch_grouped(const GroupedProblem& p, GemmArgs g, const int32_t* offsets,
                                  void* ws, hipStream_t stream) {
+    if (g.a_packed || g.c_packed) return hipErrorInvalidValue;  // row-major act only
     build_tiles(p, offsets, BM, g, ws, stream);
     g.n_tiles_n = g.N / BN;
     const int64_t blocks = static_cast<int64_t>(g.max_m_tiles) * g.n_tiles_n;
@@ -604,6 +605,7 @@ template <int TM, int MODE>
 static hipError_t launch_stream(const GroupedProblem& p, GemmArgs g, const int32_t* offsets, void* ws,
                                 hipStream_t stream) {
     constexpr int NPW = MODE == kModeW13 ? MOE_STREAM_NPW13 : MOE_STREAM_NPW2;
+    if (g.a_packed || g.c_packed) return hipErrorInvalidValue;  // row-major act only
     build_tiles(p, offsets, TM * 16, g, ws, stream);
     const int groups = g.N / (NPW * 16);
     const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(g.max_m_tiles) * groups);
@@ -613,6 +615,13 @@ static hipError_t launch_stream(const GroupedProblem& p, GemmArgs g, const int32
         stream_kernel<TM, NPW, MOE_STREAM_WAVES, MODE, MOE_STREAM_U>
             <<<blocks, MOE_STREAM_WAVES * kWave, 0, stream>>>(g);
     return hipGetLastError();
+}
+
+bool act_packed_ok(const GroupedProblem& p) {
+    // bf16: every GEMM past the weight-streaming sizes runs tile_body; fp8:
+    // every GEMM runs an fp8 tile kernel
+    return (p.dtype == MOE_DTYPE_BF16 && rows_per_active_expert(p) > MOE_STREAM_MAX_ROWS) ||
+           p.dtype == MOE_DTYPE_FP8_E4M3;
 }
 
 // g is updated with the schedule's split table when the K-split schedule
@@ -743,6 +752,7 @@ hipError_t launch_w13(const GroupedProblem& p, const void* hidden, const float* 
     g.B = static_cast<const uint8_t*>(w13);
     g.B_shared = static_cast<const uint8_t*>(shared_w13);
     g.C = act;
+    g.c_packed = p.act_packed ? 1 : 0;
     g.T = p.T;
     g.routed_rows = p.T * p.K;
     g.topk = p.K;
@@ -773,6 +783,7 @@ hipError_t launch_w2_combine(const GroupedProblem& p, const void* act, const flo
     g.B_shared = static_cast<const uint8_t*>(shared_w2);
     g.topk_weights = topk_weights;
     g.C = y;
+    g.a_packed = p.act_packed ? 1 : 0;
     g.T = p.T;
     g.routed_rows = p.T * p.K;
     g.topk = p.K;

@@ -97,6 +97,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
     const int64_t K = g.Kd;                        // bytes per row (1 byte per value)
     const int nkb = static_cast<int>(K / 128);
     const BSel bw = expert_weights<MODE>(g, tl.expert, 1);
+    const bool a_pk = MODE == kModeW2 && g.a_packed;  // w2 reads a packed act
 
     const uint8_t* src[COPIES];
 #pragma unroll
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
         if (row < BM) {
             int64_t r = tl.row0 + row;
             if (r >= tl.row1) r = tl.row0;
-            src[q] = g.A + a_source_row<MODE>(g, r) * K + chunk * 16;
+            src[q] = g.A + (MODE == kModeW2 ? act_offset(g, r, chunk * 16, K) : a_source_row<MODE>(g, r) * K + chunk * 16);
         } else {
             src[q] = bw.base + packed_offset(b_weight_row<MODE, BN, 32>(g, bw, n_tile, row - BM), chunk * 16, bw.rb);
         }
@@ -150,8 +151,8 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
 #pragma unroll
         for (int q = q0; q < q1; ++q)
             __builtin_amdgcn_global_load_lds(
-                // packed B (the later copies) advances 16x faster along k
-                reinterpret_cast<const void*>(src[q] + ((wave * COPIES + q) * RPC >= BM ? off << 4 : off)),
+                // packed B (the later copies) and a packed A advance 16x faster along k
+                reinterpret_cast<const void*>(src[q] + (a_pk || (wave * COPIES + q) * RPC >= BM ? off << 4 : off)),
                 (__attribute__((address_space(3))) void*)(st + (wave * COPIES + q) * 1024), 16, 0, 0);
         if (!GROUPED && q1 == COPIES)
             __builtin_amdgcn_global_load_lds(
@@ -333,7 +334,11 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
             const float scale = fmaxf(amax, 1e-10f) / 448.0f;
             const int64_t r = tl.row0 + lt;
             if (r < tl.row1) {
-                uint8_t* qrow = q + r * g.I + static_cast<int64_t>(n_tile) * 128 + wn * 32 + 4 * khalf;
+                // packed act: columns wn*32 .. +31 lie in one 64-byte piece of the row
+                uint8_t* qrow = q + (g.c_packed ? (r >> 4) * (static_cast<int64_t>(g.I) << 4) +
+                                                      (static_cast<int64_t>(n_tile) * 2 + (wn >> 1)) * 1024 +
+                                                      (r & 15) * 64 + (wn & 1) * 32 + 4 * khalf
+                                                : r * g.I + static_cast<int64_t>(n_tile) * 128 + wn * 32 + 4 * khalf);
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
                     uint32_t word = 0;
@@ -446,6 +451,7 @@ __device__ __forceinline__ void fp8_big_body(const GemmArgs& g, const Tile tl, c
     const int nkb = static_cast<int>(K / 128);
     const int nk = 2 * nkb;                        // stages
     const BSel bw = expert_weights<MODE>(g, tl.expert, 1);
+    const bool a_pk = MODE == kModeW2 && g.a_packed;  // w2 reads a packed act
 
     // source of this lane's 16-byte slot in each of the wave's copies
     const uint8_t* src[COPIES];
@@ -456,7 +462,7 @@ __device__ __forceinline__ void fp8_big_body(const GemmArgs& g, const Tile tl, c
         if (row < BM) {
             int64_t r = tl.row0 + row;
             if (r >= tl.row1) r = tl.row0;  // ragged tail: copy a valid row, never stored
-            src[q] = g.A + a_source_row<MODE>(g, r) * K + chunk * 16;
+            src[q] = g.A + (MODE == kModeW2 ? act_offset(g, r, chunk * 16, K) : a_source_row<MODE>(g, r) * K + chunk * 16);
         } else {
             src[q] = bw.base + packed_offset(b_weight_row<MODE, BN, 32>(g, bw, n_tile, row - BM), chunk * 16, bw.rb);
         }
@@ -492,8 +498,8 @@ __device__ __forceinline__ void fp8_big_body(const GemmArgs& g, const Tile tl, c
 #pragma unroll
         for (int q = 0; q < COPIES; ++q)
             __builtin_amdgcn_global_load_lds(
-                // packed B (the later copies) advances 16x faster along k
-                reinterpret_cast<const void*>(src[q] + ((wave * COPIES + q) * RPC >= BM ? off << 4 : off)),
+                // packed B (the later copies) and a packed A advance 16x faster along k
+                reinterpret_cast<const void*>(src[q] + (a_pk || (wave * COPIES + q) * RPC >= BM ? off << 4 : off)),
                 (__attribute__((address_space(3))) void*)(st + (wave * COPIES + q) * 1024), 16, 0, 0);
     };
 
@@ -670,7 +676,11 @@ __device__ __forceinline__ void fp8_big_body(const GemmArgs& g, const Tile tl, c
             const float scale = fmaxf(amax, 1e-10f) / 448.0f;
             const int64_t r = tl.row0 + lt;
             if (r < tl.row1) {
-                uint8_t* qrow = q + r * g.I + static_cast<int64_t>(n_tile) * 128 + wn * 32 + 4 * khalf;
+                // packed act: columns wn*32 .. +31 lie in one 64-byte piece of the row
+                uint8_t* qrow = q + (g.c_packed ? (r >> 4) * (static_cast<int64_t>(g.I) << 4) +
+                                                      (static_cast<int64_t>(n_tile) * 2 + (wn >> 1)) * 1024 +
+                                                      (r & 15) * 64 + (wn & 1) * 32 + 4 * khalf
+                                                : r * g.I + static_cast<int64_t>(n_tile) * 128 + wn * 32 + 4 * khalf);
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
                     uint32_t word = 0;

@@ -62,6 +62,11 @@ struct GemmArgs {
     int32_t weight_in;
     float act_alpha;
     float act_limit;
+    // act in the packed layout of the weights (moe_forward's own act buffer,
+    // tile kernels only): written so by w13 (c_packed), read so by w2
+    // (a_packed), every 16-row x 64-byte piece one contiguous KiB
+    int32_t a_packed;
+    int32_t c_packed;
 };
 
 constexpr int kRowBytes = 128;               // bytes of one row per k-iteration
@@ -85,6 +90,19 @@ __device__ __forceinline__ int64_t a_source_row(const GemmArgs& g, int64_t r) {
 // strided row pieces into one sequential burst.  Byte offset of (row, byte):
 __device__ __forceinline__ int64_t packed_offset(int64_t row, int64_t byte, int64_t row_bytes) {
     return (row >> 4) * (row_bytes << 4) + (byte >> 6) * 1024 + (row & 15) * 64 + (byte & 63);
+}
+
+// Byte offset of (row r, byte `byte`) of a w2 A operand (act): packed or
+// row-major with `row_bytes` per row.
+__device__ __forceinline__ int64_t act_offset(const GemmArgs& g, int64_t r, int64_t byte, int64_t row_bytes) {
+    return g.a_packed ? packed_offset(r, byte, row_bytes) : r * row_bytes + byte;
+}
+
+// Element index of (row r, column c) of the bf16 act written by w13
+// (32 elements per 64-byte piece).
+__device__ __forceinline__ int64_t act_store_index(const GemmArgs& g, int64_t r, int64_t c) {
+    return g.c_packed ? (r >> 4) * (static_cast<int64_t>(g.I) << 4) + (c >> 5) * 512 + (r & 15) * 32 + (c & 31)
+                      : r * g.I + c;
 }
 
 // Routing weight of permuted row r for the w2 epilogue (shared rows, and
@@ -341,7 +359,8 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile tl, cons
         if (row < BM) {
             int64_t r = tl.row0 + row;
             if (r >= tl.row1) r = tl.row0;  // ragged tail: copy a valid row, never stored
-            src[q] = g.A + a_source_row<MODE>(g, r) * eltK + chunk * 16;
+            src[q] = g.A + (MODE == kModeW2 ? act_offset(g, r, chunk * 16, eltK)
+                                            : a_source_row<MODE>(g, r) * eltK + chunk * 16);
         } else {
             src[q] = bw.base + packed_offset(b_weight_row<MODE, BN, 32>(g, bw, n_tile, row - BM), chunk * 16, bw.rb);
         }
@@ -350,9 +369,11 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile tl, cons
     const int nk_all = static_cast<int>(eltK / ROWB);
     const int k_first = kpart * nk_all / nparts;
     const int nk = (kpart + 1) * nk_all / nparts - k_first;
-    // bytes per k-iteration along a source row: ROWB in the row-major A,
+    // bytes per k-iteration along a source row: ROWB in a row-major A,
     // ROWB/64 KiB-blocks in the packed B (whose copies are the later ones)
-    auto kstep_shift = [&](int q) { return (wave * COPIES + q) * RPC >= BM ? 4 : 0; };
+    // and in a packed A
+    const bool a_pk = MODE == kModeW2 && g.a_packed;
+    auto kstep_shift = [&](int q) { return a_pk || (wave * COPIES + q) * RPC >= BM ? 4 : 0; };
 #pragma unroll
     for (int q = 0; q < COPIES; ++q) src[q] += (static_cast<int64_t>(k_first) * ROWB) << kstep_shift(q);
 
@@ -522,7 +543,42 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile tl, cons
     auto row_ok = [&](auto full_tag, int dr) {
         return decltype(full_tag)::value || tl.row0 + lr0 + dr < tl.row1;
     };
-    if (MODE == kModeW13) {
+    if (MODE == kModeW13 && g.c_packed) {
+        // act in the packed layout: the 32 columns of a lane group are one
+        // 64-byte piece of their row there too
+        uint16_t* act = static_cast<uint16_t*>(g.C);
+        const int64_t r0 = tl.row0 + lr0;
+        auto put = [&](int dr, int64_t col, float a) {
+            if (row_ok(std::false_type{}, dr)) act[act_store_index(g, r0 + dr, col)] = f32_to_bf16_bits(a);
+        };
+        if (g.gated) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int p = 0; p < TN / 2; ++p) {
+                    const int64_t col = static_cast<int64_t>(n_tile) * (BN / 2) + (wn * (TN / 2) + p) * 32 + ccol;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int dr = i * 32 + 8 * (v / 4) + v % 4;
+                        const float w = use_w ? row_w[lr0 + dr] : 1.0f;
+                        put(dr, col, glu_act(g, acc[i][2 * p][v] * w, acc[i][2 * p + 1][v] * w));
+                    }
+                }
+        } else {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int64_t col = static_cast<int64_t>(n_tile) * BN + wn * WTN + j * 32 + ccol;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int dr = i * 32 + 8 * (v / 4) + v % 4;
+                        const float w = use_w ? row_w[lr0 + dr] : 1.0f;
+                        put(dr, col, silu_a(acc[i][j][v] * w, g.act_alpha));
+                    }
+                }
+        }
+    } else if (MODE == kModeW13) {
         uint16_t* act = static_cast<uint16_t*>(g.C) + static_cast<int64_t>(tl.row0 + lr0) * g.I;
         if (g.gated) {
             auto epi = [&](auto full_tag, auto w_tag) {

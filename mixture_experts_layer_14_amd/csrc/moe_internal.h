@@ -66,9 +66,16 @@ struct GroupedProblem {
     float alpha = 1.0f;
     float limit = 0.0f;
     int weight_in = 0;
+    // act between the two GEMMs in the weights' packed layout (moe_forward's
+    // own buffer, rows rounded up to 16; shapes act_packed_ok accepts)
+    bool act_packed = false;
     // record of the table in the workspace (null: always build)
     TileTableKey* built = nullptr;
 };
+
+// Whether both GEMMs of the problem run tile kernels, which can hand the act
+// over in the packed layout.
+bool act_packed_ok(const GroupedProblem& p);
 
 // Scratch bytes of one grouped GEMM launch (tile table).
 size_t gemm_tile_workspace_bytes(const GroupedProblem& p);
