@@ -462,14 +462,16 @@ def profile_config(name, steps, warmup):
 
 
 def source_digest():
-    """sha256 over the HIP sources: identifies the kernels a stored counter
-    measurement belongs to."""
+    """sha256 over the sources of the grouped GEMM kernels (and the headers
+    they share): identifies the kernels a stored counter measurement belongs
+    to."""
     import glob
     import hashlib
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mixture_experts_layer_14_amd", "csrc")
-    for path in sorted(glob.glob(os.path.join(csrc, "*"))):
+    names = ("moe_gemm*", "moe_device.h", "moe_internal.h")
+    for path in sorted(p for n in names for p in glob.glob(os.path.join(csrc, n))):
         with open(path, "rb") as f:
             h.update(os.path.basename(path).encode())
             h.update(f.read())
