@@ -12,12 +12,14 @@
 //   select K keys, descending, exact ties to the lower index;
 //   weight = score (renormalised over the K selected if asked) * rsf.
 //
-// Layout: lane l holds experts e = l + 64*v, v < VPL, so every row load is
-// a run of coalesced 256-byte wave accesses.  A selection round is a DPP
-// max of the order-preserving 32-bit keys, then one ballot per v for the
-// lowest index holding it.  Groups of a power-of-two size up to 64 are whole
-// lane segments of one v: their two largest keys come from one segmented
-// DPP reduction for all groups at once.
+// Layout: lane l holds the VPL consecutive experts e = VPL*l + v, so a row
+// (or a part of it) is one vector load per lane and the wave reads it as one
+// contiguous run.  A selection round is a DPP max of the order-preserving
+// 32-bit keys, then one ballot per v and the lowest index holding the max.
+// When a group is a whole number of lanes (a power of two up to 64 of them)
+// or a run of a lane's own experts, the two largest keys of every group come
+// from the lane's own values plus one segmented DPP reduction, for all
+// groups at once.
 //
 // The logits may come as `parts` partial sums (the router gate GEMM with H
 // split into parts, parts * T * E floats): they are added in part order, the
@@ -47,57 +49,112 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return readlane_u32(v, 63);
 }
 
-// Index (64 v + lane) of the largest okey among the candidates `ok`, exact
-// ties to the lower index; the winner stops being a candidate.  -1 when no
-// candidate is left (the parameter checks rule that out).
+// Index (VPL*lane + v) of the largest okey among the candidates `ok`,
+// exact ties to the lower index; the winner stops being a candidate.  -1
+// when no candidate is left (the parameter checks rule that out).
 template <int VPL>
 __device__ __forceinline__ int take_first_max(const uint32_t (&okey)[VPL], bool (&ok)[VPL], int lane) {
     uint32_t m = 0;
 #pragma unroll
     for (int v = 0; v < VPL; ++v) m = ok[v] && okey[v] > m ? okey[v] : m;
     m = wave_max_u32(m);
-    int sel = -1;
+    int sel = 0x7fffffff;
 #pragma unroll
-    for (int v = VPL - 1; v >= 0; --v) {
+    for (int v = 0; v < VPL; ++v) {
         const uint64_t b = __ballot(ok[v] && okey[v] == m);
-        if (b) sel = v * kWave + __builtin_ctzll(b);
+        const int i = b ? __builtin_ctzll(b) * VPL + v : 0x7fffffff;
+        sel = i < sel ? i : sel;
     }
+    sel = sel == 0x7fffffff ? -1 : sel;
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) ok[v] = ok[v] && v * kWave + lane != sel;
+    for (int v = 0; v < VPL; ++v) ok[v] = ok[v] && VPL * lane + v != sel;
     return sel;
 }
 
-// Top-k of token t (its wave calls it; `lane` = lane in the wave).  PB part
-// loads are issued before their adds.
-template <int VPL, int PB>
-__device__ __forceinline__ void topk_row(const TopkArgs& a, int64_t t, int lane) {
-    const int E = a.E;
-    const float* row = a.logits + t * E;
-    float key[VPL], score[VPL];
-    bool cand[VPL];
+// VPL consecutive floats of `src` from element VPL*lane (VEC: as vector
+// loads, the caller having checked that n is a multiple of VPL and `src`
+// aligned to the vector), elements at or past n reading `fill`.  No branch:
+// a lane past n loads an element below n and discards it, so a batch of
+// these loads stays in flight together.
+template <int VPL, bool VEC>
+__device__ __forceinline__ void load_run(const float* src, int lane, int n, float fill, float (&out)[VPL]) {
+    const int e0 = VPL * lane;
+    if constexpr (VEC && VPL == 2) {
+        const float2 x = *reinterpret_cast<const float2*>(src + (e0 < n ? e0 : 0));
+        out[0] = e0 < n ? x.x : fill;
+        out[1] = e0 < n ? x.y : fill;
+    } else if constexpr (VEC && VPL % 4 == 0) {
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-        const int e = lane + kWave * v;
-        cand[v] = e < E;
-        key[v] = cand[v] ? row[e] : -INFINITY;
+        for (int h = 0; h < VPL / 4; ++h) {
+            const float4 x = *reinterpret_cast<const float4*>(src + (e0 < n ? e0 + 4 * h : 0));
+            out[4 * h] = e0 < n ? x.x : fill;
+            out[4 * h + 1] = e0 < n ? x.y : fill;
+            out[4 * h + 2] = e0 < n ? x.z : fill;
+            out[4 * h + 3] = e0 < n ? x.w : fill;
+        }
+    } else {
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            const float x = src[e0 + v < n ? e0 + v : n - 1];
+            out[v] = e0 + v < n ? x : fill;
+        }
     }
+}
+
+// Whether runs of VPL floats at `p` may be loaded as vectors (see load_run).
+template <int VPL>
+__device__ __forceinline__ bool vec_ok(const void* p, int n) {
+    constexpr uintptr_t kAlign = VPL == 2 ? 8 : 16;
+    return VPL > 1 && n % VPL == 0 && (reinterpret_cast<uintptr_t>(p) & (kAlign - 1)) == 0;
+}
+
+// The logits of token t, summed over the parts in part order; PB part loads
+// are issued before their adds (parts past the last load the last part
+// again and are not added).
+template <int VPL, int PB, bool VEC>
+__device__ __forceinline__ void load_logits(const TopkArgs& a, int64_t t, int lane, float (&key)[VPL]) {
+    const float* row = a.logits + t * a.E;
+    load_run<VPL, VEC>(row, lane, a.E, -INFINITY, key);
     for (int p0 = 1; p0 < a.parts; p0 += PB) {
         float pl[PB][VPL];
 #pragma unroll
-        for (int q = 0; q < PB; ++q)
-#pragma unroll
-            for (int v = 0; v < VPL; ++v)
-                pl[q][v] = (p0 + q < a.parts && cand[v]) ? row[(p0 + q) * a.part_stride + lane + kWave * v] : 0.0f;
+        for (int q = 0; q < PB; ++q) {
+            const int p = p0 + q < a.parts ? p0 + q : a.parts - 1;
+            load_run<VPL, VEC>(row + p * a.part_stride, lane, a.E, 0.0f, pl[q]);
+        }
 #pragma unroll
         for (int q = 0; q < PB; ++q)
 #pragma unroll
             for (int v = 0; v < VPL; ++v)
                 if (p0 + q < a.parts) key[v] += pl[q][v];
     }
+}
+
+// (largest, second largest) of two disjoint sets
+__device__ __forceinline__ float2 merge_top2(float2 x, float2 y) {
+    return float2{fmaxf(x.x, y.x), fmaxf(fminf(x.x, y.x), fmaxf(x.y, y.y))};
+}
+
+// Top-k of token t (its wave calls it; `lane` = lane in the wave).  PB part
+// loads are issued before their adds.
+template <int VPL, int PB>
+__device__ __forceinline__ void topk_row(const TopkArgs& a, int64_t t, int lane) {
+    static_assert(VPL == 1 || VPL == 2 || VPL % 4 == 0, "vector runs of 1, 2 or 4k floats");
+    const int E = a.E;
+    float key[VPL], score[VPL];
+    bool cand[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) cand[v] = VPL * lane + v < E;
+    // rows start at multiples of E floats from `logits`, parts at multiples
+    // of T*E: vector loads when the base allows them
+    if (vec_ok<VPL>(a.logits, E))
+        load_logits<VPL, PB, true>(a, t, lane, key);
+    else
+        load_logits<VPL, PB, false>(a, t, lane, key);
     if (a.logits_out) {
 #pragma unroll
         for (int v = 0; v < VPL; ++v)
-            if (cand[v]) a.logits_out[t * E + lane + kWave * v] = key[v];
+            if (cand[v]) a.logits_out[t * E + VPL * lane + v] = key[v];
     }
 
     float softmax_sum = 0.0f;
@@ -114,72 +171,96 @@ __device__ __forceinline__ void topk_row(const TopkArgs& a, int64_t t, int lane)
         }
         softmax_sum = wave_sum_f32(s);
     } else {
+        float bias[VPL];
+        if (a.bias && vec_ok<VPL>(a.bias, E))
+            load_run<VPL, true>(a.bias, lane, E, 0.0f, bias);
+        else if (a.bias)
+            load_run<VPL, false>(a.bias, lane, E, 0.0f, bias);
+        else
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) bias[v] = 0.0f;
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
-            const int e = lane + kWave * v;
             score[v] = cand[v] ? 1.0f / (1.0f + expf(-key[v])) : 0.0f;
-            key[v] = cand[v] ? score[v] + (a.bias ? a.bias[e] : 0.0f) : -INFINITY;
+            key[v] = cand[v] ? score[v] + bias[v] : -INFINITY;
         }
     }
 
     if (a.G > 1) {
         const int per = E / a.G;
         const bool two = a.bias != nullptr && per >= 2;  // group score: two largest keys, or the largest
-        // (largest, second largest) of two disjoint sets
-        auto merge = [](float2 x, float2 y) {
-            return float2{fmaxf(x.x, y.x), fmaxf(fminf(x.x, y.x), fmaxf(x.y, y.y))};
-        };
         const float2 none{-INFINITY, -INFINITY};
-        if (per <= kWave && (per & (per - 1)) == 0) {
-            // every group is the lane segment [j*per, (j+1)*per) of one v: the
-            // row shifts and broadcasts of a wave reduction, stopped at the
-            // segment size, leave each group's pair in the segment's last lane
-            float2 top[VPL];
-#pragma unroll
-            for (int v = 0; v < VPL; ++v) top[v] = cand[v] ? float2{key[v], -INFINITY} : none;
+        const int seg = per / VPL;  // lanes per group, when a group is whole lanes
+        const bool lanes_fast = per % VPL == 0 && seg <= kWave && (seg & (seg - 1)) == 0;
+        const bool inlane_fast = per < VPL && VPL % per == 0;
+        if (lanes_fast || inlane_fast) {
+            // pair[v]: the (largest, second) of the lane's keys of v's group
+            // up to v; at the group's last position, of the whole group
+            float2 pair[VPL];
 #pragma unroll
             for (int v = 0; v < VPL; ++v) {
-                if (per >= 2) top[v] = dpp_step<0x111, 0xF>(top[v], none, merge);  // row_shr:1
-                if (per >= 4) top[v] = dpp_step<0x112, 0xF>(top[v], none, merge);  // row_shr:2
-                if (per >= 8) top[v] = dpp_step<0x114, 0xF>(top[v], none, merge);  // row_shr:4
-                if (per >= 16) top[v] = dpp_step<0x118, 0xF>(top[v], none, merge); // row_shr:8
-                if (per >= 32) top[v] = dpp_step<0x142, 0xA>(top[v], none, merge); // row_bcast:15
-                if (per >= 64) top[v] = dpp_step<0x143, 0xC>(top[v], none, merge); // row_bcast:31
+                pair[v] = cand[v] ? float2{key[v], -INFINITY} : none;
+                if (v > 0 && (lanes_fast || v % per != 0)) pair[v] = merge_top2(pair[v - 1], pair[v]);
             }
-            const bool last = (lane & (per - 1)) == per - 1;
-            uint32_t gkey[VPL];
             bool gok[VPL];
+            if (lanes_fast) {
+                // the group spans `seg` lanes: a segmented reduction of the
+                // lanes' pairs leaves the group's pair in its last lane
+                float2 p = pair[VPL - 1];
+                if (seg >= 2) p = dpp_step<0x111, 0xF>(p, none, merge_top2);   // row_shr:1
+                if (seg >= 4) p = dpp_step<0x112, 0xF>(p, none, merge_top2);   // row_shr:2
+                if (seg >= 8) p = dpp_step<0x114, 0xF>(p, none, merge_top2);   // row_shr:4
+                if (seg >= 16) p = dpp_step<0x118, 0xF>(p, none, merge_top2);  // row_shr:8
+                if (seg >= 32) p = dpp_step<0x142, 0xA>(p, none, merge_top2);  // row_bcast:15
+                if (seg >= 64) p = dpp_step<0x143, 0xC>(p, none, merge_top2);  // row_bcast:31
+                pair[VPL - 1] = p;
+                const bool last = (lane & (seg - 1)) == seg - 1 && VPL * lane < E;
 #pragma unroll
-            for (int v = 0; v < VPL; ++v) {
-                gok[v] = last && (v * kWave + lane) / per < a.G;
-                gkey[v] = ordered_bits(two ? top[v].x + top[v].y : top[v].x);
+                for (int v = 0; v < VPL; ++v) gok[v] = v == VPL - 1 && last;
+            } else {
+#pragma unroll
+                for (int v = 0; v < VPL; ++v) gok[v] = v % per == per - 1 && VPL * lane + v < E;
             }
-            // the TG best groups (ties to the lower group, i.e. the lower
-            // segment end), then every lane of a kept segment stays eligible
-            uint64_t kept[VPL];
+            // the TG best groups; a group is named by its last position, in
+            // the order of the groups
+            uint32_t gkey[VPL];
 #pragma unroll
-            for (int v = 0; v < VPL; ++v) kept[v] = 0;
-            for (int r = 0; r < a.TG; ++r) {
-                const int sel = take_first_max(gkey, gok, lane);
+            for (int v = 0; v < VPL; ++v) gkey[v] = ordered_bits(two ? pair[v].x + pair[v].y : pair[v].x);
+            bool gsel[VPL];
 #pragma unroll
-                for (int v = 0; v < VPL; ++v)
-                    if (v == sel / kWave) kept[v] |= 1ull << (sel & (kWave - 1));
+            for (int v = 0; v < VPL; ++v) gsel[v] = gok[v];
+            for (int r = 0; r < a.TG; ++r) take_first_max(gkey, gok, lane);
+            // selected = was a candidate group end and is no longer one
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) gsel[v] = gsel[v] && !gok[v];
+            if (lanes_fast) {
+                const uint64_t kept = __ballot(gsel[VPL - 1]);
+                const bool mine = (kept >> (lane | (seg - 1))) & 1ull;
+#pragma unroll
+                for (int v = 0; v < VPL; ++v) cand[v] = cand[v] && mine;
+            } else {
+#pragma unroll
+                for (int v = 0; v < VPL; ++v) {
+                    bool k = false;
+#pragma unroll
+                    for (int u = 0; u < VPL; ++u)
+                        if (u / per == v / per && u % per == per - 1) k = gsel[u];
+                    cand[v] = cand[v] && k;
+                }
             }
-#pragma unroll
-            for (int v = 0; v < VPL; ++v) cand[v] = cand[v] && ((kept[v] >> (lane | (per - 1))) & 1ull);
         } else {
             // other group sizes: one wave reduction per group; group g's score
             // lands in lane g (G <= 64)
             int grp[VPL];
 #pragma unroll
-            for (int v = 0; v < VPL; ++v) grp[v] = (lane + kWave * v) / per;
+            for (int v = 0; v < VPL; ++v) grp[v] = (VPL * lane + v) / per;
             float my_gscore = -INFINITY;
             for (int g = 0; g < a.G; ++g) {
                 float2 top = none;
 #pragma unroll
                 for (int v = 0; v < VPL; ++v)
-                    if (cand[v] && grp[v] == g) top = merge(top, float2{key[v], -INFINITY});
-                top = wave_reduce_to_lane63(top, none, merge);
+                    if (cand[v] && grp[v] == g) top = merge_top2(top, float2{key[v], -INFINITY});
+                top = wave_reduce_to_lane63(top, none, merge_top2);
                 const float b1 = __uint_as_float(readlane_u32(__float_as_uint(top.x), 63));
                 const float b2 = __uint_as_float(readlane_u32(__float_as_uint(top.y), 63));
                 if (lane == g) my_gscore = two ? b1 + b2 : b1;
@@ -203,13 +284,13 @@ __device__ __forceinline__ void topk_row(const TopkArgs& a, int64_t t, int lane)
     float my_w = 0.0f, sel_sum = 0.0f;
     for (int k = 0; k < a.K; ++k) {
         const int e_sel = take_first_max(okey, cand, lane);
-        const int owner = e_sel & (kWave - 1);
-        const int v_sel = e_sel / kWave;
+        const int owner = e_sel / VPL;
+        const int v_sel = e_sel - owner * VPL;
         float s_mine = 0.0f;
 #pragma unroll
         for (int v = 0; v < VPL; ++v)
             if (v == v_sel) s_mine = score[v];
-        const float s_sel = __uint_as_float(readlane_u32(__float_as_uint(s_mine), owner));
+        const float s_sel = __uint_as_float(readlane_u32(__float_as_uint(s_mine), owner & (kWave - 1)));
         sel_sum += s_sel;
         if (lane == k) {
             my_id = e_sel;
