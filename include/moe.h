@@ -180,11 +180,17 @@ int moe_router_gemm(const moe_params *p, const void *hidden, const void *gate_w,
  *   router_logits  [T, E] fp32 out, or NULL: the logits (bitwise those of
  *                  moe_router_gemm).
  * The GEMM writes partial logits of a split hidden dimension (decode sizes)
- * into the workspace, and the top-k kernel adds them in a fixed order as it
- * reads them, so the ids and weights are bitwise those of moe_router_gemm
- * followed by moe_topk; two launches in all.
+ * into the workspace and the top-k adds them in a fixed order as it reads
+ * them, so the ids and weights are bitwise those of moe_router_gemm
+ * followed by moe_topk.  With a bf16 hidden and at most 256 tokens this is
+ * one launch: the router kernel's last blocks run the top-k once every
+ * block's partial logits are written, counting arrivals in a device array
+ * of the library (64 counters, taken in turn by successive calls, each left
+ * at zero), so at most 64 such calls may be in flight on one device at a
+ * time; otherwise a GEMM launch and a top-k launch.
  *   workspace      >= moe_workspace_size(p) bytes (unused when there is one
- *                  part and router_logits is given).
+ *                  part and router_logits is given).  Calls in flight at the
+ *                  same time need workspaces of their own.
  * Errors: as moe_router_gemm and moe_topk. */
 int moe_router_topk(const moe_params *p, const void *hidden, const void *gate_w,
                     int32_t gate_dtype, const float *e_score_correction_bias,

@@ -15,6 +15,8 @@
 // to finish their partial logits take the tokens' top-k in slices, so gate
 // GEMM and top-k are one launch.
 // fp32 hidden: one thread per logit, fp32 FMAs in order over H.
+#include <atomic>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 #include "moe_topk.h"
@@ -24,10 +26,13 @@ namespace {
 
 constexpr int kRK = 64;  // k per step (one 128-byte bf16 row slab)
 
-// Arrivals of the router kernel's blocks at the fused top-k (zero when no
-// launch is running: the last arrival wraps it back).  One per device, so
-// fused router launches that overlap on one device race.
-__device__ uint32_t router_arrivals;
+// Arrival counts of the router kernel's blocks at the fused top-k, one per
+// launch in flight (zero when none runs on it: the last arrival wraps it
+// back).  Each device holds its own array; the host hands successive
+// launches successive slots, so up to kArrivalSlots launches may overlap
+// on one device.
+constexpr int kArrivalSlots = 64;
+__device__ uint32_t router_arrivals[kArrivalSlots];
 
 // Blocks that run the fused top-k: one token per wave, at most 64 blocks
 // (the blocks waiting for the others' partial logits).
@@ -50,7 +55,7 @@ __device__ __forceinline__ int rslot(int r, int s) { return s ^ (r & 7); }
 template <bool GATE_F32, int BM, int BN, int WM, int WN, int FUSE_VPL = 0>
 __global__ __launch_bounds__(WM* WN* kWave) void router_gemm_kernel(
     const uint16_t* __restrict__ x, const void* __restrict__ gate, int64_t T, int E, int H,
-    int parts, float* __restrict__ out, TopkArgs tk) {
+    int parts, float* __restrict__ out, TopkArgs tk, int slot = 0) {
     constexpr int NT = WM * WN * kWave;
     constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
     constexpr int NB = GATE_F32 ? 2 : 1;  // gate planes in LDS: hi (and lo)
@@ -242,14 +247,15 @@ __global__ __launch_bounds__(WM* WN* kWave) void router_gemm_kernel(
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         const uint32_t total = static_cast<uint32_t>(tiles * parts);
-        if (tid == 0) s_ticket = atomicInc(&router_arrivals, total - 1);  // the last arrival wraps to 0
+        uint32_t* const arrivals = router_arrivals + slot;
+        if (tid == 0) s_ticket = atomicInc(arrivals, total - 1);  // the last arrival wraps to 0
         __syncthreads();
         const uint32_t ticket = s_ticket;
         const uint32_t fin = fused_topk_blocks(T, total, WM * WN);
         if (ticket + fin < total) return;
         if (tid == 0 && ticket + 1 < total) {
             for (uint32_t n = 0; n < (1u << 24); ++n) {
-                if (__hip_atomic_load(&router_arrivals, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) break;
+                if (__hip_atomic_load(arrivals, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) break;
                 __builtin_amdgcn_s_sleep(1);
             }
         }
@@ -529,10 +535,13 @@ bool router_topk_one_launch(int64_t T, int E, int H, int act_dtype) {
 template <int VPL>
 static void launch_fused(bool gf32, dim3 grid, const uint16_t* x, const void* gate, int64_t T, int E,
                          int H, int parts, float* partials, const TopkArgs& tk, hipStream_t stream) {
+    // successive launches take successive arrival counters
+    static std::atomic<uint32_t> next_slot{0};
+    const int slot = static_cast<int>(next_slot.fetch_add(1, std::memory_order_relaxed) % kArrivalSlots);
     if (gf32)
-        router_gemm_kernel<true, 64, 64, 2, 2, VPL><<<grid, 256, 0, stream>>>(x, gate, T, E, H, parts, partials, tk);
+        router_gemm_kernel<true, 64, 64, 2, 2, VPL><<<grid, 256, 0, stream>>>(x, gate, T, E, H, parts, partials, tk, slot);
     else
-        router_gemm_kernel<false, 64, 64, 2, 2, VPL><<<grid, 256, 0, stream>>>(x, gate, T, E, H, parts, partials, tk);
+        router_gemm_kernel<false, 64, 64, 2, 2, VPL><<<grid, 256, 0, stream>>>(x, gate, T, E, H, parts, partials, tk, slot);
 }
 
 hipError_t launch_router_topk(const void* hidden, const void* gate, int gate_dtype, int64_t T, int E,

@@ -258,3 +258,38 @@ def test_router_topk_one_launch_repeated():
         torch.cuda.synchronize()
         assert torch.equal(ids, ids0), "T=%d ids differ" % T
         assert torch.equal(w, w0), "T=%d weights differ" % T
+
+
+def test_router_topk_one_launch_on_two_streams():
+    """One-launch router calls on two streams at once (workspaces of their
+    own) take different arrival counters: each matches the separate calls
+    bitwise."""
+    cfg = synth.CONFIGS["dsv3"]
+    g = synth.make_gate(cfg, "bf16", device="cuda")
+    bias = torch.from_numpy(synth.make_correction_bias(cfg)).cuda()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    jobs = []
+    for i, T in enumerate((64, 48, 64, 17, 256, 64)):
+        x = synth.make_hidden(cfg, T, device="cuda")
+        p = _routing_params(cfg, T)
+        ws = torch.empty(max(B.moe_workspace_size(p), 256), dtype=torch.uint8, device="cuda")
+        ids = torch.full((T, cfg.K), -1, dtype=torch.int32, device="cuda")
+        w = torch.full((T, cfg.K), float("nan"), dtype=torch.float32, device="cuda")
+        jobs.append((T, x, p, ws, ids, w, streams[i % 2]))
+    torch.cuda.synchronize()
+    print("one-launch router on two streams", flush=True)
+    for _ in range(3):
+        for T, x, p, ws, ids, w, s in jobs:
+            with torch.cuda.stream(s):
+                B.moe_router_topk(p, x, g, bias, ids, w, None, ws,
+                                  stream=torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for T, x, p, ws, ids, w, s in jobs:
+        lg = torch.empty(T, cfg.E, dtype=torch.float32, device="cuda")
+        ids0 = torch.empty_like(ids)
+        w0 = torch.empty_like(w)
+        B.moe_router_gemm(p, x, g, lg, ws)
+        B.moe_topk(p, lg, bias, ids0, w0)
+        torch.cuda.synchronize()
+        assert torch.equal(ids, ids0), "T=%d ids differ" % T
+        assert torch.equal(w, w0), "T=%d weights differ" % T
