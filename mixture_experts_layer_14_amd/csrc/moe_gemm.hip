@@ -609,11 +609,15 @@ static hipError_t launch_stream(const GroupedProblem& p, GemmArgs g, const int32
     build_tiles(p, offsets, TM * 16, g, ws, stream);
     const int groups = g.N / (NPW * 16);
     const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(g.max_m_tiles) * groups);
-    if (g.Kd >= MOE_STREAM_LONG_K)
-        stream_kernel<TM, NPW, 8, MODE, MOE_STREAM_U><<<blocks, 8 * kWave, 0, stream>>>(g);
-    else
-        stream_kernel<TM, NPW, MOE_STREAM_WAVES, MODE, MOE_STREAM_U>
-            <<<blocks, MOE_STREAM_WAVES * kWave, 0, stream>>>(g);
+    // (4-row-group tiles keep 4 waves: with 8 their registers spill)
+    if constexpr (TM < 4) {
+        if (g.Kd >= MOE_STREAM_LONG_K) {
+            stream_kernel<TM, NPW, 8, MODE, MOE_STREAM_U><<<blocks, 8 * kWave, 0, stream>>>(g);
+            return hipGetLastError();
+        }
+    }
+    stream_kernel<TM, NPW, MOE_STREAM_WAVES, MODE, MOE_STREAM_U>
+        <<<blocks, MOE_STREAM_WAVES * kWave, 0, stream>>>(g);
     return hipGetLastError();
 }
 

@@ -47,6 +47,9 @@ SMALL = {
     # experts of >= 768 rows: 256 x 256 tiles in both GEMMs, ragged last
     # tiles, and a K-split w2
     "big_tiles": MC("big_tiles", E=2, K=1, H=256, I=2048, T=1600, seed=20, weight_seed=20),
+    # weight streaming with 33-64 rows per expert (4 row groups) and a long
+    # w2 reduction (I = 8192)
+    "stream_long_k": MC("stream_long_k", E=4, K=1, H=256, I=8192, T=160, seed=34, weight_seed=34),
     # activation variants (gate/up values have std ~0.45 at H=512, so a
     # limit of 0.5 clamps a good share of them); each on the tile path, the
     # weight-streaming path (few rows) and the fp32 path

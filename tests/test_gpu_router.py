@@ -30,6 +30,8 @@ CASES = [
     ("dsv3_decode_f32", "dsv3", 64, "f32"),
     ("dsv3_one_token", "dsv3", 1, "f32"),
     ("odd_experts", None, 130, "f32"),
+    # many tokens, bf16 gate, E = 256: the 128 x 256 tile, ragged last token tile
+    ("dsv3_prefill_bf16", "dsv3", 4133, "bf16"),
 ]
 
 
@@ -130,6 +132,7 @@ FUSED = [
     ("dsv3_T256", "dsv3", 256, "bf16"),
     ("dsv3_T257", "dsv3", 257, "bf16"),
     ("dsv3_prefill_f32", "dsv3", 8192, "f32"),
+    ("dsv3_prefill_bf16", "dsv3", 8192, "bf16"),
     ("mixtral_decode", "mixtral", 32, "bf16"),
     ("mixtral_prefill", "mixtral", 4096, "bf16"),
     ("qwen_tiles", "qwen", 300, "bf16"),
