@@ -16,10 +16,11 @@
 // (or a part of it) is one vector load per lane and the wave reads it as one
 // contiguous run.  A selection round is a DPP max of the order-preserving
 // 32-bit keys, then one ballot per v and the lowest index holding the max.
-// When a group is a whole number of lanes (a power of two up to 64 of them)
-// or a run of a lane's own experts, the two largest keys of every group come
-// from the lane's own values plus one segmented DPP reduction, for all
-// groups at once.
+// When a group is a whole number of lanes (a power of two up to 64 of them),
+// the two largest keys of every group come from the lane's own values plus
+// one segmented DPP reduction, for all groups at once.  (A group smaller
+// than a lane's run cannot occur: VPL is the smallest of 1, 2, 4, 8 with
+// 64*VPL >= E, so E/G < VPL would need more than 64 groups.)
 //
 // The logits may come as `parts` partial sums (the router gate GEMM with H
 // split into parts, parts * T * E floats): they are added in part order, the
@@ -191,63 +192,30 @@ __device__ __forceinline__ void topk_row(const TopkArgs& a, int64_t t, int lane)
         const bool two = a.bias != nullptr && per >= 2;  // group score: two largest keys, or the largest
         const float2 none{-INFINITY, -INFINITY};
         const int seg = per / VPL;  // lanes per group, when a group is whole lanes
-        const bool lanes_fast = per % VPL == 0 && seg <= kWave && (seg & (seg - 1)) == 0;
-        const bool inlane_fast = per < VPL && VPL % per == 0;
-        if (lanes_fast || inlane_fast) {
-            // pair[v]: the (largest, second) of the lane's keys of v's group
-            // up to v; at the group's last position, of the whole group
-            float2 pair[VPL];
+        if (per % VPL == 0 && seg <= kWave && (seg & (seg - 1)) == 0) {
+            // the lane's (largest, second) pair, then a segmented reduction
+            // over the group's `seg` lanes leaves the group's pair in its
+            // last lane
+            float2 p = none;
 #pragma unroll
-            for (int v = 0; v < VPL; ++v) {
-                pair[v] = cand[v] ? float2{key[v], -INFINITY} : none;
-                if (v > 0 && (lanes_fast || v % per != 0)) pair[v] = merge_top2(pair[v - 1], pair[v]);
-            }
-            bool gok[VPL];
-            if (lanes_fast) {
-                // the group spans `seg` lanes: a segmented reduction of the
-                // lanes' pairs leaves the group's pair in its last lane
-                float2 p = pair[VPL - 1];
-                if (seg >= 2) p = dpp_step<0x111, 0xF>(p, none, merge_top2);   // row_shr:1
-                if (seg >= 4) p = dpp_step<0x112, 0xF>(p, none, merge_top2);   // row_shr:2
-                if (seg >= 8) p = dpp_step<0x114, 0xF>(p, none, merge_top2);   // row_shr:4
-                if (seg >= 16) p = dpp_step<0x118, 0xF>(p, none, merge_top2);  // row_shr:8
-                if (seg >= 32) p = dpp_step<0x142, 0xA>(p, none, merge_top2);  // row_bcast:15
-                if (seg >= 64) p = dpp_step<0x143, 0xC>(p, none, merge_top2);  // row_bcast:31
-                pair[VPL - 1] = p;
-                const bool last = (lane & (seg - 1)) == seg - 1 && VPL * lane < E;
-#pragma unroll
-                for (int v = 0; v < VPL; ++v) gok[v] = v == VPL - 1 && last;
-            } else {
-#pragma unroll
-                for (int v = 0; v < VPL; ++v) gok[v] = v % per == per - 1 && VPL * lane + v < E;
-            }
-            // the TG best groups; a group is named by its last position, in
-            // the order of the groups
-            uint32_t gkey[VPL];
-#pragma unroll
-            for (int v = 0; v < VPL; ++v) gkey[v] = ordered_bits(two ? pair[v].x + pair[v].y : pair[v].x);
-            bool gsel[VPL];
-#pragma unroll
-            for (int v = 0; v < VPL; ++v) gsel[v] = gok[v];
+            for (int v = 0; v < VPL; ++v)
+                if (cand[v]) p = merge_top2(p, float2{key[v], -INFINITY});
+            if (seg >= 2) p = dpp_step<0x111, 0xF>(p, none, merge_top2);   // row_shr:1
+            if (seg >= 4) p = dpp_step<0x112, 0xF>(p, none, merge_top2);   // row_shr:2
+            if (seg >= 8) p = dpp_step<0x114, 0xF>(p, none, merge_top2);   // row_shr:4
+            if (seg >= 16) p = dpp_step<0x118, 0xF>(p, none, merge_top2);  // row_shr:8
+            if (seg >= 32) p = dpp_step<0x142, 0xA>(p, none, merge_top2);  // row_bcast:15
+            if (seg >= 64) p = dpp_step<0x143, 0xC>(p, none, merge_top2);  // row_bcast:31
+            // the TG best groups, each named by its last lane (in group order)
+            uint32_t gkey[1] = {ordered_bits(two ? p.x + p.y : p.x)};
+            bool gok[1] = {(lane & (seg - 1)) == seg - 1 && VPL * lane < E};
+            const bool was_end = gok[0];
             for (int r = 0; r < a.TG; ++r) take_first_max(gkey, gok, lane);
-            // selected = was a candidate group end and is no longer one
+            // selected: a group end that is no longer a candidate
+            const uint64_t kept = __ballot(was_end && !gok[0]);
+            const bool mine = (kept >> (lane | (seg - 1))) & 1ull;
 #pragma unroll
-            for (int v = 0; v < VPL; ++v) gsel[v] = gsel[v] && !gok[v];
-            if (lanes_fast) {
-                const uint64_t kept = __ballot(gsel[VPL - 1]);
-                const bool mine = (kept >> (lane | (seg - 1))) & 1ull;
-#pragma unroll
-                for (int v = 0; v < VPL; ++v) cand[v] = cand[v] && mine;
-            } else {
-#pragma unroll
-                for (int v = 0; v < VPL; ++v) {
-                    bool k = false;
-#pragma unroll
-                    for (int u = 0; u < VPL; ++u)
-                        if (u / per == v / per && u % per == per - 1) k = gsel[u];
-                    cand[v] = cand[v] && k;
-                }
-            }
+            for (int v = 0; v < VPL; ++v) cand[v] = cand[v] && mine;
         } else {
             // other group sizes: one wave reduction per group; group g's score
             // lands in lane g (G <= 64)

@@ -48,6 +48,14 @@ CASES = {
     "softmax_e128_g16": (128, 8, O.SOFTMAX, 16, 4, "none", True, 1.0),
     "softmax_e96_g6": (96, 4, O.SOFTMAX, 6, 2, "none", True, 1.0),
     "sigmoid_e72_g3_bias": (72, 4, O.SIGMOID, 3, 2, "lattice", True, 1.0),
+    # the largest routing shapes: 8 experts a lane (E > 256), K = 32, 64
+    # groups (of 8, and of 5: one reduction per group), and E = 130 (runs
+    # of 4 that end inside a lane's run: element loads)
+    "softmax_e512_k32": (512, 32, O.SOFTMAX, 0, 0, "none", True, 1.0),
+    "sigmoid_e384_g12_bias": (384, 8, O.SIGMOID, 12, 4, "lattice", True, 2.5),
+    "softmax_e512_g64": (512, 8, O.SOFTMAX, 64, 4, "none", True, 1.0),
+    "sigmoid_e320_g64_bias": (320, 16, O.SIGMOID, 64, 8, "lattice", False, 1.0),
+    "softmax_e130_k6": (130, 6, O.SOFTMAX, 0, 0, "none", False, 1.0),
 }
 
 ROWS_PER_KIND = 48
