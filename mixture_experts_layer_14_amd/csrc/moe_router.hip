@@ -532,12 +532,14 @@ bool router_topk_one_launch(int64_t T, int E, int H, int act_dtype) {
     return act_dtype == 1 && T > 0 && !router_plan(T, E, H).big && T <= 256;
 }
 
+// Successive fused launches (of every instantiation) take successive
+// arrival counters.
+static std::atomic<uint32_t> next_arrival_slot{0};
+
 template <int VPL>
 static void launch_fused(bool gf32, dim3 grid, const uint16_t* x, const void* gate, int64_t T, int E,
                          int H, int parts, float* partials, const TopkArgs& tk, hipStream_t stream) {
-    // successive launches take successive arrival counters
-    static std::atomic<uint32_t> next_slot{0};
-    const int slot = static_cast<int>(next_slot.fetch_add(1, std::memory_order_relaxed) % kArrivalSlots);
+    const int slot = static_cast<int>(next_arrival_slot.fetch_add(1, std::memory_order_relaxed) % kArrivalSlots);
     if (gf32)
         router_gemm_kernel<true, 64, 64, 2, 2, VPL><<<grid, 256, 0, stream>>>(x, gate, T, E, H, parts, partials, tk, slot);
     else
