@@ -94,6 +94,14 @@ SMALL = {
                         w_dtype="f32", shared=1, shared_I=640, seed=36, weight_seed=36),
     "shared_2I_non_gated": MC("shared_2I_non_gated", E=8, K=2, H=512, I=448, T=300,
                               non_gated=True, shared=1, shared_I=896, seed=37, weight_seed=37),
+    # the largest routing the boundary takes: 512 experts, top_k 32 (512
+    # segments in the tile table, 32 rows per token in the combine)
+    "max_routing": MC("max_routing", E=512, K=32, H=128, I=128, T=64, seed=38, weight_seed=38),
+    "max_routing_tiles": MC("max_routing_tiles", E=512, K=32, H=128, I=128, T=1100, seed=40,
+                            weight_seed=40),
+    # the widest shared expert: 16 slices of I
+    "shared_16I": MC("shared_16I", E=4, K=1, H=128, I=64, T=40, shared=1, shared_I=1024, seed=39,
+                     weight_seed=39),
 }
 
 
