@@ -330,15 +330,16 @@ def measured_peaks():
             "spec": {"bf16_mfma_tflops": PEAK_BF16_TFLOPS, "hbm_GBps": PEAK_HBM_GBS}}
 
 
-def cpu_sample(cfg, inp, tokens):
+def cpu_sample(cfg, inp, tokens, threads=None):
     """The oracle as it stands on `tokens` of the workload (only the experts
     they use are copied to the host), and its routing + permutation over all
-    T tokens; host threads (<= 16)."""
+    T tokens; host threads (<= 16, or `threads`)."""
     from mixture_experts_layer_14_amd import synth
     from oracle import oracle as O
 
-    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
-    threads = max(1, min(threads, 16))
+    if threads is None:
+        threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+        threads = max(1, min(threads, 16))
     bits = synth.tensor_bits
     logits = bits(inp["router_logits"])
     bias = bits(inp.get("e_score_correction_bias"))
@@ -432,6 +433,8 @@ def per_config(steps, warmup, peaks, with_cpu, names=None):
             row["roofline_frac_measured_peaks"] = max(m_f, m_b) / t
         if with_cpu:
             row["cpu_baseline"] = cpu_sample(cfg, inp, sample)
+            if name == "tiny":  # the tiny layer also on one host thread
+                row["cpu_baseline_1thread"] = cpu_sample(cfg, inp, sample, threads=1)
         rows.append(row)
         print("config %s: median %.3f ms, min %.3f ms" % (name, ms["median"], ms["min"]),
               file=sys.stderr, flush=True)
