@@ -80,3 +80,60 @@ def test_graph_replay_is_bitwise_eager(name):
         assert big.shape == (2 * T, cfg.H)
         assert layer.workspace(2 * T).data_ptr() == ws.data_ptr()
         assert torch.equal(got, ref), "replay %d differs from the eager forward" % rep
+
+
+def test_router_topk_graph_replay_is_bitwise_eager():
+    """moe_router_topk at a decode size (one launch: the router kernel's last
+    blocks run the top-k, counting arrivals in a device counter that every
+    launch leaves at zero) captured once and replayed with new hidden states,
+    with eager calls of other sizes between the replays: every replay equals
+    an eager call bitwise."""
+    from mixture_experts_layer_14_amd import binding as B
+
+    cfg = synth.CONFIGS["dsv3"]
+    T = 64
+    g = synth.make_gate(cfg, "bf16", device="cuda")
+    bias = torch.from_numpy(synth.make_correction_bias(cfg)).cuda()
+    src = synth.make_hidden(cfg, 4 * T, device="cuda")
+
+    def params(n):
+        return B.make_params(num_tokens=n, num_experts=cfg.E, top_k=cfg.K, hidden_size=cfg.H,
+                             intermediate_size=cfg.I, scoring_func=B.SIGMOID, renormalize=1,
+                             num_expert_group=cfg.n_group, topk_group=cfg.topk_group,
+                             routed_scaling_factor=cfg.rsf, act_dtype=B.BF16, weight_dtype=B.BF16,
+                             out_dtype=B.BF16)
+
+    p = params(T)
+    ws = torch.empty(max(B.moe_workspace_size(p), 256), dtype=torch.uint8, device="cuda")
+    x = src[:T].clone()
+    ids = torch.empty(T, cfg.K, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, cfg.K, dtype=torch.float32, device="cuda")
+    print("router graph case T", T, flush=True)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        B.moe_router_topk(p, x, g, bias, ids, w, None, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        B.moe_router_topk(p, x, g, bias, ids, w, None, ws)
+    torch.cuda.synchronize()
+
+    p2 = params(2 * T)
+    ws2 = torch.empty(max(B.moe_workspace_size(p2), 256), dtype=torch.uint8, device="cuda")
+    ids2 = torch.empty(2 * T, cfg.K, dtype=torch.int32, device="cuda")
+    w2 = torch.empty(2 * T, cfg.K, dtype=torch.float32, device="cuda")
+    for rep in range(4):
+        x.copy_(src[rep * T:(rep + 1) * T])
+        graph.replay()
+        torch.cuda.synchronize()
+        got_ids, got_w = ids.clone(), w.clone()
+        # eager work between replays: another size, then the same inputs
+        B.moe_router_topk(p2, src[:2 * T], g, bias, ids2, w2, None, ws2)
+        ref_ids = torch.empty_like(ids)
+        ref_w = torch.empty_like(w)
+        B.moe_router_topk(p, x, g, bias, ref_ids, ref_w, None, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(got_ids, ref_ids), "replay %d ids differ" % rep
+        assert torch.equal(got_w, ref_w), "replay %d weights differ" % rep
