@@ -66,7 +66,6 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
     constexpr int LDS_MAX = 160 * 1024;
     constexpr int ROW_W_BYTES = MODE == kModeW2 ? BM * 4 : 0;
     constexpr int STAGES = 4 * STAGE + RING + ROW_W_BYTES <= LDS_MAX ? 4 : 3;
-    constexpr int KSTEPS = 2;                      // 64-value MFMA steps per k block
     static_assert(ROWS % (RPC * NW) == 0 && BM % RPC == 0 && BM % NW == 0, "copy split");
     static_assert(SROWS + NBS <= kWave, "scale slots of wave 0");
     static_assert(SG == 1 || SG == 4, "scales per k-block or per group of 4");
