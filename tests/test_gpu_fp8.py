@@ -55,6 +55,17 @@ FP8_SMALL = {
     "fp8_big_tiles_clipped": MC("fp8_big_tiles_clipped", E=4, K=1, H=512, I=1024, T=900,
                                 w_dtype="fp8", seed=30, weight_seed=30, swiglu_alpha=1.702,
                                 swiglu_limit=0.5),
+    # decode sizes: weight streaming (at most 16 rows per expert, and 17-32
+    # rows), grouped sigmoid routing, a shared expert of 2I, clipped SwiGLU,
+    # three k blocks (H = 384)
+    "fp8_decode_grouped_shared_2I": MC("fp8_decode_grouped_shared_2I", E=16, K=4, H=512, I=256, T=9,
+                                       w_dtype="fp8", scoring="sigmoid", n_group=4, topk_group=2,
+                                       rsf=2.5, correction_bias=True, shared=1, shared_I=512, seed=31,
+                                       weight_seed=31, delta=1e-4),
+    "fp8_decode_clipped": MC("fp8_decode_clipped", E=8, K=2, H=384, I=384, T=5, w_dtype="fp8",
+                             seed=32, weight_seed=32, swiglu_alpha=1.702, swiglu_limit=0.5),
+    "fp8_decode_32_rows": MC("fp8_decode_32_rows", E=4, K=2, H=512, I=512, T=60, w_dtype="fp8",
+                             seed=33, weight_seed=33),
 }
 
 
@@ -155,6 +166,26 @@ def test_full_size_dsv3_fp8():
     print("  sampled %d rows: max|err|/max|ref| = %.3e" % (len(sample), err), flush=True)
     assert err <= U.TOL["fp8"]
     del layer, st, inp
+    torch.cuda.empty_cache()
+
+
+def test_full_size_dsv3_fp8_decode():
+    """The DeepSeek-V3 fp8 layer with its shared expert at T = 64 (the fp8
+    weight-streaming kernels), every token against the oracle."""
+    cfg = synth.CONFIGS["dsv3_fp8"].with_T(64)
+    T = cfg.T
+    print("case dsv3_fp8 T", T, flush=True)
+    inp, layer, out, ids, wts = _run(cfg, T)
+    ref_ids, ref_w = U.oracle_route(cfg, U.to_host_bits(inp["router_logits"]),
+                                    U.to_host_bits(inp.get("e_score_correction_bias")))
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    sample = list(range(T))
+    experts = np.unique(ref_ids)
+    ref = O.moe_forward_tokens(U.oracle_layer(cfg, inp, T, experts=experts), sample, nthreads=16)
+    err = U.rel_err(U.out_to_f64(out), ref)
+    print("  all %d rows: max|err|/max|ref| = %.3e" % (T, err), flush=True)
+    assert err <= U.TOL["fp8"]
+    del layer, inp
     torch.cuda.empty_cache()
 
 
