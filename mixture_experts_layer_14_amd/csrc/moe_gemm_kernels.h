@@ -324,12 +324,21 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile tl, cons
     constexpr int STAGE = Shape::STAGE;
     constexpr int SLOTS = ROWB / 16;               // 16-byte slots per row
     constexpr int RPC = kWave / SLOTS;             // rows per copy instruction
-    constexpr int COPIES = ROWS / RPC / NW;        // copy instructions per wave per stage
+    // Copy instructions per wave per stage.  Every wave takes an equal share
+    // of the stage's rows when they split evenly; otherwise (320 x 256: 36
+    // copies for 8 waves) the first half of the waves copy the A rows (CA
+    // each) and the second half the B rows (CB each), and each half runs a
+    // main loop of its own with its own copy count.
+    constexpr bool SPLIT = ROWS % (RPC * NW) != 0;
+    constexpr int CA = SPLIT ? BM / RPC / (NW / 2) : ROWS / RPC / NW;
+    constexpr int CB = SPLIT ? BN / RPC / (NW / 2) : CA;
+    constexpr int COPIES = CA > CB ? CA : CB;      // the larger share
     constexpr int KSTEPS = ROWB / 32;              // 16-k MFMA steps per k-iteration
     constexpr int LDS_MAX = Shape::LDS_MAX;
     constexpr int STAGES = Shape::STAGES;
     static_assert(ROWB == 64 || ROWB == 128, "row slab of 64 or 128 bytes");
-    static_assert(ROWS % (RPC * NW) == 0, "stage rows split evenly over the waves");
+    static_assert(!SPLIT || (NW % 2 == 0 && BM % (RPC * NW / 2) == 0 && BN % (RPC * NW / 2) == 0 && CA >= CB),
+                  "stage rows split evenly over the waves, or A and B rows over two halves of them");
     static_assert(BM % RPC == 0, "copy instructions never straddle A and B");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
     static_assert(MODE != kModeW13 || TN % 2 == 0, "w13 wave tile holds gate/up pairs");
@@ -350,11 +359,19 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile tl, cons
     const int64_t eltK = static_cast<int64_t>(g.Kd) * 2;
     const BSel bw = expert_weights<MODE>(g, tl.expert, 2);
 
-    // source of this lane's 16-byte slot in each of the wave's copies
+    // first stage row of this wave's copy q (wave-uniform); with SPLIT the
+    // A half of the waves copies rows [0, BM), the B half rows [BM, ROWS)
+    const bool a_wave = !SPLIT || wave < NW / 2;
+    auto copy_row0 = [&](int q) {
+        if constexpr (SPLIT) return a_wave ? (wave * CA + q) * RPC : BM + ((wave - NW / 2) * CB + q) * RPC;
+        return (wave * COPIES + q) * RPC;
+    };
+    // source of this lane's 16-byte slot in each of the wave's copies (a B
+    // wave's copies past CB are never issued; they alias its first)
     const uint8_t* src[COPIES];
 #pragma unroll
     for (int q = 0; q < COPIES; ++q) {
-        const int row = (wave * COPIES + q) * RPC + lane / SLOTS;
+        const int row = copy_row0(a_wave || q < CB ? q : 0) + lane / SLOTS;
         const int chunk = lds_slot<ROWB>(row, lane % SLOTS);  // the swizzle is an involution
         if (row < BM) {
             int64_t r = tl.row0 + row;
@@ -373,7 +390,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile tl, cons
     // ROWB/64 KiB-blocks in the packed B (whose copies are the later ones)
     // and in a packed A
     const bool a_pk = MODE == kModeW2 && g.a_packed;
-    auto kstep_shift = [&](int q) { return a_pk || (wave * COPIES + q) * RPC >= BM ? 4 : 0; };
+    auto kstep_shift = [&](int q) { return a_pk || copy_row0(q) >= BM ? 4 : 0; };
 #pragma unroll
     for (int q = 0; q < COPIES; ++q) src[q] += (static_cast<int64_t>(k_first) * ROWB) << kstep_shift(q);
 
@@ -381,8 +398,9 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile tl, cons
     // last k-iteration the source is clamped to it (a redundant in-bounds
     // copy into a buffer nobody reads again keeps the copy count per
     // k-iteration fixed and the loop free of branches)
+    const int copy_dst = copy_row0(0) * ROWB;  // RPC rows of ROWB bytes: 1 KiB per copy
     auto issue_copies = [&](int kit, int q0, int q1) {
-        uint8_t* dst = smem + (kit % STAGES) * STAGE + wave * COPIES * 1024;
+        uint8_t* dst = smem + (kit % STAGES) * STAGE + copy_dst;
         const int64_t off = static_cast<int64_t>(kit < nk ? kit : nk - 1) * ROWB;
 #pragma unroll
         for (int q = q0; q < q1; ++q)
@@ -437,9 +455,10 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile tl, cons
         for (int j = 0; j < TN; ++j) fb[j] = *reinterpret_cast<const u32x4*>(smem + pb + j * 32 * ROWB);
     };
     constexpr int kReads = TM + TN, kMfma = TM * TN;
-    // this wave's copies of all but the STAGES-2 most recent stages landed
-    auto wait_later_stages = [&]() {
-        constexpr int n = (STAGES - 2) * COPIES;
+    // this wave's copies (NC per stage) of all but the STAGES-2 most recent
+    // stages landed
+    auto wait_later_stages = [&](auto nc_tag) {
+        constexpr int n = (STAGES - 2) * decltype(nc_tag)::value;
         __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
     };
     // A ragged last tile of an expert skips the MFMAs of 32-row blocks that
@@ -449,8 +468,9 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile tl, cons
     const int live_rows = static_cast<int>(tl.row1 - tl.row0) - wm * WTM;
     const int act_tm = __builtin_amdgcn_readfirstlane(
         live_rows <= 0 ? 0 : (live_rows >= WTM ? TM : (live_rows + 31) / 32));
-    auto main_loop = [&](auto partial_tag) {
+    auto main_loop = [&](auto partial_tag, auto nc_tag) {
         constexpr bool PARTIAL = decltype(partial_tag)::value;
+        constexpr int NC = decltype(nc_tag)::value;  // this wave's copies per stage
         auto mfma_range = [&](int lo, int hi, const u32x4 (&fa)[TM], const u32x4 (&fb)[TN]) {
 #pragma unroll
             for (int m = lo; m < hi; ++m)
@@ -460,14 +480,14 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile tl, cons
                         acc[m / TN][m % TN], 0, 0, 0);
         };
 #pragma unroll
-        for (int st = 0; st < STAGES - 1; ++st) issue_copies(st, 0, COPIES);
-        wait_later_stages();
+        for (int st = 0; st < STAGES - 1; ++st) issue_copies(st, 0, NC);
+        wait_later_stages(nc_tag);
         __builtin_amdgcn_s_barrier();
         u32x4 af[2][TM], bfr[2][TN];
         read_at(a_lane(0), b_lane(0), af[0], bfr[0]);
         // copies per k-step when a stage's copies are spread over the k-steps
         // that precede the next barrier
-        constexpr int CPS = (COPIES + KSTEPS - 2) / (KSTEPS - 1);
+        constexpr int CPS = (NC + KSTEPS - 2) / (KSTEPS - 1);
         for (int it = 0; it < nk; ++it) {
             // The library is built with loops starting on 64-byte
             // boundaries; three s_nop put the loop body 12 bytes past one.
@@ -482,8 +502,8 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile tl, cons
                 read_at(stage + a_lane(s + 1), stage + b_lane(s + 1), af[(s + 1) & 1], bfr[(s + 1) & 1]);
                 // stage it+STAGES-1 goes to the buffer of stage it-1, free
                 // since the previous barrier
-                constexpr int q0 = s * CPS < COPIES ? s * CPS : COPIES;
-                constexpr int q1 = (s + 1) * CPS < COPIES ? (s + 1) * CPS : COPIES;
+                constexpr int q0 = s * CPS < NC ? s * CPS : NC;
+                constexpr int q1 = (s + 1) * CPS < NC ? (s + 1) * CPS : NC;
                 issue_copies(it + STAGES - 1, q0, q1);
                 mfma_range(0, kMfma, af[s & 1], bfr[s & 1]);
                 if constexpr (!PARTIAL) mix_sched<kMfma, kReads, q1 - q0>();
@@ -506,7 +526,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile tl, cons
             // consumed the last of them); its copies of stage it+1 must land
             // too, with those of stages it+2 .. it+STAGES-1 still in flight
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-            wait_later_stages();
+            wait_later_stages(nc_tag);
             __builtin_amdgcn_s_barrier();
             // the MFMAs of the second half stay behind the barrier
             __builtin_amdgcn_sched_barrier(0);
@@ -517,13 +537,24 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile tl, cons
             __builtin_amdgcn_sched_barrier(0);
         }
     };
+    // the A and B halves of the waves of a SPLIT tile run separate loops
+    auto run_loop = [&](auto partial_tag) {
+        if constexpr (SPLIT) {
+            if (a_wave)
+                main_loop(partial_tag, std::integral_constant<int, CA>{});
+            else
+                main_loop(partial_tag, std::integral_constant<int, CB>{});
+        } else {
+            main_loop(partial_tag, std::integral_constant<int, COPIES>{});
+        }
+    };
     if constexpr (LOOP == kLoopAuto) {
         if (tl.row1 - tl.row0 == BM)
-            main_loop(std::false_type{});
+            run_loop(std::false_type{});
         else
-            main_loop(std::true_type{});
+            run_loop(std::true_type{});
     } else {
-        main_loop(std::integral_constant<bool, LOOP == kLoopGuarded>{});
+        run_loop(std::integral_constant<bool, LOOP == kLoopGuarded>{});
     }
     // no copy may still write LDS when the block ends
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -685,10 +716,20 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
 // whole units of (n positions of a main m-tile) / 2, and units[u] describes
 // the group that owns unit u; each XCD takes a contiguous eighth of all
 // positions.
+//
+// With ext tiles, a main m-tile may also hold 257-320 rows: it runs as a
+// 320 x 256 tile (tile_body's split copies), which stages 576 rows per
+// k-iteration for 320 rows of output, so an expert whose rows exceed a
+// multiple of 256 by a little needs one such tile instead of a 256-row tile
+// plus a tail tile.  It runs every MFMA, as the tail tile does (measured on
+// the Mixtral-shape w13: the guarded loop made the layer 12 % slower, the
+// full loop as fast as without ext tiles).
 template <int MODE>
 __global__ __launch_bounds__(8 * kWave) void tile_kernel_tail(GemmArgs g) {
-    constexpr int SM = TileShape<256, 256, 64>::SMEM, ST = TileShape<128, 512, 64>::SMEM;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[SM > ST ? SM : ST];
+    constexpr int SM = TileShape<256, 256, 64>::SMEM, ST = TileShape<128, 512, 64>::SMEM,
+                  SX = TileShape<320, 256, 64>::SMEM;
+    constexpr int S1 = SM > ST ? SM : ST;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[S1 > SX ? S1 : SX];
     const int nparts = MODE == kModeW2 ? g.ksplit : 1;
     const int half = g.n_tiles_n * nparts / 2;  // positions per unit (n_tiles_n is even)
     const int total = *g.num_units * half;
@@ -704,8 +745,11 @@ __global__ __launch_bounds__(8 * kWave) void tile_kernel_tail(GemmArgs g) {
     if (r < 2 * d.cnt) {
         const int n = 2 * pair + r / d.cnt;
         const int kpart = n / g.n_tiles_n;
-        tile_body<256, 256, 2, 4, 64, MODE, kLoopAuto>(g, g.tiles[d.first_tile + r % d.cnt],
-                                                       n - kpart * g.n_tiles_n, kpart, nparts, smem);
+        const Tile tl = g.tiles[d.first_tile + r % d.cnt];
+        if (tl.row1 - tl.row0 > 256)
+            tile_body<320, 256, 2, 4, 64, MODE, kLoopFull>(g, tl, n - kpart * g.n_tiles_n, kpart, nparts, smem);
+        else
+            tile_body<256, 256, 2, 4, 64, MODE, kLoopAuto>(g, tl, n - kpart * g.n_tiles_n, kpart, nparts, smem);
     } else {
         const int kpart = 2 * pair / g.n_tiles_n;
         tile_body<128, 512, 2, 4, 64, MODE, MOE_TAIL_LOOP>(g, g.tiles[d.first_tile + d.cnt],

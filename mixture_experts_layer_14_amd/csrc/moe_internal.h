@@ -47,7 +47,7 @@ hipError_t launch_align(const int32_t* ids, int64_t n, int E, int32_t* offsets,
 struct TileTableKey {
     const void* ws = nullptr;
     const int32_t* offsets = nullptr;
-    int bm = 0, tail_rows = 0, split_nn = 0;
+    int bm = 0, tail_rows = 0, split_nn = 0, ext_rows = 0;
 };
 
 struct GroupedProblem {

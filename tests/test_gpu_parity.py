@@ -99,6 +99,15 @@ SMALL = {
     "max_routing": MC("max_routing", E=512, K=32, H=128, I=128, T=64, seed=38, weight_seed=38),
     "max_routing_tiles": MC("max_routing_tiles", E=512, K=32, H=128, I=128, T=1100, seed=40,
                             weight_seed=40),
+    # ~300 rows per expert: 320-row (ext) tiles in both GEMMs of the
+    # schedule with tail tiles (reductions of 1024), on the A/B-split copies
+    # of the 320 x 256 body
+    "ext_tiles": MC("ext_tiles", E=4, K=1, H=1024, I=1024, T=1200, seed=41, weight_seed=41),
+    # experts of 320 and 315 rows (ext tiles) and of 326 and 339 rows (a
+    # 256-row tile and a tail tile); the shared expert's 1300 rows: four
+    # 256-row tiles and an ext tile
+    "ext_main_tail": MC("ext_main_tail", E=4, K=1, H=1024, I=1024, T=1300, shared=1, seed=42,
+                        weight_seed=42),
     # the widest shared expert: 16 slices of I
     "shared_16I": MC("shared_16I", E=4, K=1, H=128, I=64, T=40, shared=1, shared_I=1024, seed=39,
                      weight_seed=39),

@@ -1,7 +1,7 @@
 """A plain-Python model of the device-side GEMM schedules, checked for
 coverage on the CPU: the tile builder (build_tiles_kernel) with tail tiles
-and with the K-split of the last round, and the block maps of
-tile_kernel_tail and tile_kernel_ksplit.  The model restates the index
+(and 320-row ext tiles) and with the K-split of the last round, and the
+block maps of tile_kernel_tail and tile_kernel_ksplit.  The model restates the index
 arithmetic of those kernels; the GPU parity tests run the kernels
 themselves.  Invariants: every output tile (m-tile x n-tile, or its K parts)
 is produced by exactly one block; every grid block index decodes in range;
@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 BM, GM, TAIL = 256, 8, 128
+EXT = 320
 
 
 def _segments(counts, shared):
@@ -30,13 +31,22 @@ def _max_m(counts, shared, E):
     return -(-(sum(counts) + T * slices) // BM) + E + slices
 
 
-def build_tail(counts, shared):
+def cover(rows, ext=True):
+    """(main m-tiles, tail tiles) of one segment: 256-row tiles, except that
+    a remainder of at most EXT - 256 rows joins the last full tile (ext) or
+    one of at most TAIL rows goes to a tail tile."""
+    rem = rows % BM
+    merge = ext and rows > BM and 0 < rem <= EXT - BM
+    tail = 1 if not merge and 0 < rem <= TAIL else 0
+    nmain = rows // BM + (1 if rem > 0 and not tail and not merge else 0)
+    return nmain, tail
+
+
+def build_tail(counts, shared, ext=True):
     """Tiles and unit table of the schedule with tail tiles."""
     tiles, units = [], []
     for r0, r1 in _segments(counts, shared):
-        rem = (r1 - r0) % BM
-        tail = 1 if 0 < rem <= TAIL else 0
-        nmain = (r1 - r0) // BM + (1 if rem > 0 and not tail else 0)
+        nmain, tail = cover(r1 - r0, ext)
         nt = nmain + tail
         start, ustart = len(tiles), len(units)
         ng = 0 if nt == 0 else (1 if nmain == 0 else -(-nmain // GM))
@@ -46,7 +56,7 @@ def build_tail(counts, shared):
             first, last = c * nmain // ng, (c + 1) * nmain // ng
             ht = tail if c == ng - 1 else 0
             for j in range(first, last + ht):
-                tl[j] = (r0 + j * BM, min(r0 + (j + 1) * BM, r1))
+                tl[j] = (r0 + j * BM, r0 + (j + 1) * BM if j + 1 < nt else r1)
             d = (start + first, last - first, ht, ustart + 2 * first)
             for u in range(2 * (last - first) + ht):
                 units[ustart + 2 * first + u] = d
@@ -54,8 +64,8 @@ def build_tail(counts, shared):
     return tiles, units
 
 
-def run_tail(counts, shared, n_tiles_n, nparts, E):
-    tiles, units = build_tail(counts, shared)
+def run_tail(counts, shared, n_tiles_n, nparts, E, ext=True):
+    tiles, units = build_tail(counts, shared, ext)
     assert all(u is not None for u in units)
     max_m = _max_m(counts, shared, E)
     assert len(tiles) <= max_m and len(units) <= 2 * max_m
@@ -76,7 +86,7 @@ def run_tail(counts, shared, n_tiles_n, nparts, E):
             kpart, n = divmod(2 * pair + r // cnt, n_tiles_n)
             keys = [(first + r % cnt, kpart, n)]
             r0, r1 = tiles[first + r % cnt]
-            assert r1 - r0 <= BM
+            assert 0 < r1 - r0 <= (EXT if ext else BM)  # > 256 rows: the 320-row body
         else:
             kpart = 2 * pair // n_tiles_n
             n512 = (2 * pair - kpart * n_tiles_n) // 2
@@ -175,11 +185,27 @@ CASES = [
 
 @pytest.mark.parametrize("name,counts,shared,E", CASES, ids=[c[0] for c in CASES])
 @pytest.mark.parametrize("n_tiles_n,nparts", [(2, 1), (16, 4), (28, 2), (112, 1)])
-def test_tail_schedule_covers_every_tile_once(name, counts, shared, E, n_tiles_n, nparts):
-    run_tail(counts, shared, n_tiles_n, nparts, E)
+@pytest.mark.parametrize("ext", [True, False], ids=["ext", "no_ext"])
+def test_tail_schedule_covers_every_tile_once(name, counts, shared, E, n_tiles_n, nparts, ext):
+    run_tail(counts, shared, n_tiles_n, nparts, E, ext)
 
 
-@pytest.mark.parametrize("name,counts,shared,E", CASES, ids=[c[0] for c in CASES])
-@pytest.mark.parametrize("nn,parts", [(1, 2), (2, 2), (16, 4), (28, 2)])
-def test_ksplit_schedule_covers_every_tile_once(name, counts, shared, E, nn, parts):
-    run_split(counts, shared, nn, parts, E)
+def test_cover_tile_heights():
+    """Every tile but the segment's last is a full 256-row tile; the last is
+    a 1-256-row tile, a 257-320-row ext tile (a full tile plus a remainder
+    of at most 64 rows) or a 1-128-row tail tile; never more
+    tiles than 256-row tiles alone would need."""
+    for rows in range(0, 3000):
+        for ext in (True, False):
+            nmain, tail = cover(rows, ext)
+            nt = nmain + tail
+            assert nt <= -(-rows // BM) and 2 * nmain + tail <= 2 * -(-rows // BM)
+            if rows == 0:
+                assert nt == 0
+                continue
+            last = rows - BM * (nt - 1)
+            assert 0 < last
+            if tail:
+                assert last <= TAIL
+            elif last > BM:
+                assert ext and last <= EXT and (rows % BM) <= EXT - BM
