@@ -593,7 +593,7 @@ template <int MODE>
 static hipError_t launch_tile_ksplit(const GroupedProblem& p, GemmArgs& g, const int32_t* offsets, void* ws,
                                      hipStream_t stream) {
     g.n_tiles_n = g.N / 256;
-    build_tiles(p, offsets, 256, g, ws, stream, 0, g.n_tiles_n);
+    build_tiles(p, offsets, 256, g, ws, stream, 0, g.n_tiles_n, g.Kd >= MOE_EXT_MIN_K ? MOE_EXT_ROWS : 0);
     // every position of either section has a block; surplus blocks exit
     const int64_t whole = static_cast<int64_t>(g.max_m_tiles) * g.n_tiles_n;
     const int64_t parts = whole * g.ksplit;

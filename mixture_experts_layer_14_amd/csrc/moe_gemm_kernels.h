@@ -777,7 +777,8 @@ __device__ __forceinline__ TilePos tile_at(int t, int m0, int nn, const Tile* ti
 // index over (part, n-tile)).
 template <int MODE>
 __global__ __launch_bounds__(8 * kWave) void tile_kernel_ksplit(GemmArgs g) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[TileShape<256, 256, 64>::SMEM];
+    constexpr int SM = TileShape<256, 256, 64>::SMEM, SX = TileShape<320, 256, 64>::SMEM;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[SM > SX ? SM : SX];
     const int nn = g.n_tiles_n, parts = g.ksplit;
     const int nt = *g.num_tiles, ns = g.split[0];
     const int pos_a = (nt - ns) * nn, pos_b = ns * nn * parts;
@@ -787,14 +788,21 @@ __global__ __launch_bounds__(8 * kWave) void tile_kernel_ksplit(GemmArgs g) {
         const int t = xcd * per_a + local;
         if (t >= pos_a) return;
         const TilePos tp = tile_at(t, 0, nn, g.tiles);
-        tile_body<256, 256, 2, 4, 64, MODE, kLoopAuto>(g, g.tiles[tp.m], tp.n, 0, 1, smem);
+        const Tile tl = g.tiles[tp.m];
+        if (tl.row1 - tl.row0 > 256)
+            tile_body<320, 256, 2, 4, 64, MODE, kLoopFull>(g, tl, tp.n, 0, 1, smem);
+        else
+            tile_body<256, 256, 2, 4, 64, MODE, kLoopAuto>(g, tl, tp.n, 0, 1, smem);
     } else if (local < per_a + per_b) {
         const int t = xcd * per_b + (local - per_a);
         if (t >= pos_b) return;
         const TilePos tp = tile_at(t, nt - ns, nn * parts, g.tiles);
         const int kpart = tp.n / nn;
-        tile_body<256, 256, 2, 4, 64, MODE, kLoopAuto>(g, g.tiles[tp.m], tp.n - kpart * nn, kpart, parts,
-                                                       smem);
+        const Tile tl = g.tiles[tp.m];
+        if (tl.row1 - tl.row0 > 256)
+            tile_body<320, 256, 2, 4, 64, MODE, kLoopFull>(g, tl, tp.n - kpart * nn, kpart, parts, smem);
+        else
+            tile_body<256, 256, 2, 4, 64, MODE, kLoopAuto>(g, tl, tp.n - kpart * nn, kpart, parts, smem);
     }
 }
 

@@ -201,7 +201,12 @@ FULL = ["mixtral_decode", "mixtral", "qwen", "dsv3_decode", "dsv3"]
 # last expert's group runs as 2 K parts and the rest whole-K; checked on
 # sampled rows (including each expert's last row)
 SAMPLED = {"w2_split_sections": MC("w2_split_sections", E=4, K=2, H=4096, I=2048, T=2200, seed=32,
-                                   weight_seed=32)}
+                                   weight_seed=32),
+           # the same schedule with ext tiles: 4 experts of 1292-1309 rows,
+           # four 256-row tiles and one 320-row tile each, in both GEMMs; the
+           # last expert's group is the K-split section
+           "w2_split_ext": MC("w2_split_ext", E=4, K=2, H=4096, I=2048, T=2600, seed=44,
+                              weight_seed=43)}
 
 
 @pytest.mark.parametrize("name", FULL + sorted(SAMPLED))
