@@ -716,14 +716,33 @@ static hipError_t launch_tile_fp8_256(const GroupedProblem& p, GemmArgs g, const
     return hipGetLastError();
 }
 
+// 256 x 256 fp8 tiles with 128 x 512 tail tiles (tile_kernel_fp8_tail; N a
+// multiple of 512): the schedule of the bf16 tail kernel, an expert's
+// remainder of at most 128 rows one tile per pair of n-tiles.
+#ifndef MOE_FP8_TAIL
+#define MOE_FP8_TAIL 1
+#endif
+template <int MODE>
+static hipError_t launch_tile_fp8_tail(const GroupedProblem& p, GemmArgs g, const int32_t* offsets,
+                                       void* ws, hipStream_t stream) {
+    build_tiles(p, offsets, 256, g, ws, stream, 128);
+    g.n_tiles_n = g.N / 256;
+    // units <= 2 per m-tile: every position of the schedule has a block
+    const int64_t total = 2 * static_cast<int64_t>(g.max_m_tiles) * (g.n_tiles_n / 2);
+    tile_kernel_fp8_tail<MODE><<<static_cast<unsigned>(8 * ((total + 7) / 8)), 8 * kWave, 0, stream>>>(g);
+    return hipGetLastError();
+}
+
 template <int MODE>
 static hipError_t fp8_gemm(const GroupedProblem& p, GemmArgs g, const int32_t* offsets, void* ws,
                            hipStream_t stream) {
     const uintptr_t sc = reinterpret_cast<uintptr_t>(g.A_scale) | reinterpret_cast<uintptr_t>(g.B_scale) |
                          reinterpret_cast<uintptr_t>(g.B_shared_scale);
     if (MOE_FP8_BIG && (g.Kd / 128) % 4 == 0 && sc % 16 == 0 && g.N % 256 == 0 &&
-        rows_per_active_expert(p) >= MOE_FP8_BIG_MIN_ROWS)
+        rows_per_active_expert(p) >= MOE_FP8_BIG_MIN_ROWS) {
+        if (MOE_FP8_TAIL && g.N % 512 == 0) return launch_tile_fp8_tail<MODE>(p, g, offsets, ws, stream);
         return launch_tile_fp8_256<MODE>(p, g, offsets, ws, stream);
+    }
     if constexpr (MODE == kModeW13) {
         return launch_tile_fp8<128, 256, 2, 4, MODE>(p, g, offsets, ws, stream);
     } else {

@@ -394,11 +394,12 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel_fp8(GemmArgs g) {
 // (one extra rounding per k block), with one multiply per element and k
 // block, as before.  A k block spans two stages of 64 bytes; four stages fit
 // beside a two-slot ring of per-group scales (as above, SG = 4).
-// LDS plan of the body below for BM rows (stages, then the scale ring, then
-// the w2 row weights).
-template <int BM, int MODE>
+// LDS plan of the body below for a BM x BN tile (stages, then the scale
+// ring, then the w2 row weights): four stages, or three where four do not
+// fit (the 128 x 512 tail tile).
+template <int BM, int MODE, int BN_ = 256>
 struct Fp8BigShape {
-    static constexpr int BN = 256, NW = 8, ROWB = 64, STAGES = 4;
+    static constexpr int BN = BN_, NW = 8, ROWB = 64;
     static constexpr int ROWS = BM + BN;
     static constexpr int STAGE = ROWS * ROWB;
     static constexpr int SROWS = BM / NW;
@@ -406,19 +407,21 @@ struct Fp8BigShape {
     static constexpr int RING_SLOT = (SPOS * 16 + 255) / 256 * 256;
     static constexpr int RING = 2 * RING_SLOT;
     static constexpr int ROW_W_BYTES = MODE == kModeW2 ? BM * 4 : 0;
+    static constexpr int STAGES = 4 * STAGE + RING + ROW_W_BYTES <= 160 * 1024 ? 4 : 3;
     static constexpr int SMEM = STAGES * STAGE + RING + ROW_W_BYTES;
 };
 
-// One BM x 256 tile (BM = 256, or 128 for a remainder of at most 128 rows:
-// half the copies, LDS reads and MFMAs of a 256-row tile) of m-tile `tl`,
+// One BM x BN tile (BM x 256 with BM = 256, or 128 for a remainder of at
+// most 128 rows: half the copies, LDS reads and MFMAs of a 256-row tile; or
+// 128 x 512, a remainder's tile for two n-tiles) of m-tile `tl`, BN-wide
 // n-tile `n_tile`; `smem` is the kernel's one LDS array.
-template <int BM, int MODE>
+template <int BM, int MODE, int BN = 256>
 __device__ __forceinline__ void fp8_big_body(const GemmArgs& g, const Tile tl, const int n_tile,
                                              uint8_t* smem) {
-    using Shape = Fp8BigShape<BM, MODE>;
-    constexpr int BN = 256, WM = 2, WN = 4, NW = WM * WN;
+    using Shape = Fp8BigShape<BM, MODE, BN>;
+    constexpr int WM = 2, WN = 4, NW = WM * WN;
     constexpr int ROWB = Shape::ROWB;              // bytes of k per stage
-    constexpr int WTM = BM / WM, WTN = BN / WN;    // tokens x 64 features per wave
+    constexpr int WTM = BM / WM, WTN = BN / WN;    // tokens x 64 (or 128) features per wave
     constexpr int TM = WTM / 32, TN = WTN / 32;
     constexpr int ROWS = Shape::ROWS;
     constexpr int SLOTS = ROWB / 16;
@@ -428,7 +431,9 @@ __device__ __forceinline__ void fp8_big_body(const GemmArgs& g, const Tile tl, c
     constexpr int STAGES = Shape::STAGES;
     constexpr int SG = 4;                          // k blocks per scale group
     constexpr int SROWS = Shape::SROWS;            // A-scale rows copied per wave
-    constexpr int NBS = MODE == kModeW13 ? 2 : BN / 128;
+    // weight block scales per k block: BN / 128 weight rows' blocks (w13:
+    // half gate, half up blocks, interleaved as the B tile's 32-row blocks)
+    constexpr int NBS = BN / 128;
     constexpr int SPOS = Shape::SPOS;
     constexpr int RING_SLOT = Shape::RING_SLOT;
     constexpr int kMfma = TM * TN, HALF = kMfma / 2;
@@ -437,7 +442,8 @@ __device__ __forceinline__ void fp8_big_body(const GemmArgs& g, const Tile tl, c
     static_assert(BM + NBS <= SPOS && SROWS + NBS <= kWave, "ring positions");
     static_assert(Shape::SMEM <= 160 * 1024, "LDS budget");
     static_assert(COPIES * (STAGES - 2) + 1 <= 63, "vmcnt immediate range");
-    static_assert(MODE != kModeW13 || (TN == 2 && WN == 4), "w13: a wave holds one gate/up pair of 32 features");
+    static_assert(MODE != kModeW13 || (TN % 2 == 0 && WN == 4 && 128 % (TN / 2 * 32) == 0),
+                  "w13: a wave holds whole gate/up pairs of 32 features inside one 128-column act group");
     static_assert(MODE != kModeW13 || BM * WN * 4 <= STAGE, "w13 amax exchange fits one stage");
     static_assert(HALF % TN == 0, "each half holds whole token blocks");
     uint8_t* const ring = smem + STAGES * STAGE;
@@ -476,7 +482,8 @@ __device__ __forceinline__ void fp8_big_body(const GemmArgs& g, const Tile tl, c
         ssrc = g.A_scale + a_source_row<MODE>(g, r) * nkb;
         const int slot = p - BM;
         if (slot >= 0 && slot < NBS) {
-            const int rep = MODE == kModeW13 ? slot * 32 : slot * 128;  // a local row of the block
+            // a local row of the block (w13: 256-row spans of gate/up 32-row blocks)
+            const int rep = MODE == kModeW13 ? (slot / 2) * 256 + (slot % 2) * 32 : slot * 128;
             const int b = static_cast<int>(b_weight_row<MODE, BN, 32>(g, bw, n_tile, rep) / 128);
             ssrc = bw.scale + static_cast<int64_t>(b) * bw.scale_rs;
         }
@@ -554,7 +561,7 @@ __device__ __forceinline__ void fp8_big_body(const GemmArgs& g, const Tile tl, c
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int lr = wn * WTN + j * 32;
-            sw[j] = rs[(BM + (MODE == kModeW13 ? (lr / 32) % 2 : lr / 128)) * 4 + kb_in_group];
+            sw[j] = rs[(BM + (MODE == kModeW13 ? (lr / 256) * 2 + (lr / 32) % 2 : lr / 128)) * 4 + kb_in_group];
         }
 #pragma unroll
         for (int i = 0; i < TM; ++i)
@@ -649,46 +656,54 @@ __device__ __forceinline__ void fp8_big_body(const GemmArgs& g, const Tile tl, c
     // lane holds token wm*WTM + i*32 + lrow and, of each 32-feature tile j,
     // the features 8*(v/4) + 4*khalf + v%4
     if constexpr (MODE == kModeW13) {
+        // NP gate/up pairs per wave; GW waves share a 128-column act group
+        constexpr int NP = TN / 2, GW = 128 / (NP * 32);
         __syncthreads();
         float* red = reinterpret_cast<float*>(smem);  // [BM][WN]
-        float act[TM][16];
+        float act[TM][NP][16];
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             float m = 0.0f;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                act[i][v] = glu_act(g, acc[i][0][v], acc[i][1][v]);
-                m = fmaxf(m, fabsf(act[i][v]));
-            }
+            for (int p = 0; p < NP; ++p)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    act[i][p][v] = glu_act(g, acc[i][2 * p][v], acc[i][2 * p + 1][v]);
+                    m = fmaxf(m, fabsf(act[i][p][v]));
+                }
             m = fmaxf(m, __shfl_xor(m, 32, kWave));
             if (khalf == 0) red[(wm * WTM + i * 32 + lrow) * WN + wn] = m;
         }
         __syncthreads();
         uint8_t* q = static_cast<uint8_t*>(g.C);
         const int ngroups_i = g.I / 128;
+        const int grp = wn / GW;  // this wave's act group in the tile
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int lt = wm * WTM + i * 32 + lrow;
-            float amax = red[lt * WN];
+            float amax = red[lt * WN + grp * GW];
 #pragma unroll
-            for (int w = 1; w < WN; ++w) amax = fmaxf(amax, red[lt * WN + w]);
+            for (int w = 1; w < GW; ++w) amax = fmaxf(amax, red[lt * WN + grp * GW + w]);
             const float scale = fmaxf(amax, 1e-10f) / 448.0f;
             const int64_t r = tl.row0 + lt;
             if (r < tl.row1) {
-                // packed act: columns wn*32 .. +31 lie in one 64-byte piece of the row
-                uint8_t* qrow = q + (g.c_packed ? (r >> 4) * (static_cast<int64_t>(g.I) << 4) +
-                                                      (static_cast<int64_t>(n_tile) * 2 + (wn >> 1)) * 1024 +
-                                                      (r & 15) * 64 + (wn & 1) * 32 + 4 * khalf
-                                                : r * g.I + static_cast<int64_t>(n_tile) * 128 + wn * 32 + 4 * khalf);
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    uint32_t word = 0;
+                for (int p = 0; p < NP; ++p) {
+                    // the pair's 32 act columns lie in one 64-byte piece of the row
+                    const int64_t col0 = static_cast<int64_t>(n_tile) * (BN / 2) + (wn * NP + p) * 32;
+                    uint8_t* qrow = q + (g.c_packed ? (r >> 4) * (static_cast<int64_t>(g.I) << 4) + (col0 >> 6) * 1024 +
+                                                          (r & 15) * 64 + (col0 & 63) + 4 * khalf
+                                                    : r * g.I + col0 + 4 * khalf);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        word |= static_cast<uint32_t>(f32_to_e4m3(act[i][4 * b + e] / scale)) << (8 * e);
-                    *reinterpret_cast<uint32_t*>(qrow + 8 * b) = word;
+                    for (int b = 0; b < 4; ++b) {
+                        uint32_t word = 0;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            word |= static_cast<uint32_t>(f32_to_e4m3(act[i][p][4 * b + e] / scale)) << (8 * e);
+                        *reinterpret_cast<uint32_t*>(qrow + 8 * b) = word;
+                    }
                 }
-                if (wn == 0 && khalf == 0) g.C_scale[r * ngroups_i + n_tile] = scale;
+                if (wn % GW == 0 && khalf == 0) g.C_scale[r * ngroups_i + n_tile * (BN / 256) + grp] = scale;
             }
         }
     } else {
@@ -731,6 +746,32 @@ __global__ __launch_bounds__(8 * kWave) void tile_kernel_fp8_256(GemmArgs g) {
         fp8_big_body<128, MODE>(g, tl, tp.n, smem);
     else
         fp8_big_body<256, MODE>(g, tl, tp.n, smem);
+}
+
+// 256 x 256 fp8 tiles with 128 x 512 tail tiles (N a multiple of 512), in
+// the schedule and block order of tile_kernel_tail: an expert's remainder of
+// at most 128 rows is one 128 x 512 tile per pair of n-tiles, which stages
+// 640 rows per 64 bytes of k where two 128 x 256 tiles stage 768, and reads
+// a quarter fewer operand bytes from LDS per output column.
+template <int MODE>
+__global__ __launch_bounds__(8 * kWave) void tile_kernel_fp8_tail(GemmArgs g) {
+    constexpr int SM = Fp8BigShape<256, MODE>::SMEM, ST = Fp8BigShape<128, MODE, 512>::SMEM;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[SM > ST ? SM : ST];
+    const int half = g.n_tiles_n / 2;  // positions per unit
+    const int total = *g.num_units * half;
+    const int per = (total + 7) / 8;
+    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+    if (local >= per) return;
+    const int t = xcd * per + local;
+    if (t >= total) return;
+    const GroupUnit d = g.units[t / half];
+    const int w = t - d.first_unit * half;
+    const int slot = 2 * d.cnt + d.tail;  // blocks per n-tile pair
+    const int pair = w / slot, r = w - pair * slot;
+    if (r < 2 * d.cnt)
+        fp8_big_body<256, MODE>(g, g.tiles[d.first_tile + r % d.cnt], 2 * pair + r / d.cnt, smem);
+    else
+        fp8_big_body<128, MODE, 512>(g, g.tiles[d.first_tile + d.cnt], pair, smem);
 }
 
 }  // namespace moe

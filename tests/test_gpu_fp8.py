@@ -55,6 +55,12 @@ FP8_SMALL = {
     "fp8_big_tiles_clipped": MC("fp8_big_tiles_clipped", E=4, K=1, H=512, I=1024, T=900,
                                 w_dtype="fp8", seed=30, weight_seed=30, swiglu_alpha=1.702,
                                 swiglu_limit=0.5),
+    # 128 x 512 tail tiles: experts of 71, 45, 33 and 21 rows (a tail tile
+    # only), one of 459 rows (a full and a ragged 256-row tile), the shared
+    # expert's 800 rows (three 256-row tiles and a 32-row tail); clipped
+    "fp8_tail_only_experts": MC("fp8_tail_only_experts", E=6, K=1, H=512, I=512, T=800,
+                                w_dtype="fp8", logit_skew="zipf", shared=1, seed=50,
+                                weight_seed=50, swiglu_limit=0.5),
     # decode sizes: weight streaming (at most 16 rows per expert, and 17-32
     # rows), grouped sigmoid routing, a shared expert of 2I, clipped SwiGLU,
     # three k blocks (H = 384)
