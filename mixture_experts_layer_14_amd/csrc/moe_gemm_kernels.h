@@ -774,7 +774,8 @@ __device__ __forceinline__ TilePos tile_at(int t, int m0, int nn, const Tile* ti
 // only they pay for partial outputs and the extra tile prologues and
 // epilogues.  Block order: each XCD takes a contiguous eighth of the
 // whole-K positions, then a contiguous eighth of the split positions (n
-// index over (part, n-tile)).
+// index over (part, n-tile)).  m-tiles of 257-320 rows (ext tiles, as in
+// tile_kernel_tail) run the 320 x 256 body.
 template <int MODE>
 __global__ __launch_bounds__(8 * kWave) void tile_kernel_ksplit(GemmArgs g) {
     constexpr int SM = TileShape<256, 256, 64>::SMEM, SX = TileShape<320, 256, 64>::SMEM;
