@@ -108,6 +108,13 @@ SMALL = {
     # 256-row tiles and an ext tile
     "ext_main_tail": MC("ext_main_tail", E=4, K=1, H=1024, I=1024, T=1300, shared=1, seed=42,
                         weight_seed=42),
+    # the ext tiles' w13 epilogue variants: non-gated with the routing
+    # weight on the input, and clipped SwiGLU with alpha (~300 rows per
+    # expert, reductions of 1024: ext tiles in both GEMMs)
+    "ext_non_gated_weight_in": MC("ext_non_gated_weight_in", E=4, K=1, H=1024, I=1024, T=1200,
+                                  seed=41, weight_seed=43, non_gated=True, weight_on_input=True),
+    "ext_clipped_swiglu": MC("ext_clipped_swiglu", E=4, K=1, H=1024, I=1024, T=1200, seed=41,
+                             weight_seed=44, swiglu_alpha=1.702, swiglu_limit=0.5),
     # the widest shared expert: 16 slices of I
     "shared_16I": MC("shared_16I", E=4, K=1, H=128, I=64, T=40, shared=1, shared_I=1024, seed=39,
                      weight_seed=39),
