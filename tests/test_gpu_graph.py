@@ -32,6 +32,12 @@ CASES = {
     # fp8 with the input quantisation and a shared expert twice as wide
     "fp8_shared_2I": MC("fp8_shared_2I", E=8, K=2, H=512, I=512, T=77, w_dtype="fp8", shared=1,
                         shared_I=1024, seed=43, weight_seed=43),
+    # 320-row ext tiles in both bf16 GEMMs (tile table built once, shared by
+    # w13 and w2 inside the forward)
+    "ext_tiles": MC("ext_tiles", E=4, K=1, H=1024, I=1024, T=1200, seed=41, weight_seed=41),
+    # the fp8 tail kernel: 256-row tiles and 128 x 512 tail tiles
+    "fp8_tail_tiles": MC("fp8_tail_tiles", E=4, K=2, H=512, I=512, T=700, w_dtype="fp8",
+                         shared=1, seed=28, weight_seed=28),
 }
 
 
