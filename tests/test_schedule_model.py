@@ -31,13 +31,13 @@ def _max_m(counts, shared, E):
     return -(-(sum(counts) + T * slices) // BM) + E + slices
 
 
-def cover(rows, ext=True):
+def cover(rows, ext=True, tail_rows=TAIL):
     """(main m-tiles, tail tiles) of one segment: 256-row tiles, except that
     a remainder of at most EXT - 256 rows joins the last full tile (ext) or
-    one of at most TAIL rows goes to a tail tile."""
+    one of at most tail_rows rows goes to a tail tile."""
     rem = rows % BM
     merge = ext and rows > BM and 0 < rem <= EXT - BM
-    tail = 1 if not merge and 0 < rem <= TAIL else 0
+    tail = 1 if not merge and 0 < rem <= tail_rows else 0
     nmain = rows // BM + (1 if rem > 0 and not tail and not merge else 0)
     return nmain, tail
 
@@ -103,11 +103,12 @@ def run_tail(counts, shared, n_tiles_n, nparts, E, ext=True):
     assert (rows == 1).all()
 
 
-def build_split(counts, shared, nn):
-    """Tiles (row0, row1, group) and the split of the K-split schedule."""
+def build_split(counts, shared, nn, ext=True):
+    """Tiles (row0, row1, group) and the split of the K-split schedule (no
+    tail tiles; ext tiles as in the tail schedule)."""
     tiles = []
     for r0, r1 in _segments(counts, shared):
-        nt = -(-(r1 - r0) // BM)
+        nt, _ = cover(r1 - r0, ext, tail_rows=0)
         start = len(tiles)
         ng = -(-nt // GM) if nt else 0
         for j in range(nt):
@@ -115,7 +116,8 @@ def build_split(counts, shared, nn):
             while j >= (c + 1) * nt // ng:
                 c += 1
             first, last = c * nt // ng, (c + 1) * nt // ng
-            tiles.append((r0 + j * BM, min(r0 + (j + 1) * BM, r1), (start + first) * 256 + last - first))
+            tiles.append((r0 + j * BM, r0 + (j + 1) * BM if j + 1 < nt else r1,
+                          (start + first) * 256 + last - first))
     nt = len(tiles)
     rem = (nt * nn) % 256
     first = nt
@@ -132,8 +134,10 @@ def _tile_at(t, m0, nn, tiles):
     return first + w % cnt, w // cnt
 
 
-def run_split(counts, shared, nn, parts, E):
-    tiles, ns, split_row = build_split(counts, shared, nn)
+def run_split(counts, shared, nn, parts, E, ext=True):
+    tiles, ns, split_row = build_split(counts, shared, nn, ext)
+    for r0, r1, _ in tiles:
+        assert 0 < r1 - r0 <= (EXT if ext else BM)
     nt = len(tiles)
     max_m = _max_m(counts, shared, E)
     blocks = 8 * (-(-(max_m * nn) // 8) + -(-(max_m * nn * parts) // 8))
@@ -188,6 +192,13 @@ CASES = [
 @pytest.mark.parametrize("ext", [True, False], ids=["ext", "no_ext"])
 def test_tail_schedule_covers_every_tile_once(name, counts, shared, E, n_tiles_n, nparts, ext):
     run_tail(counts, shared, n_tiles_n, nparts, E, ext)
+
+
+@pytest.mark.parametrize("name,counts,shared,E", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("nn,parts", [(1, 2), (2, 2), (16, 4), (28, 2)])
+@pytest.mark.parametrize("ext", [True, False], ids=["ext", "no_ext"])
+def test_ksplit_schedule_covers_every_tile_once(name, counts, shared, E, nn, parts, ext):
+    run_split(counts, shared, nn, parts, E, ext)
 
 
 def test_cover_tile_heights():
