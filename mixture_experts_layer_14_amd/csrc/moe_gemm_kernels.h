@@ -326,9 +326,9 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile tl, cons
     constexpr int RPC = kWave / SLOTS;             // rows per copy instruction
     // Copy instructions per wave per stage.  Every wave takes an equal share
     // of the stage's rows when they split evenly; otherwise (320 x 256: 36
-    // copies for 8 waves) the first half of the waves copy the A rows (CA
-    // each) and the second half the B rows (CB each), and each half runs a
-    // main loop of its own with its own copy count.
+    // copies for 8 waves, 192 x 256: 28) the first half of the waves copy the
+    // A rows (CA each) and the second half the B rows (CB each), and each
+    // half runs a main loop of its own with its own copy count.
     constexpr bool SPLIT = ROWS % (RPC * NW) != 0;
     constexpr int CA = SPLIT ? BM / RPC / (NW / 2) : ROWS / RPC / NW;
     constexpr int CB = SPLIT ? BN / RPC / (NW / 2) : CA;
@@ -337,7 +337,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile tl, cons
     constexpr int LDS_MAX = Shape::LDS_MAX;
     constexpr int STAGES = Shape::STAGES;
     static_assert(ROWB == 64 || ROWB == 128, "row slab of 64 or 128 bytes");
-    static_assert(!SPLIT || (NW % 2 == 0 && BM % (RPC * NW / 2) == 0 && BN % (RPC * NW / 2) == 0 && CA >= CB),
+    static_assert(!SPLIT || (NW % 2 == 0 && BM % (RPC * NW / 2) == 0 && BN % (RPC * NW / 2) == 0),
                   "stage rows split evenly over the waves, or A and B rows over two halves of them");
     static_assert(BM % RPC == 0, "copy instructions never straddle A and B");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
@@ -366,12 +366,13 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const Tile tl, cons
         if constexpr (SPLIT) return a_wave ? (wave * CA + q) * RPC : BM + ((wave - NW / 2) * CB + q) * RPC;
         return (wave * COPIES + q) * RPC;
     };
-    // source of this lane's 16-byte slot in each of the wave's copies (a B
-    // wave's copies past CB are never issued; they alias its first)
+    // source of this lane's 16-byte slot in each of the wave's copies (with
+    // SPLIT, a wave's copies past its own count are never issued; they alias
+    // its first)
     const uint8_t* src[COPIES];
 #pragma unroll
     for (int q = 0; q < COPIES; ++q) {
-        const int row = copy_row0(a_wave || q < CB ? q : 0) + lane / SLOTS;
+        const int row = copy_row0(q < (a_wave ? CA : CB) ? q : 0) + lane / SLOTS;
         const int chunk = lds_slot<ROWB>(row, lane % SLOTS);  // the swizzle is an involution
         if (row < BM) {
             int64_t r = tl.row0 + row;
@@ -723,7 +724,9 @@ __global__ __launch_bounds__(WM* WN* kWave) void tile_kernel(GemmArgs g) {
 // multiple of 256 by a little needs one such tile instead of a 256-row tile
 // plus a tail tile.  It runs every MFMA, as the tail tile does (measured on
 // the Mixtral-shape w13: the guarded loop made the layer 12 % slower, the
-// full loop as fast as without ext tiles).
+// full loop as fast as without ext tiles).  A main m-tile of at most 192
+// rows (an expert of 129-192 rows, or such a remainder) runs as a 192 x 256
+// tile: 448 rows staged per k-iteration instead of 512.
 template <int MODE>
 __global__ __launch_bounds__(8 * kWave) void tile_kernel_tail(GemmArgs g) {
     constexpr int SM = TileShape<256, 256, 64>::SMEM, ST = TileShape<128, 512, 64>::SMEM,
@@ -748,6 +751,8 @@ __global__ __launch_bounds__(8 * kWave) void tile_kernel_tail(GemmArgs g) {
         const Tile tl = g.tiles[d.first_tile + r % d.cnt];
         if (tl.row1 - tl.row0 > 256)
             tile_body<320, 256, 2, 4, 64, MODE, kLoopFull>(g, tl, n - kpart * g.n_tiles_n, kpart, nparts, smem);
+        else if (tl.row1 - tl.row0 <= 192)
+            tile_body<192, 256, 2, 4, 64, MODE, kLoopAuto>(g, tl, n - kpart * g.n_tiles_n, kpart, nparts, smem);
         else
             tile_body<256, 256, 2, 4, 64, MODE, kLoopAuto>(g, tl, n - kpart * g.n_tiles_n, kpart, nparts, smem);
     } else {

@@ -115,6 +115,11 @@ SMALL = {
                                   seed=41, weight_seed=43, non_gated=True, weight_on_input=True),
     "ext_clipped_swiglu": MC("ext_clipped_swiglu", E=4, K=1, H=1024, I=1024, T=1200, seed=41,
                              weight_seed=44, swiglu_alpha=1.702, swiglu_limit=0.5),
+    # 192 x 256 tiles: an expert of 136 rows and one of 650 rows (two
+    # 256-row tiles and a 138-row one), beside a full 256-row expert and a
+    # tail-only one of 58 rows
+    "tiles_192": MC("tiles_192", E=4, K=1, H=1024, I=1024, T=1100, logit_skew="zipf", seed=66,
+                    weight_seed=66),
     # the widest shared expert: 16 slices of I
     "shared_16I": MC("shared_16I", E=4, K=1, H=128, I=64, T=40, shared=1, shared_I=1024, seed=39,
                      weight_seed=39),
